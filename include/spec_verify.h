@@ -1,0 +1,242 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify round on one AMD
+ * MI355X (gfx950).
+ *
+ * What the calls compute (the pages' definitions):
+ *   - "Speculative decoding" (gpillon.github.io/ignis), "One round, step by
+ *     step": each lane holds an anchor plus up to k drafts; all lanes' columns
+ *     go through the target model once; per lane the longest run of drafts the
+ *     model itself would have chosen is kept, plus the model's own next token
+ *     (between 1 and k + 1 tokens); the state then moves forward by exactly
+ *     that committed run, attention layers keeping every committed column's
+ *     keys and recurrent layers replaying only the committed prefix.
+ *   - The same page, "The row budget": drafts per lane =
+ *     min(draft tokens, rows / lanes - 1), a budget of 0 meaning 8.
+ *   - "Draft heads and speculative decoding" (research.strata2signal.com),
+ *     "Guess, then check": the greedy walk; the textbook sampled rule it cites
+ *     (Leviathan, Kalman & Matias 2022, Def. 3.7 / Thm. 3.8).
+ *   - FreeToken tracking issue #828, "Per-request state": the verify forward
+ *     only reads the live state and stages scratch; commit rolls the state to
+ *     the accepted count; a model whose recurrent state has no buffer is
+ *     refused.
+ *
+ * Conventions shared by every call:
+ *   - Status: SPEC_OK (0) or a negative SPEC_E_* code.  All arguments are
+ *     validated on the host BEFORE anything is enqueued, so an error leaves
+ *     every caller buffer untouched.  A HIP launch failure returns SPEC_E_HIP;
+ *     an asynchronous device fault surfaces at the caller's next stream sync.
+ *   - Ownership: the caller owns every device buffer (weights, KV pools, block
+ *     tables, state, workspace, outputs).  The library never allocates or
+ *     frees device memory; it owns only the host-side spec_model object.
+ *   - Streams: `stream` is a hipStream_t passed as void*; NULL is the default
+ *     stream.  Work is enqueued asynchronously, with no implicit
+ *     synchronisation, no memset nodes and no host<->device copies, so a round
+ *     can be captured into a HIP graph.
+ *   - Rows of a round are packed lane-major: lane l owns rows
+ *     [row_start(l), row_start(l) + cols[l]) with row_start(l) = sum of cols of
+ *     lanes before l; column 0 is the anchor, column j >= 1 is draft d_j.
+ *   - Numerics are batch-invariant: every reduction order is fixed by the
+ *     model shape and by absolute positions, never by the number of rows or
+ *     lanes in the round, so a row's results do not depend on the other rows.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_MAX_ROWS 64   /* rows of one round, summed over lanes */
+#define SPEC_MAX_COLS 16   /* columns of one lane: the anchor plus up to 15 drafts */
+#define SPEC_MAX_LANES 64
+#define SPEC_KV_BLOCK 16   /* tokens per paged-KV block */
+
+enum spec_status {
+  SPEC_OK = 0,
+  SPEC_E_INVAL = -1,        /* malformed argument */
+  SPEC_E_RANGE = -2,        /* the round does not fit the lane's block table */
+  SPEC_E_UNSUPPORTED = -3,  /* shape or combination this build does not run */
+  SPEC_E_WORKSPACE = -4,    /* workspace missing or too small */
+  SPEC_E_HIP = -5           /* a HIP runtime call failed */
+};
+
+enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
+enum spec_layer_kind { SPEC_LAYER_ATTN = 0, SPEC_LAYER_GDN = 1 };
+enum spec_mode { SPEC_GREEDY = 0, SPEC_SAMPLED = 1 };
+
+/* Kernel classes that spec_profile_enable can time. */
+enum spec_kernel_class {
+  SPEC_K_NONE = -1,
+  SPEC_K_PROJ_IN = 0,   /* QKV / gated-delta-rule input projection */
+  SPEC_K_ATTN = 1,      /* verify attention */
+  SPEC_K_PROJ_O = 2,    /* attention / recurrent output projection */
+  SPEC_K_GATE_UP = 3,   /* SwiGLU gate+up projection */
+  SPEC_K_DOWN = 4,      /* MLP down projection */
+  SPEC_K_LM_HEAD = 5,   /* fused LM head statistics */
+  SPEC_K_GDN = 6,       /* gated-delta-rule column recurrence */
+  SPEC_K_COUNT = 7
+};
+
+/* Weights of one decoder layer.  Device pointers, row-major [out][in], element
+ * type = the model dtype unless noted; borrowed, never freed by the library.
+ *   norm1, norm2: float [hidden] RMSNorm gains.
+ *   w_in:   full attention: [(n_q + 2 n_kv) * head_dim][hidden], rows = q heads,
+ *           then k heads, then v heads;
+ *           gated delta rule: [3 * gdn_heads * gdn_dim + 2 * gdn_heads][hidden],
+ *           rows = q, k, v (head-major), then one alpha row and one beta row per head.
+ *   w_o:    [hidden][n_q * head_dim]  or  [hidden][gdn_heads * gdn_dim].
+ *   w_gate, w_up: [ffn][hidden];  w_down: [hidden][ffn]. */
+typedef struct {
+  const float* norm1;
+  const void* w_in;
+  const void* w_o;
+  const float* norm2;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} spec_layer_weights;
+
+/* Model description (copied by spec_model_create; pointers are borrowed).
+ * Decoder: RMSNorm -> (GQA attention with rotate-half RoPE | gated delta rule)
+ * -> residual; RMSNorm -> SwiGLU MLP -> residual; final RMSNorm -> LM head.
+ * Gated delta rule (Yang et al. 2024): alpha = sigmoid(h.w_alpha),
+ * beta = sigmoid(h.w_beta), q = q~/|q~| * d^-1/2, k = k~/|k~|,
+ * S_t = alpha S + beta (v - alpha S k) k^T, o_t = S_t q_t. */
+typedef struct {
+  int n_layers;            /* >= 0; 0 = LM head only (spec_verify_head) */
+  int hidden;              /* multiple of 32 */
+  int n_q_heads, n_kv_heads, head_dim;   /* head_dim 128 (bf16) or <= 128 (f32) */
+  int ffn;                 /* multiple of 32 */
+  int vocab;               /* multiple of 16 */
+  int dtype;               /* SPEC_F32 | SPEC_BF16: weights, KV, stored activations */
+  const int32_t* layer_kind;   /* host [n_layers]: SPEC_LAYER_ATTN | SPEC_LAYER_GDN */
+  int gdn_heads, gdn_dim;  /* gdn_dim 128 when any layer is SPEC_LAYER_GDN */
+  float rms_eps;           /* e.g. 1e-6 */
+  float rope_theta;        /* 0 = no positional encoding */
+  int kv_block;            /* must be SPEC_KV_BLOCK */
+  int attn_chunk;          /* positions per split-KV chunk (multiple of 256); 0 = 1024 */
+  const void* embed;       /* [vocab][hidden]; may be NULL for a head-only model */
+  const void* lm_head;     /* [vocab][hidden] */
+  const float* final_norm; /* [hidden]; may be NULL for a head-only model */
+  const spec_layer_weights* layers;   /* host [n_layers] */
+} spec_model_desc;
+
+typedef struct spec_model spec_model;
+
+/* One verify round.  Device buffers are read (and, by spec_commit, written)
+ * asynchronously on the stream; host arrays are read during the call only.
+ *
+ * Paged KV layout (element type = model dtype), per full-attention layer a
+ * slice of n_blocks blocks, layers in order:
+ *   k_pool [n_attn_layers][n_blocks][n_kv][16 slots][head_dim]
+ *   v_pool [n_attn_layers][n_blocks][n_kv][head_dim][16 slots]
+ * Token position p of lane l lives in block block_table[l * max_blocks + p/16],
+ * slot p % 16.  Block ids must lie in [0, n_blocks); kernels clamp others.
+ * Recurrent state (float): gdn_state [lanes][n_gdn_layers][gdn_heads][dv][dk]. */
+typedef struct {
+  int lanes;                   /* 1 .. SPEC_MAX_LANES */
+  const int32_t* cols_host;    /* host [lanes]: k_l + 1 in [1, SPEC_MAX_COLS]; sum <= SPEC_MAX_ROWS */
+  const int32_t* tokens;       /* device [R]: anchor then drafts per lane, lane-major */
+  int32_t* kv_len;             /* device [lanes]: committed length; the anchor sits at position kv_len */
+  const int32_t* kv_len_host;  /* host [lanes] mirror for the capacity check; NULL skips it */
+  const int32_t* block_table;  /* device [lanes][max_blocks] */
+  int max_blocks;              /* block-table width; capacity = 16 * max_blocks positions */
+  void* k_pool;                /* device; NULL iff the model has no attention layer */
+  void* v_pool;
+  int n_blocks;                /* blocks per layer slice of the pools */
+  float* gdn_state;            /* device; NULL iff the model has no recurrent layer */
+  int mode;                    /* SPEC_GREEDY | SPEC_SAMPLED */
+  float temperature;           /* sampled: > 0; p = softmax(z / T) */
+  const float* q_probs;        /* sampled: device [R][vocab], row of column j >= 1 = the
+                                  drafter's q for draft d_j (column-0 rows unused) */
+  uint64_t seed;               /* Philox4x32-10 key */
+  void* workspace;             /* device, >= spec_workspace_bytes; 256-byte aligned */
+  size_t workspace_bytes;
+} spec_round;
+
+/* Per-row statistics of the LM head (T = 1 in greedy mode). */
+typedef struct {
+  float max_logit;   /* max_v z_v */
+  float lse;         /* log sum_v exp(z_v / T) */
+  int32_t argmax;    /* lowest index among the maxima */
+  float z_next;      /* z at the row's next draft token; NaN on a lane's last row */
+} spec_row_stat;
+
+const char* spec_status_string(int status);
+
+/* Row-budget planner ("The row budget", gpillon.github.io/ignis):
+ * returns min(k, max(0, rows / lanes - 1)) with integer division and rows =
+ * row_budget, or 8 when row_budget == 0.  Errors (lanes <= 0, k < 0,
+ * row_budget < 0) return SPEC_E_INVAL.  Pure host function. */
+int spec_plan_drafts(int k, int row_budget, int lanes);
+
+/* Validates and copies a model description into a host object.  No HIP call. */
+int spec_model_create(const spec_model_desc* desc, spec_model** out);
+void spec_model_destroy(spec_model* model);
+
+/* Workspace bytes for rounds of up to max_lanes lanes, max_cols columns per lane
+ * and block tables max_blocks wide.  Returns a negative status on error.  The
+ * workspace also carries the staged columns from spec_verify_round to
+ * spec_commit: pass the same workspace, unmodified, to the calls of one round. */
+int64_t spec_workspace_bytes(const spec_model* model, int max_lanes, int max_cols, int max_blocks);
+
+/* The verify forward: every row through every layer once, then the fused LM
+ * head's per-row statistics (logits are never written to memory).  Reads the
+ * KV pools and recurrent state, writes neither; stages each column's K/V and
+ * recurrent inputs in the workspace.  Errors: SPEC_E_INVAL (lanes, cols,
+ * NULL buffers, sampled without q_probs or with T <= 0), SPEC_E_RANGE
+ * (kv_len_host + cols exceeds 16 * max_blocks), SPEC_E_UNSUPPORTED (recurrent
+ * layers with gdn_state == NULL), SPEC_E_WORKSPACE. */
+int spec_verify_round(const spec_model* model, const spec_round* round, void* stream);
+
+/* The LM head and row statistics alone, on caller-given final hidden states
+ * `hidden` (device [R][hidden], model dtype; no final norm is applied).  Same
+ * round fields as spec_verify_round except the KV/state ones, which are unused. */
+int spec_verify_head(const spec_model* model, const spec_round* round, const void* hidden,
+                     void* stream);
+
+/* Acceptance.  Greedy: per lane the longest prefix of drafts equal to the
+ * argmax of the row before, then the argmax at the first mismatch (or after the
+ * last draft).  Sampled: draft d_i is kept iff u * q_i(d_i) < p_{i-1}(d_i), with
+ * u the Philox uniform at (seed, position kv_len + i, lane); on the first
+ * rejection the token is drawn from max(0, p - q) by an exponential race;
+ * with every draft kept the bonus token is drawn from p_k.
+ * Outputs (device): committed[lanes] in [1, cols]; out_tokens[lanes][SPEC_MAX_COLS]
+ * holds the committed run (kept drafts, then the model's token); row_stats
+ * [R] (may be NULL).  Must follow spec_verify_round / spec_verify_head of the
+ * same round and workspace. */
+int spec_accept(const spec_model* model, const spec_round* round, int32_t* committed,
+                int32_t* out_tokens, spec_row_stat* row_stats, void* stream);
+
+/* Commit: for each lane copies the staged K/V of columns 0 .. committed-1 into
+ * the paged cache at positions kv_len .. kv_len + committed - 1, replays the
+ * same columns through the recurrent state, then kv_len += committed.
+ * committed is read on the device (no host round trip); values are clamped to
+ * [1, cols].  Rejected columns leave no trace. */
+int spec_commit(const spec_model* model, const spec_round* round, const int32_t* committed,
+                void* stream);
+
+/* Tests only: the verify forward, then the full logits float [R][vocab]. */
+int spec_debug_logits(const spec_model* model, const spec_round* round, float* logits,
+                      void* stream);
+
+/* Tests and measurement: the skinny projection kernel alone, Y[R][N] = X[R][K] W[N][K]^T
+ * (X, W in the model dtype, Y float), with the split and launch shape the round
+ * uses for an [N][K] weight.  R <= SPEC_MAX_ROWS.  `workspace` must hold
+ * spec_workspace_bytes(model, 1, R, 1) bytes or more. */
+int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float* Y, int R,
+                    int N, int K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement: record HIP events around every launch of one kernel class
+ * (SPEC_K_NONE stops recording), and read back the summed duration of the
+ * launches recorded since the last enable (synchronises on those events). */
+int spec_profile_enable(spec_model* model, int kernel_class);
+int spec_profile_collect(spec_model* model, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

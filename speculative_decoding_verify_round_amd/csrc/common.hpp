@@ -1,0 +1,210 @@
+// Shared device helpers and launch-parameter structs of the verify-round kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kMaxRows = 64;
+constexpr int kMaxCols = 16;
+constexpr int kMaxLanes = 64;
+constexpr int kBlock = 16;       // tokens per paged-KV block
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Packed lane-major row layout of a round, passed by value in kernel arguments.
+struct RowInfo {
+  int R;                         // rows
+  int L;                         // lanes
+  int8_t row_lane[kMaxRows];
+  int8_t row_col[kMaxRows];
+  int16_t lane_start[kMaxLanes + 1];
+  int8_t lane_cols[kMaxLanes];
+};
+
+// ----------------------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float ld_act(const float* p) { return *p; }
+__device__ __forceinline__ float ld_act(const bf16_t* p) { return bf2f(*p); }
+__device__ __forceinline__ void st_act(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st_act(bf16_t* p, float v) { *p = f2bf(v); }
+
+// D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
+// Lane i supplies A row (i % 16) and B column (i % 16), eight K elements each
+// (the K index of element e is 8 * (i / 16) + e for both operands); lane i
+// receives D[4 * (i / 16) + e][i % 16] for e = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Block-wide sum with a fixed reduction tree (deterministic); `red` holds >= 32 floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+__device__ __forceinline__ int clamp_blk(int b, int n) { return b < 0 ? 0 : (b >= n ? n - 1 : b); }
+
+// (value, index) order used by every argmax: larger value wins, lower index on ties.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// ----------------------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror & Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
+// Counter = (position, lane, purpose, block), key = (seed lo, seed hi).
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+constexpr uint32_t kPurposeAccept = 0u, kPurposeRace = 1u;
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = kPhiloxM0 * c[0], hi0 = __umulhi(kPhiloxM0, c[0]);
+    const uint32_t lo1 = kPhiloxM1 * c[2], hi1 = __umulhi(kPhiloxM1, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    k0 += kPhiloxW0; k1 += kPhiloxW1;
+  }
+}
+
+// Uniform in (0, 1), exact in float32: ((w >> 9) + 0.5) * 2^-23.
+__device__ __forceinline__ float u01(uint32_t w) {
+  return ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
+}
+
+// ----------------------------------------------------------------------------- launch parameters
+struct GemmParams {
+  const bf16_t* X;      // [R][K] activations (bf16)
+  const bf16_t* W0;     // [N][K]
+  const bf16_t* W1;     // [N][K] second matrix (gate/up) or null
+  int R, N, K;
+  int S;                // k-splits, each a whole number of 256-wide chunks
+  int groups;           // N / 16
+  float* P;             // [S][R][N] fp32 partials
+  bf16_t* Yb;           // [R][N] SwiGLU output (bf16)
+};
+
+struct GemmF32Params {
+  const float* X; const float* W0; const float* W1;
+  int R, N, K;
+  float* P;             // [1][R][N]
+  float* Ya;            // [R][N] SwiGLU output (fp32 model)
+};
+
+// Device-side mirror of the public spec_row_stat.
+struct spec_row_stat_dev {
+  float max_logit;
+  float lse;
+  int32_t argmax;
+  float z_next;
+};
+
+// Per-(row, group) partial statistics of the LM head.
+struct LmPartial {
+  float m;     // max logit in the group
+  float se;    // sum exp((z - m) / T) over the group
+  int arg;     // lowest-index argmax in the group
+  float zn;    // logit of the row's next draft token if it falls in the group, else NaN
+  float gk;    // best bonus race key z/T - ln(-ln U) in the group (bonus rows only)
+  int gi;      // its index
+  int pad0, pad1;
+};
+
+struct LmParams {
+  const void* X;           // [R][H] final hidden (act dtype)
+  const void* W;           // [V][H]
+  int R, V, H;
+  int groups;              // number of partial groups per row
+  const int32_t* tokens;   // [R] round tokens (next-draft lookup)
+  const int32_t* kv_len;   // [L]
+  float inv_t;             // 1 / T (1 in greedy mode)
+  int sampled;
+  uint32_t key0, key1;     // Philox key
+  LmPartial* part;         // [R][groups]
+  RowInfo ri;
+};
+
+// Row statistics after reducing the LM-head partials (internal workspace form).
+struct RowStat {
+  float m, se, zn, gk;
+  int arg, gi, pad0, pad1;
+};
+
+// Per-lane acceptance decision (internal).
+struct LaneDecision {
+  int committed;        // c in [1, cols]
+  int resid_row;        // row whose residual must be drawn, -1 if none
+  int resid_col;        // draft index i of the rejection (position kv_len + i)
+  int pad;
+  float m, se;          // stats of resid_row
+  float pad2, pad3;
+};
+
+struct RaceParams {
+  const void* X;           // [R][H]
+  const void* W;           // [V][H]
+  int V, H, L;
+  int groups;
+  const float* q;          // [R][V]
+  const int32_t* kv_len;
+  float inv_t;
+  uint32_t key0, key1;
+  const LaneDecision* dec; // [L]
+  float* part;             // [L][groups][4]: residual key, index, fallback key, index
+  RowInfo ri;
+};
+
+struct AttnParams {
+  const void* q;          // [R][nq][d]
+  const void* sk;         // staged K [R][nkv][d]
+  const void* sv;         // staged V [R][nkv][d]
+  const void* kpool;      // layer slice [n_blocks][nkv][16][d]
+  const void* vpool;      // layer slice [n_blocks][nkv][d][16]
+  const int32_t* block_table;
+  int max_blocks, n_blocks;
+  const int32_t* kv_len;
+  int nq, nkv, G, d;
+  int chunk;              // positions per workgroup chunk
+  int n_chunks;           // chunks per lane (grid x)
+  float scale_log2;       // log2(e) / sqrt(d)
+  float* part;            // [L][nkv][n_chunks][64][d + 2]
+  RowInfo ri;
+};
+
+}  // namespace sv

@@ -1,0 +1,353 @@
+// Per-row layer kernels of the verify round and the commit (gfx950).
+//
+//   embed + RMSNorm, split-K reduce + residual + RMSNorm, the RoPE table,
+//   QKV post-processing (rotation, rounding, K/V staging), the gated-delta-rule
+//   column recurrence (verify) and its replay (commit), and the KV compaction.
+//
+// Commit follows "Speculative decoding" (gpillon.github.io/ignis), step 5: the
+// state moves forward by exactly the committed run; attention layers keep the
+// keys of every committed column and recurrent layers replay only the
+// committed prefix, so a rejected column leaves no trace.  The FreeToken
+// tracking issue ("Per-request state") fixes the split: verify only reads the
+// live state and stages scratch, commit rolls the state to the accepted count.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sv {
+
+// ------------------------------------------------------------------------------- RoPE table
+// cos/sin of pos * theta^(-2i/d) for every row, evaluated in double precision.
+__global__ void k_rope_table(const int32_t* kv_len, RowInfo ri, int d, double theta, float* table) {
+  const int r = blockIdx.x, i = threadIdx.x;
+  if (i >= d / 2) return;
+  const int l = ri.row_lane[r];
+  const double pos = (double)(kv_len[l] + ri.row_col[r]);
+  const double ang = pos * pow(theta, -2.0 * (double)i / (double)d);
+  table[((size_t)r * (d / 2) + i) * 2 + 0] = (float)cos(ang);
+  table[((size_t)r * (d / 2) + i) * 2 + 1] = (float)sin(ang);
+}
+
+int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, float* table,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(k_rope_table, dim3(ri.R), dim3(64), 0, st, kv_len, ri, d, (double)theta, table);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------------------- RMSNorm family
+template <typename T>
+__device__ __forceinline__ void norm_row(const float* x, int H, const float* gain, float eps, T* h, float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
+  const float tot = block_sum(ss, red);
+  const float rs = rsqrtf(tot / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += blockDim.x) st_act(h + i, x[i] * rs * gain[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tokens, const T* embed, int V, int H,
+                                                     const float* gain, float eps, float* x, T* h) {
+  __shared__ float red[32];
+  const int r = blockIdx.x;
+  int tok = tokens[r];
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+  float* xr = x + (size_t)r * H;
+  const T* e = embed + (size_t)tok * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = ld_act(e + i);
+  __syncthreads();
+  norm_row(xr, H, gain, eps, h + (size_t)r * H, red);
+}
+
+int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
+                      float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(ri.R), dim3(256), 0, st, tokens,
+                       reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h));
+  else
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(ri.R), dim3(256), 0, st, tokens,
+                       reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// x[r] += sum_s P[s][r] (s in order), then h[r] = round(rmsnorm(x[r]) * gain)
+template <typename T>
+__global__ __launch_bounds__(256) void k_resid_norm(const float* P, int S, int R, float* x, int H,
+                                                     const float* gain, float eps, T* h) {
+  __shared__ float red[32];
+  const int r = blockIdx.x;
+  float* xr = x + (size_t)r * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    float t = P[(size_t)r * H + i];
+    for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * H + i];
+    xr[i] = xr[i] + t;
+  }
+  __syncthreads();
+  norm_row(xr, H, gain, eps, h + (size_t)r * H, red);
+}
+
+int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
+                      const RowInfo& ri, bool bf16, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, x, H, gain, eps,
+                       reinterpret_cast<bf16_t*>(h));
+  else
+    hipLaunchKernelGGL(k_resid_norm<float>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, x, H, gain, eps,
+                       reinterpret_cast<float*>(h));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------------------- QKV post
+// Sum the split-K partials of [q | k | v], rotate q and k (rotate-half, pair (i, i + d/2)),
+// round to the storage type, write q and stage K/V of every column.
+template <typename T>
+__global__ __launch_bounds__(256) void k_qkv_post(const float* P, int S, int R, const float* rope, int use_rope,
+                                                   int nq, int nkv, int d, T* q, T* sk, T* sv) {
+  const int r = blockIdx.x;
+  const int N = (nq + 2 * nkv) * d, half = d / 2;
+  auto sum = [&](int n) {
+    float t = P[(size_t)r * N + n];
+    for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * N + n];
+    return t;
+  };
+  // rotated heads: q heads then k heads, processed as (head, pair) items
+  const int npairs = (nq + nkv) * half;
+  for (int it = threadIdx.x; it < npairs; it += blockDim.x) {
+    const int hd = it / half, i = it - hd * half;
+    const float a = sum(hd * d + i), b = sum(hd * d + i + half);
+    float ra = a, rb = b;
+    if (use_rope) {
+      const float c = rope[((size_t)r * half + i) * 2], s = rope[((size_t)r * half + i) * 2 + 1];
+      ra = a * c - b * s;
+      rb = b * c + a * s;
+    }
+    T* dst = hd < nq ? q + ((size_t)r * nq + hd) * d : sk + ((size_t)r * nkv + (hd - nq)) * d;
+    st_act(dst + i, ra);
+    st_act(dst + i + half, rb);
+  }
+  for (int it = threadIdx.x; it < nkv * d; it += blockDim.x)
+    st_act(sv + (size_t)r * nkv * d + it, sum((nq + nkv) * d + it));
+}
+
+int launch_qkv_post(const float* P, int S, const float* rope, int use_rope, int nq, int nkv, int d,
+                    void* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
+                       reinterpret_cast<bf16_t*>(q), reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv));
+  else
+    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
+                       reinterpret_cast<float*>(q), reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------------------- gated delta rule
+// State S is [dv][dk] fp32 per (lane, head); thread t owns row i = t / 2, columns
+// [64 (t % 2), 64 (t % 2) + 64).  One column step (Yang et al., Gated DeltaNet):
+//   S <- alpha S + beta (v - alpha S k) k^T.
+// Verify and commit run this exact function on the exact staged inputs, so the
+// committed state is bitwise the state verify saw at the last committed column.
+constexpr int kGdnDim = 128;
+
+__device__ __forceinline__ float gdn_rowdot(const float (&s)[64], const float* vec, int half) {
+#pragma clang fp contract(off)
+  float part = 0.f;
+#pragma unroll
+  for (int c = 0; c < 64; ++c) part = __builtin_fmaf(s[c], vec[64 * half + c], part);
+  const float other = __shfl_xor(part, 1);
+  return half == 0 ? part + other : other + part;   // (low half) + (high half) on both threads
+}
+
+__device__ __forceinline__ void gdn_update(float (&s)[64], const float* kn, int half, float v_i, float alpha,
+                                           float beta) {
+#pragma clang fp contract(off)
+  const float sk = gdn_rowdot(s, kn, half);
+  const float coef = beta * (v_i - alpha * sk);
+#pragma unroll
+  for (int c = 0; c < 64; ++c) s[c] = __builtin_fmaf(alpha, s[c], coef * kn[64 * half + c]);
+}
+
+// stage layout per (row, head): kn[128], v[128], alpha, beta  (kGdnStage floats)
+constexpr int kGdnStage = 2 * kGdnDim + 2;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowInfo ri, int hg, const float* state,
+                                                     int n_gdn, int gi, float* stage, T* o) {
+  __shared__ float qn[kGdnDim], kn[kGdnDim], vv[kGdnDim], red[32], ab[2];
+  const int h = blockIdx.x, l = blockIdx.y;
+  const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
+  const int R = ri.R;
+  const int N = 3 * hg * kGdnDim + 2 * hg;
+  const float* S0 = state + (((size_t)l * n_gdn + gi) * hg + h) * kGdnDim * kGdnDim + (size_t)row_i * kGdnDim + 64 * half;
+  float s[64];
+#pragma unroll
+  for (int c = 0; c < 64; c += 4) {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + c);
+    s[c] = v4[0]; s[c + 1] = v4[1]; s[c + 2] = v4[2]; s[c + 3] = v4[3];
+  }
+  const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
+  for (int j = 0; j < cols; ++j) {
+    const int r = rs + j;
+    auto sum = [&](int n) {
+      float a = P[(size_t)r * N + n];
+      for (int ss = 1; ss < S; ++ss) a += P[((size_t)ss * R + r) * N + n];
+      return a;
+    };
+    float qv = 0.f, kv = 0.f;
+    if (t < kGdnDim) {
+      qv = sum(h * kGdnDim + t);
+      kv = sum(hg * kGdnDim + h * kGdnDim + t);
+      vv[t] = sum(2 * hg * kGdnDim + h * kGdnDim + t);
+    }
+    if (t == 0) {
+      ab[0] = 1.f / (1.f + expf(-sum(3 * hg * kGdnDim + h)));
+      ab[1] = 1.f / (1.f + expf(-sum(3 * hg * kGdnDim + hg + h)));
+    }
+    const float qq = block_sum(qv * qv, red);
+    const float kk = block_sum(kv * kv, red);
+    const float rq = rsqrtf(qq + 1e-6f) * rsqrtf((float)kGdnDim);
+    const float rk = rsqrtf(kk + 1e-6f);
+    if (t < kGdnDim) { qn[t] = qv * rq; kn[t] = kv * rk; }
+    __syncthreads();
+    const float alpha = ab[0], beta = ab[1];
+    float* stg = stage + ((size_t)r * hg + h) * kGdnStage;
+    if (t < kGdnDim) { stg[t] = kn[t]; stg[kGdnDim + t] = vv[t]; }
+    if (t == 0) { stg[2 * kGdnDim] = alpha; stg[2 * kGdnDim + 1] = beta; }
+    gdn_update(s, kn, half, vv[row_i], alpha, beta);
+    const float oi = gdn_rowdot(s, qn, half);
+    if (half == 0) st_act(o + ((size_t)r * hg + h) * kGdnDim + row_i, oi);
+    __syncthreads();
+  }
+}
+
+int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state, int n_gdn, int gi,
+                      float* stage, void* o, const RowInfo& ri, bool bf16, hipStream_t st) {
+  (void)dg;
+  dim3 grid(hg, ri.L), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_gdn_verify<bf16_t>, grid, block, 0, st, P, S, ri, hg, state, n_gdn, gi, stage,
+                       reinterpret_cast<bf16_t*>(o));
+  else
+    hipLaunchKernelGGL(k_gdn_verify<float>, grid, block, 0, st, P, S, ri, hg, state, n_gdn, gi, stage,
+                       reinterpret_cast<float*>(o));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// commit: replay columns 0 .. c-1 of every gated-delta-rule layer from the staged inputs
+__global__ __launch_bounds__(256) void k_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg,
+                                                     const float* stage, size_t stage_layer_stride, RowInfo ri) {
+  __shared__ float kn[kGdnDim], vv[kGdnDim], ab[2];
+  const int h = blockIdx.x, l = blockIdx.y, gi = blockIdx.z;
+  const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
+  const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
+  const int c = max(1, min(committed[l], cols));
+  float* S0 = state + (((size_t)l * n_gdn + gi) * hg + h) * kGdnDim * kGdnDim + (size_t)row_i * kGdnDim + 64 * half;
+  float s[64];
+#pragma unroll
+  for (int q = 0; q < 64; q += 4) {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + q);
+    s[q] = v4[0]; s[q + 1] = v4[1]; s[q + 2] = v4[2]; s[q + 3] = v4[3];
+  }
+  const float* stl = stage + gi * stage_layer_stride;
+  for (int j = 0; j < c; ++j) {
+    const float* stg = stl + ((size_t)(rs + j) * hg + h) * kGdnStage;
+    if (t < kGdnDim) { kn[t] = stg[t]; vv[t] = stg[kGdnDim + t]; }
+    if (t < 2) ab[t] = stg[2 * kGdnDim + t];
+    __syncthreads();
+    gdn_update(s, kn, half, vv[row_i], ab[0], ab[1]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 64; q += 4) *reinterpret_cast<f32x4*>(S0 + q) = f32x4{s[q], s[q + 1], s[q + 2], s[q + 3]};
+}
+
+int launch_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg, int dg, const float* stage,
+                      size_t stage_layer_stride, const RowInfo& ri, hipStream_t st) {
+  (void)dg;
+  dim3 grid(hg, ri.L, n_gdn), block(256);
+  hipLaunchKernelGGL(k_gdn_replay, grid, block, 0, st, committed, state, n_gdn, hg, stage, stage_layer_stride, ri);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------------------- KV compaction
+// Staged K/V of columns 0 .. c-1 -> paged cache at positions kv_len .. kv_len + c - 1.
+// K blocks are [slot][d], V blocks are [d][slot].
+template <typename T>
+__global__ __launch_bounds__(256) void k_commit_kv(const int32_t* committed, const int32_t* kv_len,
+                                                    const int32_t* block_table, int max_blocks, int n_blocks,
+                                                    T* kpool, T* vpool, int nkv, int d, const T* sk, const T* sv,
+                                                    size_t stage_layer_elems, RowInfo ri) {
+  const int l = blockIdx.x, li = blockIdx.y;
+  const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
+  const int c = max(1, min(committed[l], cols));
+  const int cap = max_blocks * kBlock;
+  const int kvl = max(0, min(kv_len[l], cap - cols));
+  const size_t layer_pool = (size_t)n_blocks * nkv * kBlock * d;
+  T* kp = kpool + li * layer_pool;
+  T* vp = vpool + li * layer_pool;
+  const T* skl = sk + li * stage_layer_elems;
+  const T* svl = sv + li * stage_layer_elems;
+  const int per_col = nkv * d;
+  for (int it = threadIdx.x; it < c * per_col; it += blockDim.x) {
+    const int j = it / per_col, rem = it - j * per_col;
+    const int g = rem / d, dd = rem - g * d;
+    const int pos = kvl + j;
+    const int blk = clamp_blk(block_table[(size_t)l * max_blocks + (pos >> 4)], n_blocks);
+    const size_t src = ((size_t)(rs + j) * nkv + g) * d + dd;
+    kp[(((size_t)blk * nkv + g) * kBlock + (pos & 15)) * d + dd] = skl[src];
+    vp[(((size_t)blk * nkv + g) * d + dd) * kBlock + (pos & 15)] = svl[src];
+  }
+}
+
+int launch_commit_kv(const int32_t* committed, const int32_t* kv_len, const int32_t* block_table, int max_blocks,
+                     int n_blocks, void* kpool, void* vpool, int n_attn, int nkv, int d, const void* sk,
+                     const void* sv, size_t stage_layer_elems, const RowInfo& ri, bool bf16, hipStream_t st) {
+  dim3 grid(ri.L, n_attn), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_commit_kv<bf16_t>, grid, block, 0, st, committed, kv_len, block_table, max_blocks, n_blocks,
+                       reinterpret_cast<bf16_t*>(kpool), reinterpret_cast<bf16_t*>(vpool), nkv, d,
+                       reinterpret_cast<const bf16_t*>(sk), reinterpret_cast<const bf16_t*>(sv),
+                       stage_layer_elems, ri);
+  else
+    hipLaunchKernelGGL(k_commit_kv<float>, grid, block, 0, st, committed, kv_len, block_table, max_blocks, n_blocks,
+                       reinterpret_cast<float*>(kpool), reinterpret_cast<float*>(vpool), nkv, d,
+                       reinterpret_cast<const float*>(sk), reinterpret_cast<const float*>(sv),
+                       stage_layer_elems, ri);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void k_kvlen_update(const int32_t* committed, int32_t* kv_len, RowInfo ri) {
+  const int l = threadIdx.x;
+  if (l < ri.L) kv_len[l] += max(1, min(committed[l], (int)ri.lane_cols[l]));
+}
+
+int launch_kvlen_update(const int32_t* committed, int32_t* kv_len, const RowInfo& ri, hipStream_t st) {
+  hipLaunchKernelGGL(k_kvlen_update, dim3(1), dim3(64), 0, st, committed, kv_len, ri);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void k_sum_partials(const float* P, int S, size_t n, float* Y) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    float t = P[i];
+    for (int s = 1; s < S; ++s) t += P[(size_t)s * n + i];
+    Y[i] = t;
+  }
+}
+
+int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st) {
+  const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+  hipLaunchKernelGGL(k_sum_partials, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, P, S, n, Y);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void k_copy_words(const uint32_t* src, uint32_t* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+int launch_copy_rows(const void* src, void* dst, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_copy_words, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), n);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace sv

@@ -1,0 +1,565 @@
+// C ABI of the verify round: validation, the row-budget planner, workspace
+// layout and the launch sequence on the caller's stream.  No device memory is
+// allocated here; the caller owns every device buffer.
+#include "../../include/spec_verify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+static_assert(sizeof(spec_row_stat) == sizeof(sv::spec_row_stat_dev), "row stat mirror");
+static_assert(sizeof(sv::LmPartial) == 32, "partial size");
+
+namespace {
+
+constexpr int kDefaultChunk = 1024;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layer {
+  int kind;
+  spec_layer_weights w;
+  int attn_index;   // index among attention layers, or -1
+  int gdn_index;    // index among gated-delta-rule layers, or -1
+};
+
+// K split of one projection: a function of (N, K) only, so results never depend on R.
+struct Split {
+  int S;
+};
+
+}  // namespace
+
+struct spec_model {
+  spec_model_desc d;
+  std::vector<int32_t> kinds;
+  std::vector<Layer> layers;
+  int n_attn = 0, n_gdn = 0;
+  bool bf16 = false;
+  int chunk = kDefaultChunk;
+  Split s_in_attn{1}, s_in_gdn{1}, s_o_attn{1}, s_o_gdn{1}, s_gateup{1}, s_down{1};
+  int lm_groups = 1;
+  // profiling
+  int prof_class = SPEC_K_NONE;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_events;
+  std::vector<hipEvent_t> prof_pool;
+  size_t prof_used = 0;
+};
+
+namespace {
+
+int split_for(const spec_model* m, int N, int K, bool fused_pair) {
+  if (!m->bf16 || fused_pair) return 1;
+  const int groups = (N + 15) / 16;
+  const int chunks = K / 256;
+  // aim for ~2048 waves (8 per CU) of at least one 256-wide chunk each
+  int S = (int)std::lround(2048.0 / groups);
+  S = std::max(1, std::min(S, chunks));
+  return S;
+}
+
+struct WsLayout {
+  size_t x, h, P, q, o, a, rope, stk, stv, gst, apart, lmp, rstat, dec, racep, total;
+  size_t stage_layer_elems;     // elements per attention layer in stk/stv
+  size_t gst_layer_floats;      // floats per gdn layer in gst
+  int n_chunks;
+};
+
+size_t act_bytes(const spec_model* m) { return m->bf16 ? 2 : 4; }
+
+WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
+  const spec_model_desc& d = m->d;
+  const size_t ab = act_bytes(m);
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
+  const size_t H = d.hidden;
+  const size_t qdim = (size_t)d.n_q_heads * d.head_dim;
+  const size_t gdim = (size_t)d.gdn_heads * d.gdn_dim;
+  size_t pmax = 0;   // max S * N over partial-producing projections
+  if (m->n_attn) {
+    pmax = std::max(pmax, (size_t)m->s_in_attn.S * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim);
+    pmax = std::max(pmax, (size_t)m->s_o_attn.S * H);
+  }
+  if (m->n_gdn) {
+    pmax = std::max(pmax, (size_t)m->s_in_gdn.S * (3 * gdim + 2 * d.gdn_heads));
+    pmax = std::max(pmax, (size_t)m->s_o_gdn.S * H);
+  }
+  if (d.n_layers) pmax = std::max(pmax, (size_t)m->s_down.S * H);
+  w.x = take((size_t)R * H * 4);
+  w.h = take((size_t)R * H * ab);
+  w.P = take((size_t)R * pmax * 4);
+  w.q = take((size_t)R * qdim * ab);
+  w.o = take((size_t)R * std::max(qdim, gdim) * ab);
+  w.a = take((size_t)R * d.ffn * ab);
+  w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 4);
+  w.stage_layer_elems = (size_t)R * d.n_kv_heads * d.head_dim;
+  w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
+  w.stv = take((size_t)m->n_attn * w.stage_layer_elems * ab);
+  w.gst_layer_floats = (size_t)R * d.gdn_heads * (2 * 128 + 2);
+  w.gst = take((size_t)m->n_gdn * w.gst_layer_floats * 4);
+  w.n_chunks = m->n_attn ? (max_blocks * SPEC_KV_BLOCK + m->chunk - 1) / m->chunk : 0;
+  w.apart = take((size_t)L * d.n_kv_heads * w.n_chunks * 64 * (d.head_dim + 2) * 4);
+  w.lmp = take((size_t)R * m->lm_groups * sizeof(sv::LmPartial));
+  w.rstat = take((size_t)R * sizeof(sv::RowStat));
+  w.dec = take((size_t)L * sizeof(sv::LaneDecision));
+  w.racep = take((size_t)L * m->lm_groups * 16);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off); }
+
+bool valid_layer(const spec_layer_weights& w) {
+  return w.norm1 && w.w_in && w.w_o && w.norm2 && w.w_gate && w.w_up && w.w_down;
+}
+
+int build_rowinfo(const spec_round* r, sv::RowInfo& ri) {
+  if (!r || r->lanes < 1 || r->lanes > SPEC_MAX_LANES || !r->cols_host) return SPEC_E_INVAL;
+  std::memset(&ri, 0, sizeof(ri));
+  int R = 0;
+  ri.L = r->lanes;
+  for (int l = 0; l < r->lanes; ++l) {
+    const int c = r->cols_host[l];
+    if (c < 1 || c > SPEC_MAX_COLS) return SPEC_E_INVAL;
+    if (R + c > SPEC_MAX_ROWS) return SPEC_E_INVAL;
+    ri.lane_start[l] = (int16_t)R;
+    ri.lane_cols[l] = (int8_t)c;
+    for (int j = 0; j < c; ++j) {
+      ri.row_lane[R + j] = (int8_t)l;
+      ri.row_col[R + j] = (int8_t)j;
+    }
+    R += c;
+  }
+  ri.lane_start[r->lanes] = (int16_t)R;
+  ri.R = R;
+  return SPEC_OK;
+}
+
+int max_cols(const sv::RowInfo& ri) {
+  int c = 0;
+  for (int l = 0; l < ri.L; ++l) c = std::max(c, (int)ri.lane_cols[l]);
+  return c;
+}
+
+// Common validation of a round; fills ri and the workspace layout.
+int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri, WsLayout& w) {
+  if (!m) return SPEC_E_INVAL;
+  int st = build_rowinfo(r, ri);
+  if (st) return st;
+  if (!r->tokens || !r->kv_len) return SPEC_E_INVAL;
+  if (r->mode != SPEC_GREEDY && r->mode != SPEC_SAMPLED) return SPEC_E_INVAL;
+  if (r->mode == SPEC_SAMPLED) {
+    if (!r->q_probs || !(r->temperature > 0.f) || !std::isfinite(r->temperature)) return SPEC_E_INVAL;
+  }
+  const int mb = head_only ? 1 : r->max_blocks;
+  if (!head_only) {
+    if (m->d.n_layers == 0) return SPEC_E_INVAL;
+    if (m->n_attn) {
+      if (!r->block_table || !r->k_pool || !r->v_pool || r->max_blocks < 1 || r->n_blocks < 1)
+        return SPEC_E_INVAL;
+      const int G = m->d.n_q_heads / m->d.n_kv_heads;
+      const int mq = max_cols(ri) * G;
+      if (m->bf16 && mq > 64) return SPEC_E_UNSUPPORTED;
+      if (!m->bf16 && (size_t)4 * mq * (m->d.head_dim + 2) * 4 > 65536) return SPEC_E_UNSUPPORTED;
+      if (r->kv_len_host) {
+        for (int l = 0; l < r->lanes; ++l) {
+          if (r->kv_len_host[l] < 0) return SPEC_E_INVAL;
+          if ((long long)r->kv_len_host[l] + r->cols_host[l] > (long long)r->max_blocks * SPEC_KV_BLOCK)
+            return SPEC_E_RANGE;
+        }
+      }
+    }
+    if (m->n_gdn && !r->gdn_state) return SPEC_E_UNSUPPORTED;
+  }
+  w = layout(m, ri.R, ri.L, std::max(mb, 1));
+  if (!r->workspace) return SPEC_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(r->workspace) % kAlign) != 0) return SPEC_E_WORKSPACE;
+  if (r->workspace_bytes < w.total) return SPEC_E_WORKSPACE;
+  return SPEC_OK;
+}
+
+// ---------------------------------------------------------------- profiling
+struct ProfScope {
+  spec_model* m;
+  hipStream_t st;
+  bool on;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(const spec_model* mc, int cls, hipStream_t s) : m(const_cast<spec_model*>(mc)), st(s) {
+    on = m->prof_class == cls && cls != SPEC_K_NONE;
+    if (!on) return;
+    while (m->prof_pool.size() < m->prof_used + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+      m->prof_pool.push_back(e);
+    }
+    a = m->prof_pool[m->prof_used++];
+    b = m->prof_pool[m->prof_used++];
+    hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!on) return;
+    hipEventRecord(b, st);
+    m->prof_events.emplace_back(a, b);
+  }
+};
+
+#define SV_CHECK(x)                 \
+  do {                              \
+    if ((x) != 0) return SPEC_E_HIP; \
+  } while (0)
+
+// ---------------------------------------------------------------- projections
+int project(const spec_model* m, int cls, const void* X, const void* W0, const void* W1, int R, int N, int K,
+            int S, float* P, void* Y, hipStream_t st) {
+  ProfScope ps(m, cls, st);
+  if (m->bf16) {
+    sv::GemmParams p{};
+    p.X = reinterpret_cast<const sv::bf16_t*>(X);
+    p.W0 = reinterpret_cast<const sv::bf16_t*>(W0);
+    p.W1 = reinterpret_cast<const sv::bf16_t*>(W1);
+    p.R = R; p.N = N; p.K = K; p.S = S; p.groups = (N + 15) / 16;
+    p.P = P;
+    p.Yb = reinterpret_cast<sv::bf16_t*>(Y);
+    return sv::launch_gemm_bf16(p, W1 ? 2 : 1, W1 != nullptr, st);
+  }
+  sv::GemmF32Params p{};
+  p.X = reinterpret_cast<const float*>(X);
+  p.W0 = reinterpret_cast<const float*>(W0);
+  p.W1 = reinterpret_cast<const float*>(W1);
+  p.R = R; p.N = N; p.K = K;
+  p.P = P;
+  p.Ya = reinterpret_cast<float*>(Y);
+  return sv::launch_gemm_f32(p, W1 != nullptr, st);
+}
+
+// The decoder forward for all rows; leaves the final normed hidden states in ws.h.
+int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, hipStream_t st) {
+  const spec_model_desc& d = m->d;
+  void* ws = r->workspace;
+  const bool bf = m->bf16;
+  const int R = ri.R, H = d.hidden;
+  float* x = at<float>(ws, w.x);
+  void* h = at<void>(ws, w.h);
+  float* P = at<float>(ws, w.P);
+  const size_t ab = act_bytes(m);
+  const bool rope = d.rope_theta != 0.f && m->n_attn > 0;
+  if (rope) SV_CHECK(sv::launch_rope_table(r->kv_len, ri, d.head_dim, d.rope_theta, at<float>(ws, w.rope), st));
+  const float* g0 = d.n_layers ? m->layers[0].w.norm1 : d.final_norm;
+  SV_CHECK(sv::launch_embed_norm(r->tokens, d.embed, d.vocab, H, g0, d.rms_eps, x, h, ri, bf, st));
+  const size_t apool = (size_t)r->n_blocks * d.n_kv_heads * SPEC_KV_BLOCK * d.head_dim * ab;
+  for (int i = 0; i < d.n_layers; ++i) {
+    const Layer& L = m->layers[i];
+    const float* gnext = i + 1 < d.n_layers ? m->layers[i + 1].w.norm1 : d.final_norm;
+    int S_o;
+    int Ko;
+    if (L.kind == SPEC_LAYER_ATTN) {
+      const int nq = d.n_q_heads, nkv = d.n_kv_heads, hd = d.head_dim;
+      const int Nin = (nq + 2 * nkv) * hd;
+      const int S_in = m->s_in_attn.S;
+      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
+      void* sk = at<char>(ws, w.stk) + (size_t)L.attn_index * w.stage_layer_elems * ab;
+      void* svp = at<char>(ws, w.stv) + (size_t)L.attn_index * w.stage_layer_elems * ab;
+      void* q = at<void>(ws, w.q);
+      SV_CHECK(sv::launch_qkv_post(P, S_in, at<float>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ri, bf, st));
+      sv::AttnParams ap{};
+      ap.q = q; ap.sk = sk; ap.sv = svp;
+      ap.kpool = reinterpret_cast<const char*>(r->k_pool) + (size_t)L.attn_index * apool;
+      ap.vpool = reinterpret_cast<const char*>(r->v_pool) + (size_t)L.attn_index * apool;
+      ap.block_table = r->block_table; ap.max_blocks = r->max_blocks; ap.n_blocks = r->n_blocks;
+      ap.kv_len = r->kv_len;
+      ap.nq = nq; ap.nkv = nkv; ap.G = nq / nkv; ap.d = hd;
+      ap.chunk = m->chunk; ap.n_chunks = w.n_chunks;
+      ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      ap.part = at<float>(ws, w.apart);
+      ap.ri = ri;
+      {
+        ProfScope ps(m, SPEC_K_ATTN, st);
+        SV_CHECK(sv::launch_attention(ap, bf, st));
+      }
+      SV_CHECK(sv::launch_attn_combine(ap, at<void>(ws, w.o), bf, st));
+      S_o = m->s_o_attn.S;
+      Ko = nq * hd;
+    } else {
+      const int hg = d.gdn_heads, dg = d.gdn_dim;
+      const int Nin = 3 * hg * dg + 2 * hg;
+      const int S_in = m->s_in_gdn.S;
+      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
+      float* stage = at<float>(ws, w.gst) + (size_t)L.gdn_index * w.gst_layer_floats;
+      {
+        ProfScope ps(m, SPEC_K_GDN, st);
+        SV_CHECK(sv::launch_gdn_verify(P, S_in, hg, dg, r->gdn_state, m->n_gdn, L.gdn_index, stage,
+                                       at<void>(ws, w.o), ri, bf, st));
+      }
+      S_o = m->s_o_gdn.S;
+      Ko = hg * dg;
+    }
+    SV_CHECK(project(m, SPEC_K_PROJ_O, at<void>(ws, w.o), L.w.w_o, nullptr, R, H, Ko, S_o, P, nullptr, st));
+    SV_CHECK(sv::launch_resid_norm(P, S_o, x, H, L.w.norm2, d.rms_eps, h, ri, bf, st));
+    SV_CHECK(project(m, SPEC_K_GATE_UP, h, L.w.w_gate, L.w.w_up, R, d.ffn, H, 1, nullptr, at<void>(ws, w.a), st));
+    SV_CHECK(project(m, SPEC_K_DOWN, at<void>(ws, w.a), L.w.w_down, nullptr, R, H, d.ffn, m->s_down.S, P, nullptr, st));
+    SV_CHECK(sv::launch_resid_norm(P, m->s_down.S, x, H, gnext, d.rms_eps, h, ri, bf, st));
+  }
+  return SPEC_OK;
+}
+
+int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, hipStream_t st) {
+  sv::LmParams p{};
+  p.X = at<void>(r->workspace, w.h);
+  p.W = m->d.lm_head;
+  p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden;
+  p.groups = m->lm_groups;
+  p.tokens = r->tokens;
+  p.kv_len = r->kv_len;
+  p.sampled = r->mode == SPEC_SAMPLED;
+  p.inv_t = p.sampled ? 1.0f / r->temperature : 1.0f;
+  p.key0 = (uint32_t)(r->seed & 0xffffffffu);
+  p.key1 = (uint32_t)(r->seed >> 32);
+  p.part = at<sv::LmPartial>(r->workspace, w.lmp);
+  p.ri = ri;
+  ProfScope ps(m, SPEC_K_LM_HEAD, st);
+  return sv::launch_lmhead(p, m->bf16, st) ? SPEC_E_HIP : SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_E_INVAL: return "invalid argument";
+    case SPEC_E_RANGE: return "round exceeds the lane's block table";
+    case SPEC_E_UNSUPPORTED: return "unsupported shape or configuration";
+    case SPEC_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SPEC_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int spec_plan_drafts(int k, int row_budget, int lanes) {
+  if (lanes <= 0 || k < 0 || row_budget < 0) return SPEC_E_INVAL;
+  const int rows = row_budget == 0 ? 8 : row_budget;
+  return std::max(0, std::min(k, rows / lanes - 1));
+}
+
+int spec_model_create(const spec_model_desc* desc, spec_model** out) {
+  if (!desc || !out) return SPEC_E_INVAL;
+  *out = nullptr;
+  const spec_model_desc& d = *desc;
+  if (d.n_layers < 0 || d.hidden <= 0 || d.vocab <= 0 || (d.vocab % 16) != 0) return SPEC_E_INVAL;
+  if (d.dtype != SPEC_F32 && d.dtype != SPEC_BF16) return SPEC_E_INVAL;
+  if (d.kv_block != SPEC_KV_BLOCK) return SPEC_E_UNSUPPORTED;
+  if (!d.lm_head) return SPEC_E_INVAL;
+  if (!(d.rms_eps >= 0.f) || !(d.rope_theta >= 0.f)) return SPEC_E_INVAL;
+  const bool bf = d.dtype == SPEC_BF16;
+  if (bf && (d.hidden % 256) != 0) return SPEC_E_UNSUPPORTED;
+  const int chunk = d.attn_chunk == 0 ? kDefaultChunk : d.attn_chunk;
+  if (chunk < 256 || (chunk % 256) != 0) return SPEC_E_UNSUPPORTED;
+  spec_model* m = new (std::nothrow) spec_model();
+  if (!m) return SPEC_E_INVAL;
+  m->d = d;
+  m->bf16 = bf;
+  m->chunk = chunk;
+  if (d.n_layers > 0) {
+    if (!d.layer_kind || !d.layers || !d.embed || !d.final_norm || d.ffn <= 0) { delete m; return SPEC_E_INVAL; }
+    if (bf && (d.ffn % 256) != 0) { delete m; return SPEC_E_UNSUPPORTED; }
+    m->kinds.assign(d.layer_kind, d.layer_kind + d.n_layers);
+    for (int i = 0; i < d.n_layers; ++i) {
+      Layer L{};
+      L.kind = d.layer_kind[i];
+      L.w = d.layers[i];
+      L.attn_index = L.gdn_index = -1;
+      if (!valid_layer(L.w)) { delete m; return SPEC_E_INVAL; }
+      if (L.kind == SPEC_LAYER_ATTN) L.attn_index = m->n_attn++;
+      else if (L.kind == SPEC_LAYER_GDN) L.gdn_index = m->n_gdn++;
+      else { delete m; return SPEC_E_INVAL; }
+      m->layers.push_back(L);
+    }
+    if (m->n_attn) {
+      if (d.n_q_heads <= 0 || d.n_kv_heads <= 0 || (d.n_q_heads % d.n_kv_heads) != 0) { delete m; return SPEC_E_INVAL; }
+      if (d.head_dim <= 0 || (d.head_dim % 2) != 0) { delete m; return SPEC_E_INVAL; }
+      if (bf && (d.head_dim != 128 || ((d.n_q_heads * d.head_dim) % 256) != 0)) { delete m; return SPEC_E_UNSUPPORTED; }
+      if (!bf && d.head_dim > 128) { delete m; return SPEC_E_UNSUPPORTED; }
+    }
+    if (m->n_gdn) {
+      if (d.gdn_heads <= 0 || d.gdn_dim != 128) { delete m; return SPEC_E_UNSUPPORTED; }
+      if (bf && ((d.gdn_heads * d.gdn_dim) % 256) != 0) { delete m; return SPEC_E_UNSUPPORTED; }
+    }
+  }
+  m->d.layer_kind = m->kinds.empty() ? nullptr : m->kinds.data();
+  m->d.layers = nullptr;   // per-layer weights live in m->layers
+  const int H = d.hidden;
+  if (m->n_attn) {
+    m->s_in_attn.S = split_for(m, (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, H, false);
+    m->s_o_attn.S = split_for(m, H, d.n_q_heads * d.head_dim, false);
+  }
+  if (m->n_gdn) {
+    m->s_in_gdn.S = split_for(m, 3 * d.gdn_heads * d.gdn_dim + 2 * d.gdn_heads, H, false);
+    m->s_o_gdn.S = split_for(m, H, d.gdn_heads * d.gdn_dim, false);
+  }
+  if (d.n_layers) {
+    m->s_gateup.S = 1;
+    m->s_down.S = split_for(m, H, d.ffn, false);
+  }
+  m->lm_groups = sv::lmhead_groups(d.vocab, bf);
+  *out = m;
+  return SPEC_OK;
+}
+
+void spec_model_destroy(spec_model* m) {
+  if (!m) return;
+  for (hipEvent_t e : m->prof_pool) hipEventDestroy(e);
+  delete m;
+}
+
+int64_t spec_workspace_bytes(const spec_model* m, int max_lanes, int max_cols, int max_blocks) {
+  if (!m || max_lanes < 1 || max_lanes > SPEC_MAX_LANES || max_cols < 1 || max_cols > SPEC_MAX_COLS ||
+      max_blocks < 0)
+    return SPEC_E_INVAL;
+  const int R = std::min(SPEC_MAX_ROWS, max_lanes * max_cols);
+  return (int64_t)layout(m, R, max_lanes, std::max(max_blocks, 1)).total;
+}
+
+int spec_verify_round(const spec_model* m, const spec_round* r, void* stream) {
+  sv::RowInfo ri;
+  WsLayout w;
+  int st = check_round(m, r, false, ri, w);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = forward(m, r, ri, w, s);
+  if (st) return st;
+  return lm_stats(m, r, ri, w, s);
+}
+
+int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidden, void* stream) {
+  sv::RowInfo ri;
+  WsLayout w;
+  if (!hidden) return SPEC_E_INVAL;
+  int st = check_round(m, r, true, ri, w);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * act_bytes(m), s));
+  return lm_stats(m, r, ri, w, s);
+}
+
+int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, int32_t* out_tokens,
+                spec_row_stat* row_stats, void* stream) {
+  sv::RowInfo ri;
+  WsLayout w;
+  if (!committed || !out_tokens) return SPEC_E_INVAL;
+  const bool head_only = !m || m->d.n_layers == 0;
+  int st = check_round(m, r, head_only, ri, w);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = r->workspace;
+  const bool sampled = r->mode == SPEC_SAMPLED;
+  const float inv_t = sampled ? 1.0f / r->temperature : 1.0f;
+  const uint32_t k0 = (uint32_t)(r->seed & 0xffffffffu), k1 = (uint32_t)(r->seed >> 32);
+  SV_CHECK(sv::launch_row_reduce(at<sv::LmPartial>(ws, w.lmp), m->lm_groups, ri.R, inv_t, at<sv::RowStat>(ws, w.rstat),
+                                 row_stats, s));
+  SV_CHECK(sv::launch_lane_accept(at<sv::RowStat>(ws, w.rstat), r->tokens, r->kv_len, r->q_probs, m->d.vocab,
+                                  sampled ? 1 : 0, inv_t, k0, k1, at<sv::LaneDecision>(ws, w.dec), committed,
+                                  out_tokens, ri, s));
+  if (sampled) {
+    sv::RaceParams p{};
+    p.X = at<void>(ws, w.h);
+    p.W = m->d.lm_head;
+    p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
+    p.groups = m->lm_groups;
+    p.q = r->q_probs;
+    p.kv_len = r->kv_len;
+    p.inv_t = inv_t;
+    p.key0 = k0; p.key1 = k1;
+    p.dec = at<sv::LaneDecision>(ws, w.dec);
+    p.part = at<float>(ws, w.racep);
+    p.ri = ri;
+    SV_CHECK(sv::launch_race(p, m->bf16, s));
+    SV_CHECK(sv::launch_race_finish(at<float>(ws, w.racep), m->lm_groups, at<sv::LaneDecision>(ws, w.dec),
+                                    out_tokens, ri, s));
+  }
+  return SPEC_OK;
+}
+
+int spec_commit(const spec_model* m, const spec_round* r, const int32_t* committed, void* stream) {
+  sv::RowInfo ri;
+  WsLayout w;
+  if (!committed) return SPEC_E_INVAL;
+  int st = check_round(m, r, false, ri, w);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const spec_model_desc& d = m->d;
+  if (m->n_attn)
+    SV_CHECK(sv::launch_commit_kv(committed, r->kv_len, r->block_table, r->max_blocks, r->n_blocks, r->k_pool,
+                                  r->v_pool, m->n_attn, d.n_kv_heads, d.head_dim, at<void>(r->workspace, w.stk),
+                                  at<void>(r->workspace, w.stv), w.stage_layer_elems, ri, m->bf16, s));
+  if (m->n_gdn)
+    SV_CHECK(sv::launch_gdn_replay(committed, r->gdn_state, m->n_gdn, d.gdn_heads, d.gdn_dim,
+                                   at<float>(r->workspace, w.gst), w.gst_layer_floats, ri, s));
+  SV_CHECK(sv::launch_kvlen_update(committed, r->kv_len, ri, s));
+  return SPEC_OK;
+}
+
+int spec_debug_logits(const spec_model* m, const spec_round* r, float* logits, void* stream) {
+  sv::RowInfo ri;
+  WsLayout w;
+  if (!logits) return SPEC_E_INVAL;
+  int st = check_round(m, r, false, ri, w);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = forward(m, r, ri, w, s);
+  if (st) return st;
+  // one split: the same accumulation chain as the LM-head kernel
+  return project(m, SPEC_K_NONE, at<void>(r->workspace, w.h), m->d.lm_head, nullptr, ri.R, m->d.vocab,
+                 m->d.hidden, 1, logits, nullptr, s)
+             ? SPEC_E_HIP
+             : SPEC_OK;
+}
+
+int spec_debug_gemm(const spec_model* m, const void* X, const void* W, float* Y, int R, int N, int K,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!m || !X || !W || !Y || R < 1 || R > SPEC_MAX_ROWS || N < 1 || K < 1) return SPEC_E_INVAL;
+  if (m->bf16 && (K % 256) != 0) return SPEC_E_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int S = split_for(m, N, K, false);
+  if (S == 1) return project(m, SPEC_K_PROJ_IN, X, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
+  const size_t need = (size_t)S * R * N * 4;
+  if (!workspace || workspace_bytes < need) return SPEC_E_WORKSPACE;
+  float* P = reinterpret_cast<float*>(workspace);
+  SV_CHECK(project(m, SPEC_K_PROJ_IN, X, W, nullptr, R, N, K, S, P, nullptr, s));
+  SV_CHECK(sv::launch_sum_partials(P, S, (size_t)R * N, Y, s));
+  return SPEC_OK;
+}
+
+int spec_profile_enable(spec_model* m, int kernel_class) {
+  if (!m || kernel_class < SPEC_K_NONE || kernel_class >= SPEC_K_COUNT) return SPEC_E_INVAL;
+  m->prof_class = kernel_class;
+  m->prof_events.clear();
+  m->prof_used = 0;
+  return SPEC_OK;
+}
+
+int spec_profile_collect(spec_model* m, double* total_ms, int* launches) {
+  if (!m || !total_ms || !launches) return SPEC_E_INVAL;
+  double t = 0.0;
+  for (auto& ev : m->prof_events) {
+    if (hipEventSynchronize(ev.second) != hipSuccess) return SPEC_E_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess) return SPEC_E_HIP;
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int)m->prof_events.size();
+  return SPEC_OK;
+}
+
+}  // extern "C"

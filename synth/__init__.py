@@ -18,5 +18,5 @@ Recipes (the pages give model families and sizes, not data):
 from .configs import CONFIGS, ModelConfig, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     model_weights, layer_weights, head_weights, prompt_tokens, kv_context,
-    block_table, gdn_state, drafter_rows, planted_drafts, uniform_tokens,
+    block_table, gdn_state, drafter_rows, planted_drafts, uniform_tokens, hidden_states,
 )

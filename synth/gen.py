@@ -151,3 +151,9 @@ def planted_drafts(seed: int, tag: int, reference: Sequence[int], alpha, vocab: 
     other = r.integers(0, vocab - 1, size=n)
     other = other + (other >= ref)      # uniform over tokens != ref
     return np.where(hit, ref, other).astype(np.int32)
+
+
+def hidden_states(cfg: ModelConfig, rows: int, tag: int = 0) -> np.ndarray:
+    """Final hidden states [rows, hidden] ~ N(0, 1) at the model's precision (LM-head-only rounds)."""
+    a = _rng(cfg.input_seed, 23, tag).standard_normal(size=(rows, cfg.hidden), dtype=np.float32)
+    return _to_storage(a, cfg.dtype)

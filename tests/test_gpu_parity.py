@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, on the same seeded inputs.
+
+Bars: committed tokens bit-exact except at rows whose oracle top-2 logit gap is
+below 5e-2 (those are counted); logits within 1e-4 max-abs for fp32 weights and
+3e-2 for bf16 weights; integer state (kv_len, committed counts) exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import GAP_EXCUSE, Pair, compare_rows, log, top2_gap
+from helpers import small_dense, small_hybrid
+from oracle import accept_greedy, accept_sampled, row_stats
+from oracle.accept import argmax_lowest
+from synth.configs import ModelConfig
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_head_model(H=256, V=1024):
+    from speculative_decoding_verify_round_amd.runtime import DeviceModel
+    cfg = ModelConfig(name="gemm-probe", n_layers=0, hidden=H, n_q_heads=0, n_kv_heads=0, head_dim=0, ffn=0,
+                      vocab=V, dtype="bf16", layer_kinds=(), head_only=True)
+    w = {"lm_head": np.zeros((V, H), np.float32), "final_norm": np.ones(H, np.float32)}
+    return DeviceModel(cfg, w)
+
+
+@pytest.mark.parametrize("R,N,K", [(1, 16, 256), (5, 40, 512), (16, 48, 1024), (33, 200, 2048),
+                                   (64, 7168, 5120), (8, 5120, 17408), (64, 34816, 5120)])
+def test_projection_kernel(R, N, K):
+    from speculative_decoding_verify_round_amd import binding as B
+    log(f"projection R={R} N={N} K={K}")
+    dm = _bf16_head_model()
+    g = torch.Generator().manual_seed(R * 7919 + N)
+    X = torch.randn(R, K, generator=g).to(torch.bfloat16)
+    W = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
+    ref = (X.double() @ W.double().T).numpy()
+    Xd, Wd = X.cuda(), W.cuda()
+    ws = torch.zeros(64 * N * 64 * 4 + 256, dtype=torch.uint8, device="cuda")
+    Y = torch.empty(R, N, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    B.spec_debug_gemm(dm.handle, Xd.data_ptr(), Wd.data_ptr(), Y.data_ptr(), R, N, K, ws.data_ptr(), ws.numel(), st)
+    y = Y.cpu().numpy()
+    err = np.max(np.abs(y - ref))
+    assert err <= 2e-6 * np.sqrt(K) + 1e-6, err
+    # batch invariance: the first row alone gives the same bits
+    Y1 = torch.empty(1, N, dtype=torch.float32, device="cuda")
+    B.spec_debug_gemm(dm.handle, Xd.data_ptr(), Wd.data_ptr(), Y1.data_ptr(), 1, N, K, ws.data_ptr(), ws.numel(), st)
+    assert torch.equal(Y1[0], Y[0])
+    dm.close()
+
+
+def _prefill(pair, prompts, chunk=16):
+    """Teacher-forced rounds on both sides: every prompt token but the last becomes context."""
+    L = len(prompts)
+    done = 0
+    n = len(prompts[0]) - 1
+    while done < n:
+        c = min(chunk, n - done)
+        toks = [list(map(int, p[done:done + c])) for p in prompts]
+        ores = pair.om.verify_round(pair.oc, toks)
+        rc = pair.dc.round(toks, kv_len_host=list(pair.oc.kv_len))
+        logits = pair.dc.debug_logits(rc).cpu().numpy()
+        pair.om.commit(pair.oc, ores, [c] * L)
+        pair.dc.commit(rc, torch.full((L,), c, dtype=torch.int32, device="cuda"))
+        done += c
+        yield ores.logits, logits
+
+
+def test_tiny_fp32_rounds_match_oracle_and_plain_greedy():
+    """Tiny fp32 decoder: 64-token prompt, 16 greedy rounds at k = 3 with drafts that
+    equal the plain-greedy token with probability 0.7."""
+    cfg = synth.get_config("tiny-fp32")
+    log("tiny-fp32: setup")
+    pair = Pair(cfg, lanes=1, context=0, max_blocks=16)
+    prompt = synth.prompt_tokens(cfg)
+    for ol, gl in _prefill(pair, [prompt]):
+        assert np.max(np.abs(ol - gl)) < 1e-4
+    ref = pair.om.plain_greedy(pair.oc.copy(), [int(prompt[-1])], 16 * (cfg.k + 1) + 2)[0]
+    anchor, out, n_rows, mism = int(prompt[-1]), [], 0, []
+    for rnd in range(cfg.rounds):
+        P = len(out)
+        drafts = list(map(int, synth.planted_drafts(cfg.input_seed, rnd, ref[P:P + cfg.k], 0.7, cfg.vocab)))
+        toks = [[anchor] + drafts]
+        ores = pair.om.verify_round(pair.oc, toks)
+        oc_, oem = accept_greedy(ores.logits, drafts)
+        rc = pair.dc.round(toks, kv_len_host=list(pair.oc.kv_len))
+        gl = pair.dc.debug_logits(rc).cpu().numpy()
+        assert np.max(np.abs(gl - ores.logits)) < 1e-4
+        pair.dc.verify(rc)
+        pair.dc.accept(rc)
+        c, em, st = pair.dc.results(rc)
+        n_rows += rc.R
+        for r in range(rc.R):
+            if st["argmax"][r] != argmax_lowest(ores.logits[r]):
+                mism.append(top2_gap(ores.logits[r]))
+        ostats = row_stats(ores.logits, [*drafts, -1])
+        assert np.max(np.abs(st["lse"] - ostats["lse"])) < 1e-4
+        assert np.max(np.abs(st["max"] - ostats["max"])) < 1e-4
+        assert em[0] == oem and c[0] == oc_, (rnd, em, oem)
+        pair.om.commit(pair.oc, ores, [oc_])
+        pair.dc.commit(rc)
+        out += em[0]
+        anchor = em[0][-1]
+    torch.cuda.synchronize()
+    assert out == [int(t) for t in ref[:len(out)]]           # speculative greedy = plain greedy
+    assert int(pair.dc.kv_len[0]) == int(pair.oc.kv_len[0]) == 63 + len(out)
+    for li in range(cfg.n_attn):
+        K, V = pair.dc.get_kv(li, 0, 0, int(pair.oc.kv_len[0]))
+        ok, ov = pair.oc.gather(li, 0, int(pair.oc.kv_len[0]))
+        assert np.max(np.abs(K - ok)) < 1e-4 and np.max(np.abs(V - ov)) < 1e-4
+    assert not mism
+    log(f"tiny-fp32: {len(out)} tokens in {cfg.rounds} rounds")
+    pair.close()
+
+
+def _round_parity(pair, lane_tokens, mode="greedy", T=1.0, q=None, seed=0, logit_tol=3e-2):
+    """One verify round on both sides; returns (oracle result, gpu committed, gpu tokens, mismatches)."""
+    cfg = pair.cfg
+    ores = pair.om.verify_round(pair.oc, lane_tokens)
+    qd = torch.from_numpy(q).cuda() if q is not None else None
+    rc = pair.dc.round(lane_tokens, mode=mode, temperature=T, q_probs=qd, seed=seed,
+                       kv_len_host=list(pair.oc.kv_len))
+    gl = pair.dc.debug_logits(rc).cpu().numpy()
+    lerr = float(np.max(np.abs(gl - ores.logits)))
+    assert lerr <= logit_tol, lerr
+    pair.dc.verify(rc)
+    pair.dc.accept(rc)
+    c, em, st = pair.dc.results(rc)
+    mism = []
+    for l, rows in enumerate(ores.lane_rows):
+        lz = ores.logits[rows.start:rows.stop]
+        drafts = lane_tokens[l][1:]
+        if mode == "greedy":
+            oc_, oem = accept_greedy(lz, drafts)
+        else:
+            oc_, oem = accept_sampled(lz, drafts, q[rows.start + 1:rows.stop], T, seed, l, int(pair.oc.kv_len[l]))
+        if (oc_, oem) != (int(c[l]), em[l]):
+            gaps = [top2_gap(lz[j]) for j in range(len(rows))]
+            mism.append((l, oc_, oem, int(c[l]), em[l], min(gaps)))
+    return ores, rc, c, em, st, lerr, mism
+
+
+def test_small_dense_bf16_round_and_commit():
+    cfg = small_dense(hidden=256, head_dim=128, ffn=512, vocab=1024, context=37)
+    pair = Pair(cfg, lanes=3, context=37, max_blocks=8)
+    toks = [[5], [7, 8, 9, 10], [11, 12, 13, 14, 15, 16, 17]]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
+    log(f"small-dense: logit err {lerr:.2e}, mismatches {mism}")
+    assert not mism
+    pair.om.commit(pair.oc, ores, list(c))
+    pair.dc.commit(rc)
+    torch.cuda.synchronize()
+    assert list(pair.dc.kv_len.cpu().numpy()) == list(pair.oc.kv_len)
+    for li in range(cfg.n_attn):
+        for l in range(3):
+            n = int(pair.oc.kv_len[l])
+            K, V = pair.dc.get_kv(li, l, 0, n)
+            ok, ov = pair.oc.gather(li, l, n)
+            assert np.mean(K == ok) > 0.999 and np.mean(V == ov) > 0.999
+            assert np.max(np.abs(K - ok)) <= 2 ** -7 * np.max(np.abs(ok)) + 1e-6
+    pair.close()
+
+
+@pytest.mark.parametrize("context", [250, 1021])
+def test_attention_chunks_and_own_columns_cross_boundaries(context):
+    """Split-KV chunks of 256 positions; the round's own columns straddle a chunk boundary."""
+    cfg = small_dense(hidden=256, head_dim=128, ffn=512, vocab=1024, context=context, n_layers=1,
+                      layer_kinds=("attn",))
+    pair = Pair(cfg, lanes=2, context=context, max_blocks=(context + 40) // 16 + 1, attn_chunk=256)
+    toks = [[1, 2, 3, 4, 5, 6, 7, 8], [9, 10, 11]]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
+    log(f"chunks ctx={context}: logit err {lerr:.2e}")
+    assert not mism
+    pair.close()
+
+
+def test_small_hybrid_bf16_round_and_commit():
+    cfg = small_hybrid(hidden=256, head_dim=128, ffn=512, vocab=1024, gdn_heads=2, gdn_dim=128, context=40)
+    pair = Pair(cfg, lanes=2, context=40, max_blocks=8)
+    toks = [[3, 4, 5, 6], [7, 8, 9]]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
+    log(f"small-hybrid: logit err {lerr:.2e}, mismatches {mism}")
+    assert not mism
+    pair.om.commit(pair.oc, ores, list(c))
+    pair.dc.commit(rc)
+    torch.cuda.synchronize()
+    for gi in range(cfg.n_gdn):
+        g = pair.dc.gdn[:, gi].cpu().numpy()
+        o = pair.oc.gdn[gi]
+        assert np.max(np.abs(g - o)) <= 1e-5 * np.max(np.abs(o)) + 1e-6
+    pair.close()
+
+
+def test_sampled_rounds_small_dense():
+    cfg = small_dense(hidden=256, head_dim=128, ffn=512, vocab=1024, context=37)
+    pair = Pair(cfg, lanes=4, context=37, max_blocks=8)
+    total, bad = 0, []
+    for rnd in range(6):
+        q, d = synth.drafter_rows(cfg.input_seed, rnd, 4 * 5, cfg.vocab)
+        toks = [[int(100 + l)] + [int(x) for x in d[l * 5 + 1:(l + 1) * 5]] for l in range(4)]
+        ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks, "sampled", 0.8, q, seed=4242 + rnd)
+        total += 4
+        bad += mism
+    log(f"sampled small-dense: {len(bad)} of {total} lanes differ: {bad}")
+    assert not bad
+    pair.close()
+
+
+def test_head_only_full_size_greedy_and_sampled():
+    """LM head + acceptance at the 151,936 x 5,120 head: 8 lanes x 8 rows of given hidden states."""
+    cfg = synth.get_config("head-v151936")
+    log("head-only: weights")
+    w = synth.head_weights(cfg)
+    from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel
+    from oracle import OracleModel
+    om = OracleModel(cfg, w)
+    dm = DeviceModel(cfg, w)
+    L, k = cfg.lanes, cfg.k
+    R = L * (k + 1)
+    dc = DeviceCache(dm, L, 1, 1, kv_len=[cfg.context] * L)
+    hid = synth.hidden_states(cfg, R)
+    log("head-only: oracle logits")
+    z = om.lm_head(hid)
+    hd = torch.from_numpy(hid).to("cuda", torch.bfloat16)
+    for mode in cfg.modes:
+        q, d = synth.drafter_rows(cfg.input_seed, 99, R, cfg.vocab)
+        toks = []
+        for l in range(L):
+            toks.append([int(l)] + [int(x) for x in d[l * (k + 1) + 1:(l + 1) * (k + 1)]])
+        T = cfg.temperature if mode == "sampled" else 1.0
+        rc = dc.round(toks, mode=mode, temperature=T, q_probs=torch.from_numpy(q).cuda() if mode == "sampled" else None,
+                      seed=cfg.philox_seed)
+        dc.verify_head(rc, hd)
+        dc.accept(rc)
+        c, em, st = dc.results(rc)
+        nxt = []
+        for l in range(L):
+            nxt += toks[l][1:] + [-1]
+        os_ = row_stats(z, nxt, T)
+        assert np.max(np.abs(st["max"] - os_["max"])) < 1e-3
+        assert np.max(np.abs(st["lse"] - os_["lse"])) < 1e-3
+        zn_ok = np.isnan(os_["z_next"]) == np.isnan(st["z_next"])
+        assert zn_ok.all()
+        m = ~np.isnan(os_["z_next"])
+        assert np.max(np.abs(st["z_next"][m] - os_["z_next"][m])) < 1e-3
+        arg_mism = [r for r in range(R) if st["argmax"][r] != os_["argmax"][r]]
+        assert all(top2_gap(z[r]) < GAP_EXCUSE for r in arg_mism), arg_mism
+        lanes_bad = []
+        for l in range(L):
+            lz = z[l * (k + 1):(l + 1) * (k + 1)]
+            if mode == "greedy":
+                oc_, oem = accept_greedy(lz, toks[l][1:])
+            else:
+                oc_, oem = accept_sampled(lz, toks[l][1:], q[l * (k + 1) + 1:(l + 1) * (k + 1)], T,
+                                          cfg.philox_seed, l, cfg.context)
+            if (oc_, oem) != (int(c[l]), em[l]):
+                lanes_bad.append((l, oc_, oem, int(c[l]), em[l]))
+        log(f"head-only {mode}: committed {list(c)}, differing lanes {lanes_bad}, argmax mism {arg_mism}")
+        assert not lanes_bad
+    dm.close()

@@ -119,10 +119,12 @@ class OracleModel:
     exactly representable at the model's storage precision.
     """
 
-    def __init__(self, cfg, weights: Dict[str, object]):
+    def __init__(self, cfg, weights: Dict[str, object], keep_f64: bool = True):
         self.cfg = cfg
         self.w = weights
         self.dtype = cfg.dtype
+        # float64 copies of resident weight matrices, made once (a streamed model keeps none)
+        self._f64 = {} if keep_f64 and "layers" in weights else None
 
     # ------------------------------------------------------------------ helpers
     def _layer(self, i: int) -> Dict[str, np.ndarray]:
@@ -133,10 +135,19 @@ class OracleModel:
     def _st(self, x) -> np.ndarray:
         return store(x, self.dtype)
 
-    @staticmethod
-    def _matT(x, w) -> np.ndarray:
+    def _w64(self, w) -> np.ndarray:
+        if self._f64 is None:
+            return np.asarray(w, np.float64)
+        key = id(w)
+        hit = self._f64.get(key)
+        if hit is None or hit[0] is not w:
+            hit = (w, np.asarray(w, np.float64))
+            self._f64[key] = hit
+        return hit[1]
+
+    def _matT(self, x, w) -> np.ndarray:
         """float32(x @ w.T) with float64 accumulation."""
-        return f32(np.asarray(x, np.float64) @ np.asarray(w, np.float64).T)
+        return f32(np.asarray(x, np.float64) @ self._w64(w).T)
 
     def lm_head(self, hidden) -> np.ndarray:
         return self._matT(hidden, self.w["lm_head"])

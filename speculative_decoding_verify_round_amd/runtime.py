@@ -143,15 +143,16 @@ class DeviceCache:
                                    device=dev)
         self.block_table = None
         self.k_pool = self.v_pool = None
-        if cfg.n_attn and pools:
+        if cfg.n_attn:
             bt = block_table if block_table is not None else np.arange(lanes * max_blocks).reshape(lanes, max_blocks)
             self.block_table = torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev)
+        if cfg.n_attn and pools:
             shape_k = (cfg.n_attn, n_blocks, cfg.n_kv_heads, B.SPEC_KV_BLOCK, cfg.head_dim)
             shape_v = (cfg.n_attn, n_blocks, cfg.n_kv_heads, cfg.head_dim, B.SPEC_KV_BLOCK)
             self.k_pool = torch.zeros(shape_k, dtype=model.tdtype, device=dev)
             self.v_pool = torch.zeros(shape_v, dtype=model.tdtype, device=dev)
         self.gdn = None
-        if cfg.n_gdn:
+        if cfg.n_gdn and pools:
             self.gdn = torch.zeros((lanes, cfg.n_gdn, cfg.gdn_heads, cfg.gdn_dim, cfg.gdn_dim), dtype=torch.float32,
                                    device=dev)
         nbytes = B.spec_workspace_bytes(model.handle, lanes, max_cols, max(1, max_blocks))

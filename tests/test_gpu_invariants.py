@@ -1,0 +1,134 @@
+"""Properties of the HIP path that hold at any size, checked bit for bit on the GPU.
+
+  * a round run twice gives identical bits (no races, no order-dependent sums);
+  * a lane's rows do not depend on the other lanes of the round (batch invariance);
+  * drafts after column j do not change rows 0..j (causal among own columns);
+  * verify + commit(c) leaves the same cache and recurrent state as c plain
+    one-column rounds, and row j of a verify round equals the plain round at
+    that position (the commit contract of the pages' "One round, step by step",
+    step 5, made exact by position-fixed reduction orders).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import log
+from helpers import small_hybrid
+from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg():
+    return small_hybrid(hidden=256, head_dim=128, ffn=512, vocab=1024, gdn_heads=2, gdn_dim=128, context=45)
+
+
+class Dev:
+    def __init__(self, cfg, lanes=2, context=45, max_blocks=8, chunk=256):
+        self.cfg = cfg
+        self.w = synth.model_weights(cfg)
+        self.dm = DeviceModel(cfg, self.w, attn_chunk=chunk)
+        self.bt, self.nb = synth.block_table(cfg, lanes, max_blocks)
+        self.lanes, self.context, self.max_blocks = lanes, context, max_blocks
+        self.dc = self.fresh()
+
+    def fresh(self, lanes=None, lane_ids=None):
+        lane_ids = list(range(self.lanes)) if lane_ids is None else lane_ids
+        dc = DeviceCache(self.dm, len(lane_ids), self.max_blocks, self.nb, block_table=self.bt[lane_ids],
+                         kv_len=[self.context] * len(lane_ids))
+        for li in range(self.cfg.n_attn):
+            for i, l in enumerate(lane_ids):
+                k, v = synth.kv_context(self.cfg, li, l, self.context)
+                dc.set_kv(li, i, 0, k, v)
+        for gi in range(self.cfg.n_gdn):
+            for i, l in enumerate(lane_ids):
+                dc.set_gdn(gi, i, synth.gdn_state(self.cfg, gi, l))
+        torch.cuda.synchronize()
+        return dc
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = Dev(_cfg())
+    yield d
+    d.dm.close()
+
+
+def _logits(dc, toks):
+    rc = dc.round(toks)
+    z = dc.debug_logits(rc)
+    torch.cuda.synchronize()
+    return z.cpu().numpy()
+
+
+def test_run_twice_identical(dev):
+    toks = [[1, 2, 3, 4, 5], [6, 7, 8]]
+    a = _logits(dev.dc, toks)
+    b = _logits(dev.dc, toks)
+    assert np.array_equal(a, b)
+    rc = dev.dc.round(toks)
+    dev.dc.verify(rc); dev.dc.accept(rc)
+    s1 = dev.dc.row_stats.clone()
+    dev.dc.verify(rc); dev.dc.accept(rc)
+    assert torch.equal(s1, dev.dc.row_stats)
+
+
+def test_lane_rows_independent_of_other_lanes(dev):
+    both = _logits(dev.dc, [[1, 2, 3, 4, 5], [6, 7, 8]])
+    alone = dev.fresh(lane_ids=[1])
+    one = _logits(alone, [[6, 7, 8]])
+    assert np.array_equal(both[5:], one)
+
+
+def test_causal_over_own_columns(dev):
+    a = _logits(dev.dc, [[1, 2, 3, 4, 5, 6, 7]])
+    b = _logits(dev.dc, [[1, 2, 3, 99, 98, 97, 96]])
+    assert np.array_equal(a[:3], b[:3])
+    assert not np.array_equal(a[3:], b[3:])
+
+
+@pytest.mark.parametrize("c", [1, 3, 5])
+def test_commit_equals_plain_steps(dev, c):
+    toks = [11, 12, 13, 14, 15]
+    A = dev.fresh(lane_ids=[0])
+    rc = A.round([toks])
+    A.verify(rc)
+    A.commit(rc, torch.tensor([c], dtype=torch.int32, device="cuda"))
+    Bc = dev.fresh(lane_ids=[0])
+    plain_rows = []
+    for t in toks:
+        r1 = Bc.round([[t]])
+        plain_rows.append(Bc.debug_logits(r1)[0].clone())
+        if len(plain_rows) <= c:
+            Bc.verify(r1)
+            Bc.commit(r1, torch.tensor([1], dtype=torch.int32, device="cuda"))
+        else:
+            break
+    torch.cuda.synchronize()
+    assert int(A.kv_len[0]) == int(Bc.kv_len[0]) == dev.context + c
+    assert torch.equal(A.k_pool, Bc.k_pool) and torch.equal(A.v_pool, Bc.v_pool)
+    assert torch.equal(A.gdn, Bc.gdn)
+    # row j of the verify round equals the plain round at the same position
+    V = dev.fresh(lane_ids=[0])
+    z = V.debug_logits(V.round([toks]))
+    for j in range(min(c + 1, len(toks))):
+        assert torch.equal(z[j], plain_rows[j]), j
+    log(f"commit({c}) == {c} plain steps, bitwise")
+
+
+def test_rejected_columns_leave_no_trace(dev):
+    A = dev.fresh(lane_ids=[0])
+    before_k, before_v = A.k_pool.clone(), A.v_pool.clone()
+    rc = A.round([[1, 2, 3, 4, 5, 6]])
+    A.verify(rc)
+    A.commit(rc, torch.tensor([2], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    changed = (A.k_pool != before_k).reshape(A.k_pool.shape[0], A.k_pool.shape[1], -1).any(-1)   # [layer, block]
+    # only the block(s) holding positions context .. context + 1 may change
+    blocks = {int(dev.bt[0][(dev.context + j) // 16]) for j in range(2)}
+    assert set(torch.nonzero(changed.any(0)).flatten().tolist()) <= blocks
+    K, _ = A.get_kv(0, 0, dev.context + 2, 4)
+    Kb = before_k[0][[int(dev.bt[0][(dev.context + 2 + j) // 16]) for j in range(4)], :,
+                     [(dev.context + 2 + j) % 16 for j in range(4)], :].float().cpu().numpy()
+    assert np.array_equal(K, Kb)

@@ -153,14 +153,25 @@ def test_small_dense_bf16_round_and_commit():
     pair.dc.commit(rc)
     torch.cuda.synchronize()
     assert list(pair.dc.kv_len.cpu().numpy()) == list(pair.oc.kv_len)
+    check_committed_cache(pair, 37)
+    pair.close()
+
+
+def check_committed_cache(pair, context):
+    """Committed K/V against the oracle's commit: the context rows are untouched; the first
+    attention layer's new rows are bitwise equal (its inputs are the embeddings); deeper layers
+    agree within the bf16 logit tolerance, since one rounding flip upstream moves a whole row."""
+    cfg = pair.cfg
     for li in range(cfg.n_attn):
-        for l in range(3):
+        for l in range(pair.lanes):
             n = int(pair.oc.kv_len[l])
             K, V = pair.dc.get_kv(li, l, 0, n)
             ok, ov = pair.oc.gather(li, l, n)
-            assert np.mean(K == ok) > 0.999 and np.mean(V == ov) > 0.999
-            assert np.max(np.abs(K - ok)) <= 2 ** -7 * np.max(np.abs(ok)) + 1e-6
-    pair.close()
+            assert np.array_equal(K[:context], ok[:context]) and np.array_equal(V[:context], ov[:context])
+            if li == 0 and cfg.layer_kinds[0] == "attn":
+                assert np.array_equal(K, ok) and np.array_equal(V, ov)
+            for a, b in ((K, ok), (V, ov)):
+                assert np.max(np.abs(a[context:] - b[context:])) <= 3e-2 * max(1.0, np.max(np.abs(b)))
 
 
 @pytest.mark.parametrize("context", [250, 1021])

@@ -22,8 +22,8 @@ Gated-delta-rule layer (Yang, Kautz & Hatamizadeh, "Gated Delta Networks"):
 The state is stored in float32 after every column, as the device stores it.
 
 Precision: float64 arithmetic, one rounding to float32 per dot product or
-reduction; bf16 rounding at the storage points of a bf16 model (see
-oracle.numerics).
+reduction; a bf16 model's weights and KV cache hold bf16 values, so k and v
+are rounded to bf16 as they are staged for the cache (see oracle.numerics).
 """
 from dataclasses import dataclass, field
 from typing import Callable, Dict, List, Optional, Sequence
@@ -101,7 +101,7 @@ class KVCache:
 @dataclass
 class RoundResult:
     logits: np.ndarray                 # [R, V] float32
-    hidden: np.ndarray                 # [R, H] final normed hidden (storage precision)
+    hidden: np.ndarray                 # [R, H] final normed hidden (float32)
     row_lane: np.ndarray               # [R]
     row_col: np.ndarray                # [R]
     lane_rows: List[range]             # rows of each lane
@@ -133,7 +133,13 @@ class OracleModel:
         return self.w["layer_fn"](i)
 
     def _st(self, x) -> np.ndarray:
+        """Storage precision of the KV cache (the model's dtype)."""
         return store(x, self.dtype)
+
+    @staticmethod
+    def _act(x) -> np.ndarray:
+        """Activations are float32 values."""
+        return f32(x)
 
     def _w64(self, w) -> np.ndarray:
         if self._f64 is None:
@@ -177,7 +183,7 @@ class OracleModel:
         ia = ig = 0
         for i in range(cfg.n_layers):
             lw = self._layer(i)
-            h = self._st(rmsnorm(x, lw["norm1"], cfg.rms_eps))
+            h = self._act(rmsnorm(x, lw["norm1"], cfg.rms_eps))
             if cfg.layer_kinds[i] == "attn":
                 o, k, v = self._attention(h, lw, ia, cache, lane_rows, pos)
                 staged_k.append(k)
@@ -188,12 +194,12 @@ class OracleModel:
                 gdn_staged.append(st)
                 ig += 1
             x = f32(x.astype(np.float64) + self._matT(o, lw["w_o"]))
-            h2 = self._st(rmsnorm(x, lw["norm2"], cfg.rms_eps))
+            h2 = self._act(rmsnorm(x, lw["norm2"], cfg.rms_eps))
             g = self._matT(h2, lw["w_gate"])
             u = self._matT(h2, lw["w_up"])
-            a = self._st(silu(g) * u.astype(np.float64))
+            a = self._act(silu(g) * u.astype(np.float64))
             x = f32(x.astype(np.float64) + self._matT(a, lw["w_down"]))
-        hf = self._st(rmsnorm(x, self.w["final_norm"], cfg.rms_eps))
+        hf = self._act(rmsnorm(x, self.w["final_norm"], cfg.rms_eps))
         logits = self.lm_head(hf)
         return RoundResult(logits, hf, row_lane, row_col, lane_rows, staged_k, staged_v, gdn_staged)
 
@@ -206,8 +212,8 @@ class OracleModel:
         q = y[:, : nq * d].reshape(R, nq, d)
         k = y[:, nq * d: (nq + nkv) * d].reshape(R, nkv, d)
         v = y[:, (nq + nkv) * d:].reshape(R, nkv, d)
-        q = self._st(rope(q, pos, cfg.rope_theta))
-        k = self._st(rope(k, pos, cfg.rope_theta))
+        q = self._act(rope(q, pos, cfg.rope_theta))
+        k = self._st(rope(k, pos, cfg.rope_theta))     # staged for the cache
         v = self._st(v)
         o = np.zeros((R, nq, d), np.float64)
         for l, rows in enumerate(lane_rows):
@@ -216,7 +222,7 @@ class OracleModel:
             keys = np.concatenate([ck, k[rows.start:rows.stop]], axis=0)
             vals = np.concatenate([cv, v[rows.start:rows.stop]], axis=0)
             o[rows.start:rows.stop] = attend(q[rows.start:rows.stop], keys, vals, n_ctx)
-        return self._st(o).reshape(R, nq * d), k, v
+        return self._act(o).reshape(R, nq * d), k, v
 
     def _gdn_inputs(self, h, lw):
         cfg = self.cfg
@@ -254,7 +260,7 @@ class OracleModel:
             for r in rows:
                 S = self.gdn_step(S, kn[r], v[r], alpha[r], beta[r])
                 o[r] = np.einsum("hij,hj->hi", S.astype(np.float64), qn[r].astype(np.float64))
-        o = self._st(f32(o)).reshape(R, hg * dg)
+        o = f32(o).reshape(R, hg * dg)
         return o, {"q": qn, "k": kn, "v": v, "alpha": alpha, "beta": beta}
 
     # ------------------------------------------------------------------ commit

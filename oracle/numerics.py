@@ -1,9 +1,11 @@
 """Rounding and element-wise textbook functions used by the oracle (float64 math).
 
-Storage contract for bf16 models: values are rounded to bf16 (round to nearest,
-ties to even) where such a model stores bf16 -- RMSNorm outputs, q/k/v after
-the positional rotation, the attention output and the SwiGLU product; the
-residual stream, logits and the gated-delta-rule quantities stay float32.
+Storage contract for bf16 models: what is stored in bf16 is the weights and
+the KV cache -- each column's k (after the positional rotation) and v are
+rounded to bf16 (round to nearest, ties to even) because that is the form the
+cache keeps them in.  Every activation (residual stream, RMSNorm outputs, q,
+attention output, SwiGLU product, gated-delta-rule quantities, logits) is a
+float32 value: one rounding of the float64 result.
 """
 import numpy as np
 

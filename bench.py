@@ -1,0 +1,302 @@
+"""Benchmark of the verify round on one MI355X.
+
+Workload (default): the 27B-class dense bf16 decoder (64 layers, H 5120, 40 q /
+8 kv heads x 128, SwiGLU FFN 17408, vocab 151936, random N(0, 0.02) weights)
+with 8 lanes x (k = 7 drafts + anchor) = 64 rows per round and 8192 tokens of
+synthetic committed context per lane in paged KV.  Drafts are planted against
+the model's own plain-greedy continuation with per-slot acceptance falling
+linearly from 0.9 (slot 1) to 0.35 (slot 7); a miss plants a different token.
+
+One step = one verify round through the whole hot path: the forward over all
+rows, the fused LM-head statistics, greedy acceptance and the commit, followed
+by the copy of the committed run back to the host (the drafter's input).
+Steps continue decoding from where the previous one stopped.
+
+Prints one JSON line: committed tokens/s as `value`, verify rows/s, the round's
+HBM roofline fraction, the dominant kernel's achieved bandwidth measured with
+HIP events over the timed region, and the oracle timed on host cores on a
+bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from speculative_decoding_verify_round_amd import binding as B  # noqa: E402
+from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "committed tokens/s & verify rows/s at lanes×(k+1); % of HBM roofline"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------- synthetic inputs on the GPU
+def gpu_weights(cfg, seed: int):
+    """Random N(0, 0.02) bf16 weights generated on the device (seeded per tensor)."""
+    dev = torch.device("cuda")
+
+    def normal(tid, shape, std=0.02):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 100003 + tid)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        flat = out.view(-1)
+        step = 1 << 26
+        for s in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - s)
+            flat[s:s + n] = (torch.randn(n, generator=g, device=dev) * std).to(torch.bfloat16)
+        return out
+
+    H, F = cfg.hidden, cfg.ffn
+    w = {"embed": normal(0, (cfg.vocab, H)), "lm_head": normal(1, (cfg.vocab, H)),
+         "final_norm": torch.ones(H, device=dev), "layers": []}
+    for i in range(cfg.n_layers):
+        base = 100 + 16 * i
+        n_in = cfg.qkv_rows if cfg.layer_kinds[i] == "attn" else cfg.gdn_in_rows
+        n_o = cfg.n_q_heads * cfg.head_dim if cfg.layer_kinds[i] == "attn" else cfg.gdn_heads * cfg.gdn_dim
+        w["layers"].append({
+            "norm1": torch.ones(H, device=dev), "norm2": torch.ones(H, device=dev),
+            "w_in": normal(base, (n_in, H)), "w_o": normal(base + 1, (H, n_o)),
+            "w_gate": normal(base + 2, (F, H)), "w_up": normal(base + 3, (F, H)), "w_down": normal(base + 4, (H, F)),
+        })
+    return w
+
+
+def fill_pools(dc: DeviceCache, seed: int):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for pool in (dc.k_pool, dc.v_pool):
+        for li in range(pool.shape[0]):
+            flat = pool[li].view(-1)
+            step = 1 << 26
+            for s in range(0, flat.numel(), step):
+                n = min(step, flat.numel() - s)
+                flat[s:s + n] = torch.randn(n, generator=g, device="cuda").to(pool.dtype)
+
+
+# ---------------------------------------------------------------------------- algorithmic bytes
+def round_bytes(cfg, lanes, k, context, committed_mean):
+    """Bytes a round must move: weights once, KV once per lane, staging, compaction, embeddings."""
+    ab = 2
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    R = lanes * (k + 1)
+    per_layer = (cfg.qkv_rows * H + H * cfg.n_q_heads * cfg.head_dim + 3 * F * H) * ab
+    weights = cfg.n_layers * per_layer + V * H * ab
+    kv_row = 2 * cfg.n_kv_heads * cfg.head_dim * ab * cfg.n_attn
+    kv = lanes * context * kv_row
+    staging = R * kv_row
+    compaction = lanes * committed_mean * kv_row * 2
+    embed = R * H * ab
+    return weights + kv + staging + compaction + embed
+
+
+def gate_up_bytes(cfg, R):
+    return 2 * cfg.ffn * cfg.hidden * 2 + R * cfg.hidden * 2 + R * cfg.ffn * 2
+
+
+# ---------------------------------------------------------------------------- CPU baseline (oracle)
+def cpu_baseline(cfg, lanes, k, context, tokens_per_round):
+    """The oracle on a bounded sample of the same round: one of the 64 layers and the LM head
+    for all rows, at full width and context; scaled to a full round."""
+    import oracle
+    from oracle import KVCache, OracleModel
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = cores
+    one = synth.get_config(cfg.name, n_layers=1)
+    log("cpu baseline: generating a 1-layer sample")
+    w = synth.model_weights(one)
+    om = OracleModel(one, w, keep_f64=False)          # streamed weights, as a 64-layer oracle runs
+    blocks = (context + 16) // 16 + 1
+    bt, nb = synth.block_table(one, lanes, blocks)
+    oc = KVCache(kv_len=np.full(lanes, context, np.int64), block_table=bt.astype(np.int64), block=16)
+    oc.pool_k.append(np.zeros((nb, 16, one.n_kv_heads, one.head_dim), np.float32))
+    oc.pool_v.append(np.zeros_like(oc.pool_k[0]))
+    for l in range(lanes):
+        kk, vv = synth.kv_context(one, 0, l, context)
+        oc.scatter(0, l, 0, kk, vv)
+    toks = [[int(t) for t in synth.uniform_tokens(one.input_seed, 40 + l, k + 1, one.vocab)] for l in range(lanes)]
+    log("cpu baseline: timing one layer + LM head")
+    t0 = time.perf_counter()
+    res = om.verify_round(oc, toks)
+    t_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    om.lm_head(res.hidden)
+    t_head = time.perf_counter() - t0
+    t_layer = max(t_all - t_head, 1e-9)
+    t_round = cfg.n_layers * t_layer + t_head
+    tok_s = lanes * tokens_per_round / t_round
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "threads": threads, "kind": "oracle",
+            "sample": f"1 of {cfg.n_layers} decoder layers + LM head, {lanes} lanes x {k + 1} rows, context "
+                      f"{context}; {t_layer:.2f} s/layer and {t_head:.2f} s LM head scaled to a "
+                      f"{t_round:.1f} s round"}
+
+
+# ---------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="dense-27b")
+    ap.add_argument("--lanes", type=int, default=8)
+    ap.add_argument("--k", type=int, default=7)
+    ap.add_argument("--context", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plain-steps", type=int, default=10, help="plain one-row rounds timed for comparison")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the verify round does not shard "
+                                   "(--gpus must be 1)"}))
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs one process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    cfg = synth.get_config(args.config)
+    L, k, ctx = args.lanes, args.k, args.context
+    R = L * (k + 1)
+    steps, warm = args.steps, args.warmup
+    total_rounds = steps + warm
+    ref_len = total_rounds * (k + 1) + 2
+    max_blocks = (ctx + ref_len + 32) // 16 + 1
+    log(f"{cfg.name}: weights on the device")
+    w = gpu_weights(cfg, cfg.weight_seed)
+    dm = DeviceModel(cfg, w)
+    del w
+    bt, nb = synth.block_table(cfg, L, max_blocks)
+    dc = DeviceCache(dm, L, max_blocks, nb, block_table=bt, kv_len=[ctx] * L)
+    log("KV context")
+    fill_pools(dc, cfg.input_seed)
+    if dc.gdn is not None:
+        dc.gdn.normal_(0.0, 1.0 / np.sqrt(128.0))
+    torch.cuda.synchronize()
+    anchors = [int(t) for t in synth.uniform_tokens(cfg.input_seed, 5, L, cfg.vocab)]
+
+    # reference plain-greedy continuation (one row per lane per round); also the plain-round timing
+    log(f"reference continuation: {ref_len} plain rounds")
+    ref = np.zeros((L, ref_len + 1), np.int64)
+    ref[:, 0] = anchors
+    cur = torch.tensor(anchors, dtype=torch.int32, device="cuda")
+    plain_times = []
+    for s in range(ref_len):
+        rc = dc.round([[0]] * L, tokens_dev=cur)
+        t0 = time.perf_counter()
+        dc.verify(rc)
+        dc.accept(rc, stats=False)
+        dc.commit(rc)
+        nxt = dc.out_tokens[:, 0].clone()
+        torch.cuda.synchronize()
+        plain_times.append(time.perf_counter() - t0)
+        ref[:, s + 1] = nxt.cpu().numpy()
+        cur = nxt
+    plain_ms = float(np.median(plain_times[2:2 + max(1, args.plain_steps)]) * 1e3)
+    dc.set_kv_len([ctx] * L)
+
+    # planted drafts: slot i matches the reference with probability alpha_i
+    alpha = np.linspace(0.9, 0.35, k)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.input_seed, 77])))
+    pos = np.zeros(L, np.int64)          # tokens committed so far per lane (ref[l, pos] is the anchor)
+
+    def drafts_for(l):
+        p = int(pos[l])
+        d = []
+        for i in range(k):
+            t = int(ref[l, p + 1 + i])
+            if rng.random() >= alpha[i]:
+                t = (t + 1 + int(rng.integers(0, cfg.vocab - 1))) % cfg.vocab
+            d.append(t)
+        return d
+
+    tok_host = torch.empty(R, dtype=torch.int32).pin_memory()
+    tok_dev = torch.empty(R, dtype=torch.int32, device="cuda")
+    committed_log = []
+
+    def step():
+        flat = []
+        for l in range(L):
+            flat += [int(ref[l, pos[l]])] + drafts_for(l)
+        tok_host.copy_(torch.tensor(flat, dtype=torch.int32))
+        tok_dev.copy_(tok_host, non_blocking=True)
+        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev)
+        dc.verify(rc)
+        dc.accept(rc, stats=False)
+        dc.commit(rc)
+        c = dc.committed.cpu().numpy()          # the per-round device -> host crossing
+        for l in range(L):
+            pos[l] += int(c[l])
+        committed_log.append(c.copy())
+
+    log(f"warmup {warm} steps")
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    committed_log.clear()
+    B.spec_profile_enable(dm.handle, B.SPEC_K_GATE_UP)
+    log(f"timed {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gu_ms, gu_n = B.spec_profile_collect(dm.handle)
+    B.spec_profile_enable(dm.handle, B.SPEC_K_NONE)
+
+    committed = np.array(committed_log)               # [steps, L]
+    ms_step = elapsed / steps * 1e3
+    tok_s = committed.sum() / elapsed
+    rows_s = R * steps / elapsed
+    tpr = float(committed.mean())
+    textbook = 1.0 + float(np.sum(np.cumprod(alpha)))
+    rbytes = round_bytes(cfg, L, k, ctx + int(pos.mean()), tpr)
+    gu_avg_ms = gu_ms / max(gu_n, 1)
+    gu_bytes = gate_up_bytes(cfg, R)
+    gu_gbs = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer dense bf16 decoder H{cfg.hidden}, "
+                               f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, FFN {cfg.ffn}, "
+                               f"vocab {cfg.vocab}; {L} lanes x (k={k} + 1) = {R} rows, context {ctx}, greedy, "
+                               f"drafts planted at slot acceptance 0.9..0.35",
+                   "lanes": L, "k": k, "rows": R, "context": ctx, "mode": "greedy"},
+        "verify_rows_per_s": round(rows_s, 1),
+        "tokens_per_round": round(tpr, 3),
+        "textbook_tokens_per_round": round(textbook, 3),
+        "drafter": f"planted α 0.9..0.35 · depth {k}, no gate · acceptance "
+                   f"{(committed - 1).sum()}/{committed.size * k} guesses · greedy · {L} streams",
+        "plain_round_ms": round(plain_ms, 3),
+        "verify_over_plain": round(ms_step / plain_ms, 3),
+        "round_roofline_frac": round(rbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "gate/up projection (SwiGLU epilogue)",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(gu_avg_ms, 5), "launches": gu_n, "bytes_per_launch": gu_bytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, L, k, ctx, tpr)
+    dm.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

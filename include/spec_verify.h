@@ -225,7 +225,8 @@ int spec_debug_logits(const spec_model* model, const spec_round* round, float* l
 
 /* Tests and measurement: the skinny projection kernel alone, Y[R][N] = X[R][K] W[N][K]^T
  * (X, W in the model dtype, Y float), with the split and launch shape the round
- * uses for an [N][K] weight.  R <= SPEC_MAX_ROWS.  `workspace` must hold
+ * uses for an [N][K] weight.  X is taken as exact (one bf16 plane); inside a
+ * round a bf16 model's float32 activations enter the same kernel as two planes.  R <= SPEC_MAX_ROWS.  `workspace` must hold
  * spec_workspace_bytes(model, 1, R, 1) bytes or more. */
 int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float* Y, int R,
                     int N, int K, void* workspace, size_t workspace_bytes, void* stream);

@@ -15,24 +15,29 @@
 // therefore independent of how many columns the round carries and of whether
 // a key is still staged or already committed.
 //
-// bf16 path (head_dim 128), per 32-position step:
-//   S^T[pos][query] = K . Q^T with v_mfma_f32_16x16x32_bf16 (K rows = A, Q = B);
-//   P = exp2(S * log2(e)/sqrt(d) - m) kept in fp32 and split into bf16 hi + lo
-//   parts; O^T[d][query] += V^T . P_hi^T + V^T . P_lo^T.  The V pool is stored
-//   d-major inside a block ([d][16 slots]) so that the V^T operand is read
-//   straight from memory; the lane's key order inside the K = 32 MFMA step
-//   equals the order in which the S^T result left it, so P needs no shuffle.
+// bf16 path (head_dim 128): the workgroup stages 64-position K and V tiles in
+// LDS (the next tile's loads are in flight while the current one is used);
+// wave w owns query tile w (16 of the lane's (k+1) x G query rows) over the
+// whole chunk.  Per 32 positions:
+//   S^T[pos][query] = K . Q^T with v_mfma_f32_16x16x32_bf16 (K rows = A; the
+//   float32 queries = B, as bf16 hi + lo planes);
+//   P = exp2(S * log2(e)/sqrt(d) - m) in fp32, split into bf16 hi + lo;
+//   O^T[d][query] += V^T . P^T.  The V pool is stored d-major inside a block
+//   ([d][16 slots]) so that V^T tiles are contiguous; the lane's key order
+//   inside the K = 32 MFMA step equals the order in which the S^T result left
+//   it, so P needs no shuffle.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
 template <int QT>
-__global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnParams p) {
-  constexpr int D = 128, PW = D + 2;
-  __shared__ float lds[4 * QT * 16 * PW];
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
+  constexpr int D = 128, STEP = 64, KP = D + 8, VP = STEP + 8, PW = D + 2;
+  __shared__ bf16_t Ks[STEP * KP];   // [position][d], rows padded by 16 B
+  __shared__ bf16_t Vs[D * VP];      // [d][position], rows padded by 16 B
   const int c = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int cols = p.ri.lane_cols[l], rs = p.ri.lane_start[l];
   const int cap = p.max_blocks * kBlock;
@@ -41,102 +46,114 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnParams p) {
   const int pos0 = c * p.chunk;
   if (pos0 >= end) return;
   const int Mq = cols * p.G;
-  const int wlen = p.chunk >> 2;
-  const int wb = pos0 + wave * wlen, we = min(wb + wlen, end);
+  const int cend = min(pos0 + p.chunk, end);
+  const int nsteps = (cend - pos0 + STEP - 1) / STEP;
   const int* bt = p.block_table + (size_t)l * p.max_blocks;
-  const bf16_t* Qp = reinterpret_cast<const bf16_t*>(p.q);
+  const float* Qp = p.q;
   const bf16_t* Kp = reinterpret_cast<const bf16_t*>(p.kpool);
   const bf16_t* Vp = reinterpret_cast<const bf16_t*>(p.vpool);
   const bf16_t* SK = reinterpret_cast<const bf16_t*>(p.sk);
   const bf16_t* SV = reinterpret_cast<const bf16_t*>(p.sv);
   const int nkv = p.nkv;
 
-  u32x4 qf[QT][4];
-  int lim[QT];
+  // ---- cooperative staging of one 64-position step: 4 K items and 4 V items of 16 B per thread
+  u32x4 kreg[4], vreg[4];
+  auto load_step = [&](int s) {
+    const int base = pos0 + s * STEP;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int m = qt * 16 + r16;
-    if (m < Mq) {
-      const int j = m / p.G, hh = m - j * p.G;
-      const bf16_t* ptr = Qp + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) qf[qt][ds] = *reinterpret_cast<const u32x4*>(ptr + ds * 32);
-      lim[qt] = kvl + j;
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) qf[qt][ds] = u32x4{0u, 0u, 0u, 0u};
-      lim[qt] = -1;
+    for (int j = 0; j < 4; ++j) {
+      const int pos = base + (tid >> 4) + 16 * j, seg = tid & 15;
+      const bf16_t* src = nullptr;
+      if (pos < kvl) src = Kp + (((size_t)clamp_blk(bt[pos >> 4], p.n_blocks) * nkv + g) * kBlock + (pos & 15)) * D;
+      else if (pos < end) src = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D;
+      kreg[j] = src ? *reinterpret_cast<const u32x4*>(src + seg * 8) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  float mrun[QT], lrun[QT];
-  f32x4 O[QT][8];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = -INFINITY; lrun[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int p0 = wb; p0 < we; p0 += 32) {
-    // K rows of the two 16-position tiles: lane row = r16, d slice by kq
-    u32x4 kf[2][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int pos = p0 + st * 16 + r16;
-      const bf16_t* kp = nullptr;
-      if (pos < kvl) {
-        const int blk = clamp_blk(bt[pos >> 4], p.n_blocks);
-        kp = Kp + (((size_t)blk * nkv + g) * kBlock + (pos & 15)) * D + kq * 8;
-      } else if (pos < end) {
-        kp = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D + kq * 8;
-      }
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        kf[st][ds] = kp ? *reinterpret_cast<const u32x4*>(kp + ds * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // V^T operand: lane row d = dt*16 + r16; keys 4kq..4kq+3 of each tile
-    u32x4 vf[8];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int base = p0 + st * 16;
-      if (base + 16 <= kvl) {
-        const int blk = clamp_blk(bt[base >> 4], p.n_blocks);
-        const bf16_t* vp = Vp + (((size_t)blk * nkv + g) * D + r16) * kBlock + 4 * kq;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(vp + (size_t)dt * 16 * kBlock);
-          vf[dt][2 * st] = v2[0];
-          vf[dt][2 * st + 1] = v2[1];
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int bpos = base + 16 * j, d = tid >> 1, hf = tid & 1;
+      if (bpos + 16 <= kvl) {
+        const int blk = clamp_blk(bt[bpos >> 4], p.n_blocks);
+        vreg[j] = *reinterpret_cast<const u32x4*>(Vp + (((size_t)blk * nkv + g) * D + d) * kBlock + hf * 8);
       } else {
-        const int blk = base < kvl ? clamp_blk(bt[base >> 4], p.n_blocks) : 0;
+        const int blk = bpos < kvl ? clamp_blk(bt[bpos >> 4], p.n_blocks) : 0;
+        uint32_t w[4];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const int d = dt * 16 + r16;
-          bf16_t e4[4];
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t two = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int pos = base + 4 * kq + e;
+          for (int hh = 0; hh < 2; ++hh) {
+            const int pos = bpos + hf * 8 + 2 * e2 + hh;
             bf16_t v = 0;
             if (pos < kvl) v = Vp[(((size_t)blk * nkv + g) * D + d) * kBlock + (pos & 15)];
             else if (pos < end) v = SV[((size_t)(rs + pos - kvl) * nkv + g) * D + d];
-            e4[e] = v;
+            two |= (uint32_t)v << (16 * hh);
           }
-          vf[dt][2 * st] = (uint32_t)e4[0] | ((uint32_t)e4[1] << 16);
-          vf[dt][2 * st + 1] = (uint32_t)e4[2] | ((uint32_t)e4[3] << 16);
+          w[e2] = two;
         }
+        vreg[j] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
+  };
+  auto store_step = [&]() {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * j) * KP + (tid & 15) * 8) = kreg[j];
+      *reinterpret_cast<u32x4*>(Vs + (tid >> 1) * VP + 16 * j + (tid & 1) * 8) = vreg[j];
+    }
+  };
+
+  // ---- this wave's query tile: rows m = wave*16 + r16 (column j = m / G, head g*G + m % G)
+  const bool owner = wave < QT && wave * 16 < Mq;
+  const int m = wave * 16 + r16;
+  u32x4 qh[4], ql[4];            // the float32 query as bf16 hi + lo planes
+  int lim = -1;
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) { qh[ds] = u32x4{0u, 0u, 0u, 0u}; ql[ds] = qh[ds]; }
+  if (owner && m < Mq) {
+    const int j = m / p.G, hh = m - j * p.G;
+    const float* ptr = Qp + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
+        qh[ds][i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        ql[ds][i] = (uint32_t)f2bf(v[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * i + 1] - bf2f(h1)) << 16);
+      }
+    }
+    lim = kvl + j;
+  }
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_step(0);
+  for (int s = 0; s < nsteps; ++s) {
+    __syncthreads();              // every wave is done reading the previous step
+    store_step();
+    __syncthreads();              // this step is staged
+    if (s + 1 < nsteps) load_step(s + 1);   // in flight during the compute below
+    if (!owner) continue;
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const int p0 = pos0 + s * STEP + ss * 32;
       f32x4 sc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
+        const bf16_t* kr = Ks + (ss * 32 + st * 16 + r16) * KP + kq * 8;
         sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) sc[st] = mfma_bf16(kf[st][ds], qf[qt][ds], sc[st]);
+        for (int ds = 0; ds < 4; ++ds) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + ds * 32);
+          sc[st] = mfma_bf16(kf, ql[ds], sc[st]);
+          sc[st] = mfma_bf16(kf, qh[ds], sc[st]);
+        }
       }
-      // lane holds S^T[p0 + 16 st + 4 kq + e][query qt*16 + r16]
+      // lane holds S^T[p0 + 16 st + 4 kq + e][query m]
       float x[8];
       float mx = -INFINITY;
 #pragma unroll
@@ -144,79 +161,58 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int pos = p0 + st * 16 + 4 * kq + e;
-          const float v = pos <= lim[qt] ? sc[st][e] * p.scale_log2 : -INFINITY;
+          const float v = pos <= lim ? sc[st][e] * p.scale_log2 : -INFINITY;
           x[st * 4 + e] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[qt], mx);
+      const float mnew = fmaxf(mrun, mx);
       float pr[8];
       float alpha = 1.f;
       if (mnew == -INFINITY) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) pr[i] = 0.f;
       } else {
-        alpha = exp2f(mrun[qt] - mnew);
+        alpha = exp2f(mrun - mnew);
 #pragma unroll
         for (int i = 0; i < 8; ++i) pr[i] = exp2f(x[i] - mnew);
       }
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) ps += pr[i];
-      lrun[qt] = lrun[qt] * alpha + ps;
-      mrun[qt] = mnew;
+      lrun = lrun * alpha + ps;
+      mrun = mnew;
+      // P = hi + lo in bf16 (what is left is below 2^-17 P)
       u32x4 ph, pl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16_t h0 = f2bf(pr[2 * i]), h1 = f2bf(pr[2 * i + 1]);
-        const bf16_t l0 = f2bf(pr[2 * i] - bf2f(h0)), l1 = f2bf(pr[2 * i + 1] - bf2f(h1));
         ph[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        pl[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        pl[i] = (uint32_t)f2bf(pr[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(pr[2 * i + 1] - bf2f(h1)) << 16);
       }
+      // O^T[d][m] += V^T[d][keys] P^T[keys][m]; the lane's keys are (tile st, 4 kq .. 4 kq + 3)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        O[qt][dt] *= alpha;
-        O[qt][dt] = mfma_bf16(vf[dt], ph, O[qt][dt]);
-        O[qt][dt] = mfma_bf16(vf[dt], pl, O[qt][dt]);
+        const bf16_t* vr = Vs + (dt * 16 + r16) * VP + ss * 32 + 4 * kq;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vr + 16);
+        const u32x4 vf = {a0[0], a0[1], a1[0], a1[1]};
+        O[dt] *= alpha;
+        O[dt] = mfma_bf16(vf, pl, O[dt]);
+        O[dt] = mfma_bf16(vf, ph, O[dt]);
       }
     }
   }
-  // wave partials -> LDS; lane holds O^T[d = dt*16 + 4kq + e][query qt*16 + r16]
+  if (!owner) return;
+  // chunk partial of query m: lane holds O^T[d = dt*16 + 4kq + e][m]
+  float lt = lrun + __shfl_xor(lrun, 16);
+  lt += __shfl_xor(lt, 32);
+  if (m >= Mq) return;
+  float* out = p.part + ((((size_t)l * nkv + g) * p.n_chunks + c) * 64 + m) * PW;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float lt = lrun[qt] + __shfl_xor(lrun[qt], 16);
-    lt += __shfl_xor(lt, 32);
-    const int m = qt * 16 + r16;
-    float* dst = lds + ((size_t)wave * QT * 16 + m) * PW;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[dt * 16 + 4 * kq + e] = O[qt][dt][e];
-    if (kq == 0) { dst[D] = mrun[qt]; dst[D + 1] = lt; }
-  }
-  __syncthreads();
-  float* out = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
-  for (int idx = threadIdx.x; idx < Mq * D; idx += blockDim.x) {
-    const int m = idx >> 7, dd = idx & (D - 1);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, lds[((size_t)w * QT * 16 + m) * PW + D]);
-    float Oc = 0.f, Lc = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float* src = lds + ((size_t)w * QT * 16 + m) * PW;
-        if (src[D] != -INFINITY) {
-          const float f = exp2f(src[D] - M);
-          Oc += src[dd] * f;
-          Lc += src[D + 1] * f;
-        }
-      }
-    }
-    out[(size_t)m * PW + dd] = Oc;
-    if (dd == 0) { out[(size_t)m * PW + D] = M; out[(size_t)m * PW + D + 1] = Lc; }
-  }
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * kq) = O[dt];
+  if (kq == 0) { out[D] = mrun; out[D + 1] = lt; }
 }
 
 // fp32 model: VALU, one query row at a time per wave, 64 positions per step (lane = position).
@@ -245,7 +241,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
     const int j = m / p.G, hh = m - j * p.G;
     const float* q = Qp + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D;
     const int lim = kvl + j;
-    float mr = -INFINITY, lr = 0.f, o0 = 0.f, o1 = 0.f;
+    float mr = -INFINITY;
+    double lr = 0.0, o0 = 0.0, o1 = 0.0;
     for (int p0 = wb; p0 < we; p0 += 64) {
       const int pos = p0 + lane;
       const bool valid = pos < we && pos <= lim;
@@ -254,20 +251,23 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         const float* kr;
         if (pos < kvl) kr = Kp + (((size_t)clamp_blk(bt[pos >> 4], p.n_blocks) * nkv + g) * kBlock + (pos & 15)) * D;
         else kr = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D;
-        float a = 0.f;
-        for (int i = 0; i < D; ++i) a = fmaf(q[i], kr[i], a);
-        s = a * p.scale_log2;
+        double a = 0.0;
+        for (int i = 0; i < D; ++i) a += (double)q[i] * (double)kr[i];
+        s = (float)(a * p.scale_log2);
       }
       const float mx = wave_max(s);
       const float mnew = fmaxf(mr, mx);
       if (mnew == -INFINITY) continue;
       const float alpha = exp2f(mr - mnew);
       const float pr = valid ? exp2f(s - mnew) : 0.f;
-      lr = lr * alpha + wave_sum(pr);
+      double psum = pr;
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1) psum += __shfl_xor(psum, mm);
+      lr = lr * (double)alpha + psum;
       o0 *= alpha; o1 *= alpha;
       const int nval = min(64, we - p0);
       for (int t = 0; t < nval; ++t) {
-        const float pt = __shfl(pr, t);
+        const double pt = __shfl(pr, t);
         const int vp = p0 + t;
         const float* vrow;
         size_t stride;
@@ -278,15 +278,15 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
           vrow = SV + ((size_t)(rs + vp - kvl) * nkv + g) * D;
           stride = 1;
         }
-        if (lane < D) o0 = fmaf(pt, vrow[(size_t)lane * stride], o0);
-        if (lane + 64 < D) o1 = fmaf(pt, vrow[(size_t)(lane + 64) * stride], o1);
+        if (lane < D) o0 += pt * (double)vrow[(size_t)lane * stride];
+        if (lane + 64 < D) o1 += pt * (double)vrow[(size_t)(lane + 64) * stride];
       }
       mr = mnew;
     }
     float* dst = lds + ((size_t)wave * Mq + m) * PW;
-    if (lane < D) dst[lane] = o0;
-    if (lane + 64 < D) dst[lane + 64] = o1;
-    if (lane == 0) { dst[D] = mr; dst[D + 1] = lr; }
+    if (lane < D) dst[lane] = (float)o0;
+    if (lane + 64 < D) dst[lane + 64] = (float)o1;
+    if (lane == 0) { dst[D] = mr; dst[D + 1] = (float)lr; }
   }
   __syncthreads();
   float* out = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
@@ -294,19 +294,19 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
     const int m = idx / D, dd = idx - m * D;
     float M = -INFINITY;
     for (int w = 0; w < 4; ++w) M = fmaxf(M, lds[((size_t)w * Mq + m) * PW + D]);
-    float Oc = 0.f, Lc = 0.f;
+    double Oc = 0.0, Lc = 0.0;
     if (M != -INFINITY) {
       for (int w = 0; w < 4; ++w) {
         const float* src = lds + ((size_t)w * Mq + m) * PW;
         if (src[D] != -INFINITY) {
-          const float f = exp2f(src[D] - M);
-          Oc += src[dd] * f;
-          Lc += src[D + 1] * f;
+          const double f = exp2((double)src[D] - (double)M);
+          Oc += (double)src[dd] * f;
+          Lc += (double)src[D + 1] * f;
         }
       }
     }
-    out[(size_t)m * PW + dd] = Oc;
-    if (dd == 0) { out[(size_t)m * PW + D] = M; out[(size_t)m * PW + D + 1] = Lc; }
+    out[(size_t)m * PW + dd] = (float)Oc;
+    if (dd == 0) { out[(size_t)m * PW + D] = M; out[(size_t)m * PW + D + 1] = (float)Lc; }
   }
 }
 
@@ -347,17 +347,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
     const int m = idx / D, dd = idx - m * D;
     float M = -INFINITY;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, base[((size_t)c * 64 + m) * PW + D]);
-    float Oc = 0.f, Lc = 0.f;
+    double Oc = 0.0, Lc = 0.0;
     for (int c = 0; c < nch; ++c) {
       const float* src = base + ((size_t)c * 64 + m) * PW;
       if (src[D] != -INFINITY) {
-        const float f = exp2f(src[D] - M);
-        Oc += src[dd] * f;
-        Lc += src[D + 1] * f;
+        const double f = exp2((double)src[D] - (double)M);
+        Oc += (double)src[dd] * f;
+        Lc += (double)src[D + 1] * f;
       }
     }
     const int j = m / p.G, hh = m - j * p.G;
-    st_act(o + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + dd, Oc / Lc);
+    st_out(o, (size_t)p.ri.R * p.nq * D, ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + dd, (float)(Oc / Lc));
   }
 }
 

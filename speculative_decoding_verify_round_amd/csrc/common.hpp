@@ -80,6 +80,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ int clamp_blk(int b, int n) { return b < 0 ? 0 : (b >= n ? n - 1 : b); }
 
+// Block-wide float64 sum with a fixed reduction tree; `red` holds >= 32 doubles.
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
 // (value, index) order used by every argmax: larger value wins, lower index on ties.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -109,15 +122,31 @@ __device__ __forceinline__ float u01(uint32_t w) {
 }
 
 // ----------------------------------------------------------------------------- launch parameters
+// A float32 activation x is handed to the MFMA projections as two bf16 planes,
+// hi = bf16(x) and lo = bf16(x - hi) (x = hi + lo to 2^-17 relative).
+__device__ __forceinline__ void st_planes(bf16_t* hi, size_t plane, float v) {
+  const bf16_t h = f2bf(v);
+  hi[0] = h;
+  hi[plane] = f2bf(v - bf2f(h));
+}
+
+// Store a float32 activation: as is for an fp32 model, as hi/lo bf16 planes for a bf16 model.
+__device__ __forceinline__ void st_out(float* base, size_t plane, size_t i, float v) {
+  (void)plane;
+  base[i] = v;
+}
+__device__ __forceinline__ void st_out(bf16_t* base, size_t plane, size_t i, float v) { st_planes(base + i, plane, v); }
+
 struct GemmParams {
-  const bf16_t* X;      // [R][K] activations (bf16)
+  const bf16_t* Xh;     // [R][K] activation hi plane
+  const bf16_t* Xl;     // [R][K] lo plane, or null when the activations are exact bf16
   const bf16_t* W0;     // [N][K]
   const bf16_t* W1;     // [N][K] second matrix (gate/up) or null
   int R, N, K;
   int S;                // k-splits, each a whole number of 256-wide chunks
   int groups;           // N / 16
   float* P;             // [S][R][N] fp32 partials
-  bf16_t* Yb;           // [R][N] SwiGLU output (bf16)
+  bf16_t* Yb;           // SwiGLU output as planes [2][R][N]
 };
 
 struct GemmF32Params {
@@ -147,7 +176,8 @@ struct LmPartial {
 };
 
 struct LmParams {
-  const void* X;           // [R][H] final hidden (act dtype)
+  const void* X;           // final hidden: planes [2][R][H] (bf16 model) or [R][H] float
+  int xs;                  // bf16 planes in use (1: exact bf16 hidden states, 2: hi + lo)
   const void* W;           // [V][H]
   int R, V, H;
   int groups;              // number of partial groups per row
@@ -177,9 +207,10 @@ struct LaneDecision {
 };
 
 struct RaceParams {
-  const void* X;           // [R][H]
+  const void* X;           // planes [2][R][H] (bf16 model) or [R][H] float
+  int xs;
   const void* W;           // [V][H]
-  int V, H, L;
+  int R, V, H, L;
   int groups;
   const float* q;          // [R][V]
   const int32_t* kv_len;
@@ -191,7 +222,7 @@ struct RaceParams {
 };
 
 struct AttnParams {
-  const void* q;          // [R][nq][d]
+  const float* q;         // [R][nq][d] float32 queries
   const void* sk;         // staged K [R][nkv][d]
   const void* sv;         // staged V [R][nkv][d]
   const void* kpool;      // layer slice [n_blocks][nkv][16][d]

@@ -21,55 +21,74 @@
 namespace sv {
 
 constexpr int kSteps = 8;   // MFMA k-steps (32 each) per 256-wide chunk
+constexpr int kRingW = 8;   // k-steps of W in flight per wave
+constexpr int kRingX = 2;   // k-steps of X in flight per wave (L1/L2 hits)
 
-// Ring depth (k-steps of W and X in flight per wave): eight, or four for the
-// widest variant so that it stays within 256 VGPRs (two waves per SIMD).
-template <int RT, int NMAT>
-struct Ring { static constexpr int U = (RT + NMAT > 5) ? 4 : 8; };
-
-// acc[m][t] += W_m[16 features][k] * X[16 rows of tile t][k]^T over k-chunks [c0, c1).
-template <int RT, int NMAT>
-__device__ __forceinline__ void gemm_core(const bf16_t* const (&wb)[NMAT], const bf16_t* const (&xb)[RT],
-                                          int c0, int c1, f32x4 (&acc)[NMAT][RT]) {
-  constexpr int U = Ring<RT, NMAT>::U;
+// acc[m][t][e] += W_m[16 features][k] . X[16 rows of tile t][k] over k-chunks [c0, c1).
+// X arrives as XS bf16 planes (hi, lo); each k-step chains the planes' MFMAs
+// (lo first) from a zero accumulator, and the step's fp32 result is added to a
+// float64 accumulator, so the K sum carries about one fp32 ulp of error.
+// Loads are issued X(step + 2) before W(step + 8) so that waiting for an X
+// step never waits for the younger W loads behind it (vmcnt counts in order).
+template <int RT, int NMAT, int XS>
+__device__ __forceinline__ void gemm_core(const bf16_t* const (&wb)[NMAT], const bf16_t* const (&xb)[XS][RT],
+                                          int c0, int c1, double (&acc)[NMAT][RT][4]) {
   if (c0 >= c1) return;
-  const int s0 = c0 * kSteps, ns = (c1 - c0) * kSteps;   // a multiple of U
-  u32x4 wr[U][NMAT];
-  u32x4 xr[U][RT];
+  const int s0 = c0 * kSteps, ns = (c1 - c0) * kSteps;   // a multiple of kRingW
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  u32x4 wr[kRingW][NMAT];
+  u32x4 xr[kRingX][XS][RT];
+  auto loadW = [&](int slot, int st) {
+    const int k = (s0 + st) * 32;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int k = (s0 + u) * 32;
+    for (int m = 0; m < NMAT; ++m) wr[slot][m] = ld_stream(reinterpret_cast<const u32x4*>(wb[m] + k));
+  };
+  auto loadX = [&](int slot, int st) {
+    const int k = (s0 + st) * 32;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) wr[u][m] = ld_stream(reinterpret_cast<const u32x4*>(wb[m] + k));
+    for (int x = 0; x < XS; ++x)
 #pragma unroll
-    for (int t = 0; t < RT; ++t) xr[u][t] = *reinterpret_cast<const u32x4*>(xb[t] + k);
-  }
-  for (int i = 0; i < ns - U; i += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) acc[m][t] = mfma_bf16(wr[u][m], xr[u][t], acc[m][t]);
-      const int k = (s0 + i + U + u) * 32;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) wr[u][m] = ld_stream(reinterpret_cast<const u32x4*>(wb[m] + k));
-#pragma unroll
-      for (int t = 0; t < RT; ++t) xr[u][t] = *reinterpret_cast<const u32x4*>(xb[t] + k);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
+      for (int t = 0; t < RT; ++t) xr[slot][x][t] = *reinterpret_cast<const u32x4*>(xb[x][t] + k);
+  };
+  auto step = [&](int ws, int xsl) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[m][t] = mfma_bf16(wr[u][m], xr[u][t], acc[m][t]);
+      for (int t = 0; t < RT; ++t) {
+        f32x4 d = zero;
+#pragma unroll
+        for (int x = XS - 1; x >= 0; --x) d = mfma_bf16(wr[ws][m], xr[xsl][x][t], d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[m][t][e] += (double)d[e];
+      }
+  };
+#pragma unroll
+  for (int u = 0; u < kRingX; ++u) loadX(u, u);
+#pragma unroll
+  for (int u = 0; u < kRingW; ++u) loadW(u, u);
+  for (int i = 0; i < ns - kRingW; i += kRingW) {
+#pragma unroll
+    for (int u = 0; u < kRingW; ++u) {
+      step(u, u % kRingX);
+      loadX(u % kRingX, i + u + kRingX);
+      loadW(u, i + u + kRingW);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRingW; ++u) {
+    step(u, u % kRingX);
+    if (u + kRingX < kRingW) loadX(u % kRingX, ns - kRingW + u + kRingX);
+  }
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// float(silu(g) * u) evaluated in float64 from the fp32-rounded projections
+__device__ __forceinline__ float swiglu(double g64, double u64) {
+  const double g = (double)(float)g64, u = (double)(float)u64;
+  return (float)(g / (1.0 + exp(-g)) * u);
+}
 
 // ------------------------------------------------------------------------------- projection
-template <int RT, int NMAT, bool SWIGLU>
+template <int RT, int NMAT, bool SWIGLU, int XS>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
@@ -83,40 +102,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p) {
   const bf16_t* wb[NMAT];
   wb[0] = p.W0 + (size_t)nrow * p.K + kq * 8;
   if constexpr (NMAT > 1) wb[1] = p.W1 + (size_t)nrow * p.K + kq * 8;
-  const bf16_t* xb[RT];
+  const bf16_t* xb[XS][RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    const int row = min(t * 16 + r16, p.R - 1);
-    xb[t] = p.X + (size_t)row * p.K + kq * 8;
+    const size_t off = (size_t)min(t * 16 + r16, p.R - 1) * p.K + kq * 8;
+    xb[0][t] = p.Xh + off;
+    if constexpr (XS > 1) xb[1][t] = p.Xl + off;
   }
-  f32x4 acc[NMAT][RT];
+  double acc[NMAT][RT][4];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_core<RT, NMAT>(wb, xb, c0, c1, acc);
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[m][t][e] = 0.0;
+  gemm_core<RT, NMAT, XS>(wb, xb, c0, c1, acc);
   // lane holds D[feature n0 + 4 kq + e][row t * 16 + r16]
+  const size_t plane = (size_t)p.R * p.N;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int r = t * 16 + r16;
     if (r >= p.R) continue;
     const int nf = n0 + 4 * kq;
-    if (nf + 4 > p.N) {     // ragged last group: element stores
-      for (int e = 0; e < 4 && nf + e < p.N; ++e) {
-        if constexpr (!SWIGLU) p.P[((size_t)s * p.R + r) * p.N + nf + e] = acc[0][t][e];
-        else p.Yb[(size_t)r * p.N + nf + e] = f2bf(silu(acc[0][t][e]) * acc[1][t][e]);
-      }
-      continue;
-    }
     if constexpr (!SWIGLU) {
-      float* dst = p.P + ((size_t)s * p.R + r) * p.N + n0 + 4 * kq;
-      *reinterpret_cast<f32x4*>(dst) = acc[0][t];
+      if (nf + 4 <= p.N) {
+        *reinterpret_cast<f32x4*>(p.P + ((size_t)s * p.R + r) * p.N + nf) =
+            f32x4{(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
+      } else {
+        for (int e = 0; e < 4 && nf + e < p.N; ++e) p.P[((size_t)s * p.R + r) * p.N + nf + e] = (float)acc[0][t][e];
+      }
     } else {
-      uint32_t lo = (uint32_t)f2bf(silu(acc[0][t][0]) * acc[1][t][0]) |
-                    ((uint32_t)f2bf(silu(acc[0][t][1]) * acc[1][t][1]) << 16);
-      uint32_t hi = (uint32_t)f2bf(silu(acc[0][t][2]) * acc[1][t][2]) |
-                    ((uint32_t)f2bf(silu(acc[0][t][3]) * acc[1][t][3]) << 16);
-      *reinterpret_cast<u32x2*>(p.Yb + (size_t)r * p.N + n0 + 4 * kq) = u32x2{lo, hi};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nf + e < p.N) st_planes(p.Yb + (size_t)r * p.N + nf + e, plane, swiglu(acc[0][t][e], acc[1][t][e]));
     }
   }
 }
@@ -124,19 +142,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p) {
 int launch_gemm_bf16(const GemmParams& p, int nmat, bool swiglu, hipStream_t st) {
   const int RT = (p.R + 15) / 16;
   const int waves = p.groups * p.S;
+  const bool two = p.Xl != nullptr;
   dim3 grid((waves + 3) / 4), block(256);
-#define SV_GEMM(RT_, NM_, SW_) hipLaunchKernelGGL((k_gemm_bf16<RT_, NM_, SW_>), grid, block, 0, st, p)
-#define SV_GEMM_RT(NM_, SW_)             \
-  switch (RT) {                          \
-    case 1: SV_GEMM(1, NM_, SW_); break; \
-    case 2: SV_GEMM(2, NM_, SW_); break; \
-    case 3: SV_GEMM(3, NM_, SW_); break; \
-    default: SV_GEMM(4, NM_, SW_); break; \
+#define SV_GEMM(RT_, NM_, SW_, XS_) hipLaunchKernelGGL((k_gemm_bf16<RT_, NM_, SW_, XS_>), grid, block, 0, st, p)
+#define SV_GEMM_RT(NM_, SW_, XS_)             \
+  switch (RT) {                               \
+    case 1: SV_GEMM(1, NM_, SW_, XS_); break; \
+    case 2: SV_GEMM(2, NM_, SW_, XS_); break; \
+    case 3: SV_GEMM(3, NM_, SW_, XS_); break; \
+    default: SV_GEMM(4, NM_, SW_, XS_); break; \
   }
   if (nmat == 1) {
-    SV_GEMM_RT(1, false);
+    if (two) { SV_GEMM_RT(1, false, 2); } else { SV_GEMM_RT(1, false, 1); }
   } else {
-    SV_GEMM_RT(2, true);   // two matrices only ever feed the SwiGLU epilogue
+    SV_GEMM_RT(2, true, 2);   // two matrices only ever feed the SwiGLU epilogue
   }
   (void)swiglu;
 #undef SV_GEMM_RT
@@ -145,20 +164,20 @@ int launch_gemm_bf16(const GemmParams& p, int nmat, bool swiglu, hipStream_t st)
 }
 
 // fp32 weights: a plain VALU dot product per output (fixed K order).
-__global__ void k_gemm_f32(GemmF32Params p, int swiglu) {
+__global__ void k_gemm_f32(GemmF32Params p, int use_swiglu) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x, r = blockIdx.y;
   if (n >= p.N) return;
   const float* x = p.X + (size_t)r * p.K;
   const float* w = p.W0 + (size_t)n * p.K;
-  float a = 0.f;
-  for (int k = 0; k < p.K; ++k) a = fmaf(x[k], w[k], a);
-  if (!swiglu) {
-    p.P[(size_t)r * p.N + n] = a;
+  double a = 0.0;
+  for (int k = 0; k < p.K; ++k) a += (double)x[k] * (double)w[k];
+  if (!use_swiglu) {
+    p.P[(size_t)r * p.N + n] = (float)a;
   } else {
     const float* w1 = p.W1 + (size_t)n * p.K;
-    float b = 0.f;
-    for (int k = 0; k < p.K; ++k) b = fmaf(x[k], w1[k], b);
-    p.Ya[(size_t)r * p.N + n] = silu(a) * b;
+    double b = 0.0;
+    for (int k = 0; k < p.K; ++k) b += (double)x[k] * (double)w1[k];
+    p.Ya[(size_t)r * p.N + n] = swiglu(a, b);
   }
 }
 
@@ -262,7 +281,7 @@ __device__ __forceinline__ Stat tile_stats(const float z[4], int v0, const RowMe
   return s;
 }
 
-template <int RT>
+template <int RT, int XS>
 __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
   __shared__ Stat sh[4][kMaxRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -270,17 +289,23 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
   const int tiles = p.V >> 4;
   const int tile = blockIdx.x * 4 + wave;
   const bool valid = tile < tiles;
-  f32x4 acc[1][RT];
+  double acc[1][RT][4];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[0][t][e] = 0.0;
   if (valid) {
     const bf16_t* X = reinterpret_cast<const bf16_t*>(p.X);
     const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
     const bf16_t* wb[1] = {W + (size_t)(tile * 16 + r16) * p.H + kq * 8};
-    const bf16_t* xb[RT];
+    const bf16_t* xb[XS][RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) xb[t] = X + (size_t)min(t * 16 + r16, p.R - 1) * p.H + kq * 8;
-    gemm_core<RT, 1>(wb, xb, 0, p.H >> 8, acc);
+    for (int t = 0; t < RT; ++t) {
+      const size_t off = (size_t)min(t * 16 + r16, p.R - 1) * p.H + kq * 8;
+      xb[0][t] = X + off;
+      if constexpr (XS > 1) xb[1][t] = X + (size_t)p.R * p.H + off;
+    }
+    gemm_core<RT, 1, XS>(wb, xb, 0, p.H >> 8, acc);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -290,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
       RowMeta rm;
       rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0;
       if (r < p.R) rm = row_meta(p, r);
-      const float z[4] = {acc[0][t][0], acc[0][t][1], acc[0][t][2], acc[0][t][3]};
+      const float z[4] = {(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
       s = tile_stats(z, tile * 16 + 4 * kq, rm, p);
       if (r >= p.R) s = stat_identity();
     }
@@ -316,8 +341,9 @@ __global__ void k_lmhead_f32(LmParams p) {
   Stat s = stat_identity();
   if (v < p.V) {
     const float* w = reinterpret_cast<const float*>(p.W) + (size_t)v * p.H;
-    float z = 0.f;
-    for (int k = 0; k < p.H; ++k) z = fmaf(X[k], w[k], z);
+    double zz = 0.0;
+    for (int k = 0; k < p.H; ++k) zz += (double)X[k] * (double)w[k];
+    const float z = (float)zz;
     s.m = z; s.arg = v; s.se = 1.f;
     s.zn = (rm.next_tok == v) ? z : NAN;
     if (p.sampled && rm.bonus) {
@@ -346,12 +372,13 @@ int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st) {
   if (bf16) {
     const int RT = (p.R + 15) / 16;
     dim3 grid(p.groups), block(256);
-    switch (RT) {
-      case 1: hipLaunchKernelGGL(k_lmhead_bf16<1>, grid, block, 0, st, p); break;
-      case 2: hipLaunchKernelGGL(k_lmhead_bf16<2>, grid, block, 0, st, p); break;
-      case 3: hipLaunchKernelGGL(k_lmhead_bf16<3>, grid, block, 0, st, p); break;
-      default: hipLaunchKernelGGL(k_lmhead_bf16<4>, grid, block, 0, st, p); break;
+#define SV_LM(RT_, XS_) hipLaunchKernelGGL((k_lmhead_bf16<RT_, XS_>), grid, block, 0, st, p)
+    if (p.xs == 1) {
+      switch (RT) { case 1: SV_LM(1, 1); break; case 2: SV_LM(2, 1); break; case 3: SV_LM(3, 1); break; default: SV_LM(4, 1); }
+    } else {
+      switch (RT) { case 1: SV_LM(1, 2); break; case 2: SV_LM(2, 2); break; case 3: SV_LM(3, 2); break; default: SV_LM(4, 2); }
     }
+#undef SV_LM
   } else {
     dim3 grid(p.groups, p.R), block(256);
     hipLaunchKernelGGL(k_lmhead_f32, grid, block, 0, st, p);
@@ -411,7 +438,7 @@ __device__ __forceinline__ RaceKey race_xor(RaceKey r, int x) {
   return race_merge(r, o);
 }
 
-template <int RT>
+template <int RT, int XS>
 __global__ __launch_bounds__(256, 2) void k_race_bf16(RaceParams p) {
   __shared__ RaceKey sh[4][kMaxLanes];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -423,28 +450,31 @@ __global__ __launch_bounds__(256, 2) void k_race_bf16(RaceParams p) {
   bool any = false;
   for (int l = 0; l < p.L; ++l) any |= p.dec[l].resid_row >= 0;
   if (!any) return;
-  f32x4 acc[1][RT];
+  double acc[1][RT][4];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[0][t][e] = 0.0;
   if (valid) {
     const bf16_t* X = reinterpret_cast<const bf16_t*>(p.X);
     const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
     const bf16_t* wb[1] = {W + (size_t)(tile * 16 + r16) * p.H + kq * 8};
-    const bf16_t* xb[RT];
+    const bf16_t* xb[XS][RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int l = min(t * 16 + r16, p.L - 1);
       const int row = max(p.dec[l].resid_row, 0);
-      xb[t] = X + (size_t)row * p.H + kq * 8;
+      xb[0][t] = X + (size_t)row * p.H + kq * 8;
+      if constexpr (XS > 1) xb[1][t] = X + (size_t)p.R * p.H + (size_t)row * p.H + kq * 8;
     }
-    gemm_core<RT, 1>(wb, xb, 0, p.H >> 8, acc);
+    gemm_core<RT, 1, XS>(wb, xb, 0, p.H >> 8, acc);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int l = t * 16 + r16;
     RaceKey rk = race_identity();
     if (valid && l < p.L && p.dec[l].resid_row >= 0) {
-      const float z[4] = {acc[0][t][0], acc[0][t][1], acc[0][t][2], acc[0][t][3]};
+      const float z[4] = {(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
       race_lane(z, tile * 16 + 4 * kq, p, l, rk);
     }
     rk = race_xor(rk, 16);
@@ -468,8 +498,9 @@ __global__ void k_race_f32(RaceParams p) {
   if (d.resid_row >= 0 && v < p.V) {
     const float* X = reinterpret_cast<const float*>(p.X) + (size_t)d.resid_row * p.H;
     const float* w = reinterpret_cast<const float*>(p.W) + (size_t)v * p.H;
-    float z = 0.f;
-    for (int k = 0; k < p.H; ++k) z = fmaf(X[k], w[k], z);
+    double zz = 0.0;
+    for (int k = 0; k < p.H; ++k) zz += (double)X[k] * (double)w[k];
+    const float z = (float)zz;
     const uint32_t pos = (uint32_t)(p.kv_len[l] + d.resid_col);
     uint32_t c[4] = {pos, (uint32_t)l, kPurposeRace, (uint32_t)(v >> 2)};
     philox4x32_10(c, p.key0, p.key1);
@@ -495,12 +526,13 @@ int launch_race(const RaceParams& p, bool bf16, hipStream_t st) {
   if (bf16) {
     const int RT = (p.L + 15) / 16;
     dim3 grid(p.groups), block(256);
-    switch (RT) {
-      case 1: hipLaunchKernelGGL(k_race_bf16<1>, grid, block, 0, st, p); break;
-      case 2: hipLaunchKernelGGL(k_race_bf16<2>, grid, block, 0, st, p); break;
-      case 3: hipLaunchKernelGGL(k_race_bf16<3>, grid, block, 0, st, p); break;
-      default: hipLaunchKernelGGL(k_race_bf16<4>, grid, block, 0, st, p); break;
+#define SV_RACE(RT_, XS_) hipLaunchKernelGGL((k_race_bf16<RT_, XS_>), grid, block, 0, st, p)
+    if (p.xs == 1) {
+      switch (RT) { case 1: SV_RACE(1, 1); break; case 2: SV_RACE(2, 1); break; case 3: SV_RACE(3, 1); break; default: SV_RACE(4, 1); }
+    } else {
+      switch (RT) { case 1: SV_RACE(1, 2); break; case 2: SV_RACE(2, 2); break; case 3: SV_RACE(3, 2); break; default: SV_RACE(4, 2); }
     }
+#undef SV_RACE
   } else {
     dim3 grid(p.groups, p.L), block(256);
     hipLaunchKernelGGL(k_race_f32, grid, block, 0, st, p);

@@ -19,14 +19,14 @@ int launch_attention(const AttnParams& p, bool bf16, hipStream_t st);
 int launch_attn_combine(const AttnParams& p, void* o, bool bf16, hipStream_t st);
 
 // per-row layers
-int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, float* table,
+int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, double* table,
                       hipStream_t st);
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
                       float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
                       const RowInfo& ri, bool bf16, hipStream_t st);
-int launch_qkv_post(const float* P, int S, const float* rope, int use_rope, int nq, int nkv, int d,
-                    void* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st);
+int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
+                    float* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state, int n_gdn, int gi,
                       float* stage, void* o, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg, int dg, const float* stage,
@@ -36,6 +36,7 @@ int launch_commit_kv(const int32_t* committed, const int32_t* kv_len, const int3
                      const void* sv, size_t stage_layer_elems, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_kvlen_update(const int32_t* committed, int32_t* kv_len, const RowInfo& ri, hipStream_t st);
 int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st);
+int launch_hidden_planes(const void* src, void* dst, size_t n, hipStream_t st);
 int launch_copy_rows(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // acceptance

@@ -16,37 +16,41 @@
 namespace sv {
 
 // ------------------------------------------------------------------------------- RoPE table
-// cos/sin of pos * theta^(-2i/d) for every row, evaluated in double precision.
-__global__ void k_rope_table(const int32_t* kv_len, RowInfo ri, int d, double theta, float* table) {
+// cos/sin of pos * theta^(-2i/d) for every row, in double precision.
+__global__ void k_rope_table(const int32_t* kv_len, RowInfo ri, int d, double theta, double* table) {
   const int r = blockIdx.x, i = threadIdx.x;
   if (i >= d / 2) return;
   const int l = ri.row_lane[r];
   const double pos = (double)(kv_len[l] + ri.row_col[r]);
   const double ang = pos * pow(theta, -2.0 * (double)i / (double)d);
-  table[((size_t)r * (d / 2) + i) * 2 + 0] = (float)cos(ang);
-  table[((size_t)r * (d / 2) + i) * 2 + 1] = (float)sin(ang);
+  table[((size_t)r * (d / 2) + i) * 2 + 0] = cos(ang);
+  table[((size_t)r * (d / 2) + i) * 2 + 1] = sin(ang);
 }
 
-int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, float* table,
+int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, double* table,
                       hipStream_t st) {
   hipLaunchKernelGGL(k_rope_table, dim3(ri.R), dim3(64), 0, st, kv_len, ri, d, (double)theta, table);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // ------------------------------------------------------------------------------- RMSNorm family
+// h = float32(x / sqrt(mean(x^2) + eps) * gain), evaluated in float64; a bf16
+// model stores h as its hi/lo bf16 planes (plane = R * H elements apart).
 template <typename T>
-__device__ __forceinline__ void norm_row(const float* x, int H, const float* gain, float eps, T* h, float* red) {
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
-  const float tot = block_sum(ss, red);
-  const float rs = rsqrtf(tot / (float)H + eps);
-  for (int i = threadIdx.x; i < H; i += blockDim.x) st_act(h + i, x[i] * rs * gain[i]);
+__device__ __forceinline__ void norm_row(const float* x, int H, const float* gain, float eps, T* h, size_t plane,
+                                         double* red) {
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += (double)x[i] * (double)x[i];
+  const double tot = block_sum_f64(ss, red);
+  const double scale = 1.0 / sqrt(tot / (double)H + (double)eps);
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    st_out(h, plane, i, (float)((double)x[i] * scale * (double)gain[i]));
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tokens, const T* embed, int V, int H,
-                                                     const float* gain, float eps, float* x, T* h) {
-  __shared__ float red[32];
+                                                     const float* gain, float eps, float* x, T* h, int R) {
+  __shared__ double red[32];
   const int r = blockIdx.x;
   int tok = tokens[r];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
@@ -54,17 +58,17 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tokens, const
   const T* e = embed + (size_t)tok * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = ld_act(e + i);
   __syncthreads();
-  norm_row(xr, H, gain, eps, h + (size_t)r * H, red);
+  norm_row(xr, H, gain, eps, h + (size_t)r * H, (size_t)R * H, red);
 }
 
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
                       float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
     hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(ri.R), dim3(256), 0, st, tokens,
-                       reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h));
+                       reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h), ri.R);
   else
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(ri.R), dim3(256), 0, st, tokens,
-                       reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h));
+                       reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h), ri.R);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -72,16 +76,16 @@ int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, co
 template <typename T>
 __global__ __launch_bounds__(256) void k_resid_norm(const float* P, int S, int R, float* x, int H,
                                                      const float* gain, float eps, T* h) {
-  __shared__ float red[32];
+  __shared__ double red[32];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    float t = P[(size_t)r * H + i];
+    double t = P[(size_t)r * H + i];
     for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * H + i];
-    xr[i] = xr[i] + t;
+    xr[i] = (float)((double)xr[i] + (double)(float)t);   // x + float(projection)
   }
   __syncthreads();
-  norm_row(xr, H, gain, eps, h + (size_t)r * H, red);
+  norm_row(xr, H, gain, eps, h + (size_t)r * H, (size_t)R * H, red);
 }
 
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
@@ -99,69 +103,74 @@ int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain,
 // Sum the split-K partials of [q | k | v], rotate q and k (rotate-half, pair (i, i + d/2)),
 // round to the storage type, write q and stage K/V of every column.
 template <typename T>
-__global__ __launch_bounds__(256) void k_qkv_post(const float* P, int S, int R, const float* rope, int use_rope,
-                                                   int nq, int nkv, int d, T* q, T* sk, T* sv) {
+__global__ __launch_bounds__(256) void k_qkv_post(const float* P, int S, int R, const double* rope, int use_rope,
+                                                   int nq, int nkv, int d, float* q, T* sk, T* sv) {
   const int r = blockIdx.x;
   const int N = (nq + 2 * nkv) * d, half = d / 2;
-  auto sum = [&](int n) {
-    float t = P[(size_t)r * N + n];
+  auto sum = [&](int n) {       // the projection, rounded once to float32
+    double t = P[(size_t)r * N + n];
     for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * N + n];
-    return t;
+    return (double)(float)t;
   };
   // rotated heads: q heads then k heads, processed as (head, pair) items
   const int npairs = (nq + nkv) * half;
   for (int it = threadIdx.x; it < npairs; it += blockDim.x) {
     const int hd = it / half, i = it - hd * half;
-    const float a = sum(hd * d + i), b = sum(hd * d + i + half);
-    float ra = a, rb = b;
+    const double a = sum(hd * d + i), b = sum(hd * d + i + half);
+    double ra = a, rb = b;
     if (use_rope) {
-      const float c = rope[((size_t)r * half + i) * 2], s = rope[((size_t)r * half + i) * 2 + 1];
+      const double c = rope[((size_t)r * half + i) * 2], s = rope[((size_t)r * half + i) * 2 + 1];
       ra = a * c - b * s;
       rb = b * c + a * s;
     }
-    T* dst = hd < nq ? q + ((size_t)r * nq + hd) * d : sk + ((size_t)r * nkv + (hd - nq)) * d;
-    st_act(dst + i, ra);
-    st_act(dst + i + half, rb);
+    if (hd < nq) {
+      float* dst = q + ((size_t)r * nq + hd) * d;
+      dst[i] = (float)ra;
+      dst[i + half] = (float)rb;
+    } else {
+      T* dst = sk + ((size_t)r * nkv + (hd - nq)) * d;     // staged for the bf16 cache
+      st_act(dst + i, (float)ra);
+      st_act(dst + i + half, (float)rb);
+    }
   }
   for (int it = threadIdx.x; it < nkv * d; it += blockDim.x)
-    st_act(sv + (size_t)r * nkv * d + it, sum((nq + nkv) * d + it));
+    st_act(sv + (size_t)r * nkv * d + it, (float)sum((nq + nkv) * d + it));
 }
 
-int launch_qkv_post(const float* P, int S, const float* rope, int use_rope, int nq, int nkv, int d,
-                    void* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st) {
+int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
+                    float* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
     hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
-                       reinterpret_cast<bf16_t*>(q), reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv));
+                       q, reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv));
   else
     hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
-                       reinterpret_cast<float*>(q), reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv));
+                       q, reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // ------------------------------------------------------------------------------- gated delta rule
 // State S is [dv][dk] fp32 per (lane, head); thread t owns row i = t / 2, columns
 // [64 (t % 2), 64 (t % 2) + 64).  One column step (Yang et al., Gated DeltaNet):
-//   S <- alpha S + beta (v - alpha S k) k^T.
-// Verify and commit run this exact function on the exact staged inputs, so the
-// committed state is bitwise the state verify saw at the last committed column.
+//   S <- float32(alpha S + beta (v - alpha S k) k^T), evaluated in float64,
+// so the state is stored in float32 after every column.  Verify and commit run
+// this exact function on the exact staged inputs, so the committed state is
+// bitwise the state verify saw at the last committed column.
 constexpr int kGdnDim = 128;
 
-__device__ __forceinline__ float gdn_rowdot(const float (&s)[64], const float* vec, int half) {
-#pragma clang fp contract(off)
-  float part = 0.f;
+__device__ __forceinline__ double gdn_rowdot(const float (&s)[64], const double* vec, int half) {
+  double part = 0.0;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) part = __builtin_fmaf(s[c], vec[64 * half + c], part);
-  const float other = __shfl_xor(part, 1);
+  for (int c = 0; c < 64; ++c) part += (double)s[c] * vec[64 * half + c];
+  const double other = __shfl_xor(part, 1);
   return half == 0 ? part + other : other + part;   // (low half) + (high half) on both threads
 }
 
-__device__ __forceinline__ void gdn_update(float (&s)[64], const float* kn, int half, float v_i, float alpha,
-                                           float beta) {
-#pragma clang fp contract(off)
-  const float sk = gdn_rowdot(s, kn, half);
-  const float coef = beta * (v_i - alpha * sk);
+__device__ __forceinline__ void gdn_update(float (&s)[64], const double* kn, int half, double v_i, double alpha,
+                                           double beta) {
+  const double sk = gdn_rowdot(s, kn, half);
+  const double coef = beta * (v_i - alpha * sk);
 #pragma unroll
-  for (int c = 0; c < 64; ++c) s[c] = __builtin_fmaf(alpha, s[c], coef * kn[64 * half + c]);
+  for (int c = 0; c < 64; ++c) s[c] = (float)(alpha * (double)s[c] + coef * kn[64 * half + c]);
 }
 
 // stage layout per (row, head): kn[128], v[128], alpha, beta  (kGdnStage floats)
@@ -170,7 +179,7 @@ constexpr int kGdnStage = 2 * kGdnDim + 2;
 template <typename T>
 __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowInfo ri, int hg, const float* state,
                                                      int n_gdn, int gi, float* stage, T* o) {
-  __shared__ float qn[kGdnDim], kn[kGdnDim], vv[kGdnDim], red[32], ab[2];
+  __shared__ double qn[kGdnDim], kn[kGdnDim], vv[kGdnDim], red[32], ab[2];
   const int h = blockIdx.x, l = blockIdx.y;
   const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
   const int R = ri.R;
@@ -185,34 +194,35 @@ __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowIn
   const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
   for (int j = 0; j < cols; ++j) {
     const int r = rs + j;
-    auto sum = [&](int n) {
-      float a = P[(size_t)r * N + n];
+    auto proj = [&](int n) {   // the projection, rounded once to float32
+      double a = P[(size_t)r * N + n];
       for (int ss = 1; ss < S; ++ss) a += P[((size_t)ss * R + r) * N + n];
-      return a;
+      return (double)(float)a;
     };
-    float qv = 0.f, kv = 0.f;
+    double qv = 0.0, kv = 0.0;
     if (t < kGdnDim) {
-      qv = sum(h * kGdnDim + t);
-      kv = sum(hg * kGdnDim + h * kGdnDim + t);
-      vv[t] = sum(2 * hg * kGdnDim + h * kGdnDim + t);
+      qv = proj(h * kGdnDim + t);
+      kv = proj(hg * kGdnDim + h * kGdnDim + t);
+      vv[t] = proj(2 * hg * kGdnDim + h * kGdnDim + t);
     }
     if (t == 0) {
-      ab[0] = 1.f / (1.f + expf(-sum(3 * hg * kGdnDim + h)));
-      ab[1] = 1.f / (1.f + expf(-sum(3 * hg * kGdnDim + hg + h)));
+      ab[0] = (double)(float)(1.0 / (1.0 + exp(-proj(3 * hg * kGdnDim + h))));
+      ab[1] = (double)(float)(1.0 / (1.0 + exp(-proj(3 * hg * kGdnDim + hg + h))));
     }
-    const float qq = block_sum(qv * qv, red);
-    const float kk = block_sum(kv * kv, red);
-    const float rq = rsqrtf(qq + 1e-6f) * rsqrtf((float)kGdnDim);
-    const float rk = rsqrtf(kk + 1e-6f);
-    if (t < kGdnDim) { qn[t] = qv * rq; kn[t] = kv * rk; }
+    const double qq = block_sum_f64(qv * qv, red);
+    const double kk = block_sum_f64(kv * kv, red);
+    if (t < kGdnDim) {
+      qn[t] = (double)(float)(qv / sqrt(qq + 1e-6) / sqrt((double)kGdnDim));
+      kn[t] = (double)(float)(kv / sqrt(kk + 1e-6));
+    }
     __syncthreads();
-    const float alpha = ab[0], beta = ab[1];
+    const double alpha = ab[0], beta = ab[1];
     float* stg = stage + ((size_t)r * hg + h) * kGdnStage;
-    if (t < kGdnDim) { stg[t] = kn[t]; stg[kGdnDim + t] = vv[t]; }
-    if (t == 0) { stg[2 * kGdnDim] = alpha; stg[2 * kGdnDim + 1] = beta; }
+    if (t < kGdnDim) { stg[t] = (float)kn[t]; stg[kGdnDim + t] = (float)vv[t]; }
+    if (t == 0) { stg[2 * kGdnDim] = (float)alpha; stg[2 * kGdnDim + 1] = (float)beta; }
     gdn_update(s, kn, half, vv[row_i], alpha, beta);
-    const float oi = gdn_rowdot(s, qn, half);
-    if (half == 0) st_act(o + ((size_t)r * hg + h) * kGdnDim + row_i, oi);
+    const double oi = gdn_rowdot(s, qn, half);
+    if (half == 0) st_out(o, (size_t)R * hg * kGdnDim, ((size_t)r * hg + h) * kGdnDim + row_i, (float)oi);
     __syncthreads();
   }
 }
@@ -233,7 +243,7 @@ int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state,
 // commit: replay columns 0 .. c-1 of every gated-delta-rule layer from the staged inputs
 __global__ __launch_bounds__(256) void k_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg,
                                                      const float* stage, size_t stage_layer_stride, RowInfo ri) {
-  __shared__ float kn[kGdnDim], vv[kGdnDim], ab[2];
+  __shared__ double kn[kGdnDim], vv[kGdnDim], ab[2];
   const int h = blockIdx.x, l = blockIdx.y, gi = blockIdx.z;
   const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
   const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
@@ -248,8 +258,8 @@ __global__ __launch_bounds__(256) void k_gdn_replay(const int32_t* committed, fl
   const float* stl = stage + gi * stage_layer_stride;
   for (int j = 0; j < c; ++j) {
     const float* stg = stl + ((size_t)(rs + j) * hg + h) * kGdnStage;
-    if (t < kGdnDim) { kn[t] = stg[t]; vv[t] = stg[kGdnDim + t]; }
-    if (t < 2) ab[t] = stg[2 * kGdnDim + t];
+    if (t < kGdnDim) { kn[t] = (double)stg[t]; vv[t] = (double)stg[kGdnDim + t]; }
+    if (t < 2) ab[t] = (double)stg[2 * kGdnDim + t];
     __syncthreads();
     gdn_update(s, kn, half, vv[row_i], ab[0], ab[1]);
     __syncthreads();
@@ -334,6 +344,21 @@ __global__ void k_sum_partials(const float* P, int S, size_t n, float* Y) {
 int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st) {
   const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
   hipLaunchKernelGGL(k_sum_partials, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, P, S, n, Y);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// given bf16 hidden states -> hi plane, zero lo plane
+__global__ void k_hidden_planes(const bf16_t* src, bf16_t* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    dst[i] = src[i];
+    dst[n + i] = 0;
+  }
+}
+
+int launch_hidden_planes(const void* src, void* dst, size_t n, hipStream_t st) {
+  const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+  hipLaunchKernelGGL(k_hidden_planes, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -94,13 +94,15 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
     pmax = std::max(pmax, (size_t)m->s_o_gdn.S * H);
   }
   if (d.n_layers) pmax = std::max(pmax, (size_t)m->s_down.S * H);
+  // activations are float32: an fp32 model keeps them as floats, a bf16 model as
+  // hi/lo bf16 planes [2][R][width] (the same four bytes per element)
   w.x = take((size_t)R * H * 4);
-  w.h = take((size_t)R * H * ab);
+  w.h = take((size_t)R * H * 4);
   w.P = take((size_t)R * pmax * 4);
-  w.q = take((size_t)R * qdim * ab);
-  w.o = take((size_t)R * std::max(qdim, gdim) * ab);
-  w.a = take((size_t)R * d.ffn * ab);
-  w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 4);
+  w.q = take((size_t)R * qdim * 4);
+  w.o = take((size_t)R * std::max(qdim, gdim) * 4);
+  w.a = take((size_t)R * d.ffn * 4);
+  w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 8);
   w.stage_layer_elems = (size_t)R * d.n_kv_heads * d.head_dim;
   w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
   w.stv = take((size_t)m->n_attn * w.stage_layer_elems * ab);
@@ -219,12 +221,15 @@ struct ProfScope {
   } while (0)
 
 // ---------------------------------------------------------------- projections
-int project(const spec_model* m, int cls, const void* X, const void* W0, const void* W1, int R, int N, int K,
-            int S, float* P, void* Y, hipStream_t st) {
+// X: an fp32 model's float activations [R][K]; for a bf16 model the hi plane of
+// [2][R][K] bf16 planes (two_planes) or a single exact bf16 plane.
+int project(const spec_model* m, int cls, const void* X, bool two_planes, const void* W0, const void* W1, int R,
+            int N, int K, int S, float* P, void* Y, hipStream_t st) {
   ProfScope ps(m, cls, st);
   if (m->bf16) {
     sv::GemmParams p{};
-    p.X = reinterpret_cast<const sv::bf16_t*>(X);
+    p.Xh = reinterpret_cast<const sv::bf16_t*>(X);
+    p.Xl = two_planes ? p.Xh + (size_t)R * K : nullptr;
     p.W0 = reinterpret_cast<const sv::bf16_t*>(W0);
     p.W1 = reinterpret_cast<const sv::bf16_t*>(W1);
     p.R = R; p.N = N; p.K = K; p.S = S; p.groups = (N + 15) / 16;
@@ -253,7 +258,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
   float* P = at<float>(ws, w.P);
   const size_t ab = act_bytes(m);
   const bool rope = d.rope_theta != 0.f && m->n_attn > 0;
-  if (rope) SV_CHECK(sv::launch_rope_table(r->kv_len, ri, d.head_dim, d.rope_theta, at<float>(ws, w.rope), st));
+  if (rope) SV_CHECK(sv::launch_rope_table(r->kv_len, ri, d.head_dim, d.rope_theta, at<double>(ws, w.rope), st));
   const float* g0 = d.n_layers ? m->layers[0].w.norm1 : d.final_norm;
   SV_CHECK(sv::launch_embed_norm(r->tokens, d.embed, d.vocab, H, g0, d.rms_eps, x, h, ri, bf, st));
   const size_t apool = (size_t)r->n_blocks * d.n_kv_heads * SPEC_KV_BLOCK * d.head_dim * ab;
@@ -266,11 +271,11 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       const int nq = d.n_q_heads, nkv = d.n_kv_heads, hd = d.head_dim;
       const int Nin = (nq + 2 * nkv) * hd;
       const int S_in = m->s_in_attn.S;
-      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
+      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, true, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
       void* sk = at<char>(ws, w.stk) + (size_t)L.attn_index * w.stage_layer_elems * ab;
       void* svp = at<char>(ws, w.stv) + (size_t)L.attn_index * w.stage_layer_elems * ab;
-      void* q = at<void>(ws, w.q);
-      SV_CHECK(sv::launch_qkv_post(P, S_in, at<float>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ri, bf, st));
+      float* q = at<float>(ws, w.q);
+      SV_CHECK(sv::launch_qkv_post(P, S_in, at<double>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ri, bf, st));
       sv::AttnParams ap{};
       ap.q = q; ap.sk = sk; ap.sv = svp;
       ap.kpool = reinterpret_cast<const char*>(r->k_pool) + (size_t)L.attn_index * apool;
@@ -293,7 +298,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       const int hg = d.gdn_heads, dg = d.gdn_dim;
       const int Nin = 3 * hg * dg + 2 * hg;
       const int S_in = m->s_in_gdn.S;
-      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
+      SV_CHECK(project(m, SPEC_K_PROJ_IN, h, true, L.w.w_in, nullptr, R, Nin, H, S_in, P, nullptr, st));
       float* stage = at<float>(ws, w.gst) + (size_t)L.gdn_index * w.gst_layer_floats;
       {
         ProfScope ps(m, SPEC_K_GDN, st);
@@ -303,10 +308,12 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       S_o = m->s_o_gdn.S;
       Ko = hg * dg;
     }
-    SV_CHECK(project(m, SPEC_K_PROJ_O, at<void>(ws, w.o), L.w.w_o, nullptr, R, H, Ko, S_o, P, nullptr, st));
+    SV_CHECK(project(m, SPEC_K_PROJ_O, at<void>(ws, w.o), true, L.w.w_o, nullptr, R, H, Ko, S_o, P, nullptr, st));
     SV_CHECK(sv::launch_resid_norm(P, S_o, x, H, L.w.norm2, d.rms_eps, h, ri, bf, st));
-    SV_CHECK(project(m, SPEC_K_GATE_UP, h, L.w.w_gate, L.w.w_up, R, d.ffn, H, 1, nullptr, at<void>(ws, w.a), st));
-    SV_CHECK(project(m, SPEC_K_DOWN, at<void>(ws, w.a), L.w.w_down, nullptr, R, H, d.ffn, m->s_down.S, P, nullptr, st));
+    SV_CHECK(project(m, SPEC_K_GATE_UP, h, true, L.w.w_gate, L.w.w_up, R, d.ffn, H, 1, nullptr, at<void>(ws, w.a),
+                     st));
+    SV_CHECK(project(m, SPEC_K_DOWN, at<void>(ws, w.a), true, L.w.w_down, nullptr, R, H, d.ffn, m->s_down.S, P,
+                     nullptr, st));
     SV_CHECK(sv::launch_resid_norm(P, m->s_down.S, x, H, gnext, d.rms_eps, h, ri, bf, st));
   }
   return SPEC_OK;
@@ -315,6 +322,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
 int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, hipStream_t st) {
   sv::LmParams p{};
   p.X = at<void>(r->workspace, w.h);
+  p.xs = m->d.n_layers == 0 ? 1 : 2;
   p.W = m->d.lm_head;
   p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden;
   p.groups = m->lm_groups;
@@ -448,7 +456,10 @@ int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidde
   int st = check_round(m, r, true, ri, w);
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * act_bytes(m), s));
+  if (m->bf16)
+    SV_CHECK(sv::launch_hidden_planes(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden, s));
+  else
+    SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * 4, s));
   return lm_stats(m, r, ri, w, s);
 }
 
@@ -473,8 +484,9 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
   if (sampled) {
     sv::RaceParams p{};
     p.X = at<void>(ws, w.h);
+    p.xs = m->d.n_layers == 0 ? 1 : 2;
     p.W = m->d.lm_head;
-    p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
+    p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
     p.groups = m->lm_groups;
     p.q = r->q_probs;
     p.kv_len = r->kv_len;
@@ -519,7 +531,7 @@ int spec_debug_logits(const spec_model* m, const spec_round* r, float* logits, v
   st = forward(m, r, ri, w, s);
   if (st) return st;
   // one split: the same accumulation chain as the LM-head kernel
-  return project(m, SPEC_K_NONE, at<void>(r->workspace, w.h), m->d.lm_head, nullptr, ri.R, m->d.vocab,
+  return project(m, SPEC_K_NONE, at<void>(r->workspace, w.h), true, m->d.lm_head, nullptr, ri.R, m->d.vocab,
                  m->d.hidden, 1, logits, nullptr, s)
              ? SPEC_E_HIP
              : SPEC_OK;
@@ -531,11 +543,11 @@ int spec_debug_gemm(const spec_model* m, const void* X, const void* W, float* Y,
   if (m->bf16 && (K % 256) != 0) return SPEC_E_UNSUPPORTED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int S = split_for(m, N, K, false);
-  if (S == 1) return project(m, SPEC_K_PROJ_IN, X, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
+  if (S == 1) return project(m, SPEC_K_PROJ_IN, X, false, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
   const size_t need = (size_t)S * R * N * 4;
   if (!workspace || workspace_bytes < need) return SPEC_E_WORKSPACE;
   float* P = reinterpret_cast<float*>(workspace);
-  SV_CHECK(project(m, SPEC_K_PROJ_IN, X, W, nullptr, R, N, K, S, P, nullptr, s));
+  SV_CHECK(project(m, SPEC_K_PROJ_IN, X, false, W, nullptr, R, N, K, S, P, nullptr, s));
   SV_CHECK(sv::launch_sum_partials(P, S, (size_t)R * N, Y, s));
   return SPEC_OK;
 }

@@ -158,9 +158,9 @@ def test_small_dense_bf16_round_and_commit():
 
 
 def check_committed_cache(pair, context):
-    """Committed K/V against the oracle's commit: the context rows are untouched; the first
-    attention layer's new rows are bitwise equal (its inputs are the embeddings); deeper layers
-    agree within the bf16 logit tolerance, since one rounding flip upstream moves a whole row."""
+    """Committed K/V against the oracle's commit: context rows untouched; new rows are the
+    bf16 cache values of nearly identical float32 k/v, so they agree bit for bit except for
+    rare single bf16-step rounding differences."""
     cfg = pair.cfg
     for li in range(cfg.n_attn):
         for l in range(pair.lanes):
@@ -168,10 +168,9 @@ def check_committed_cache(pair, context):
             K, V = pair.dc.get_kv(li, l, 0, n)
             ok, ov = pair.oc.gather(li, l, n)
             assert np.array_equal(K[:context], ok[:context]) and np.array_equal(V[:context], ov[:context])
-            if li == 0 and cfg.layer_kinds[0] == "attn":
-                assert np.array_equal(K, ok) and np.array_equal(V, ov)
-            for a, b in ((K, ok), (V, ov)):
-                assert np.max(np.abs(a[context:] - b[context:])) <= 3e-2 * max(1.0, np.max(np.abs(b)))
+            for a, b in ((K[context:], ok[context:]), (V[context:], ov[context:])):
+                assert np.mean(a == b) > 0.99
+                assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b))    # at most one bf16 step
 
 
 @pytest.mark.parametrize("context", [250, 1021])

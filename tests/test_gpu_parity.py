@@ -170,7 +170,9 @@ def check_committed_cache(pair, context):
             assert np.array_equal(K[:context], ok[:context]) and np.array_equal(V[:context], ov[:context])
             for a, b in ((K[context:], ok[context:]), (V[context:], ov[context:])):
                 assert np.mean(a == b) > 0.99
-                assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b))    # at most one bf16 step
+                # one bf16 step of the value, or (near zero) a small fraction of the vector's scale
+                tol = np.maximum(2.0 ** -7 * np.abs(b), 1e-4 * np.max(np.abs(b), axis=-1, keepdims=True))
+                assert np.all(np.abs(a - b) <= tol)
 
 
 @pytest.mark.parametrize("context", [250, 1021])

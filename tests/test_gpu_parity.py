@@ -159,8 +159,9 @@ def test_small_dense_bf16_round_and_commit():
 
 def check_committed_cache(pair, context):
     """Committed K/V against the oracle's commit: context rows untouched; new rows are the
-    bf16 cache values of nearly identical float32 k/v, so they agree bit for bit except for
-    rare single bf16-step rounding differences."""
+    bf16 cache values of nearly identical float32 k/v.  The projections see each float32
+    activation as two bf16 planes (2^-17 relative), so a few percent of the cache values
+    at depth round one bf16 step away from the oracle's; none differ by more."""
     cfg = pair.cfg
     for li in range(cfg.n_attn):
         for l in range(pair.lanes):
@@ -169,7 +170,7 @@ def check_committed_cache(pair, context):
             ok, ov = pair.oc.gather(li, l, n)
             assert np.array_equal(K[:context], ok[:context]) and np.array_equal(V[:context], ov[:context])
             for a, b in ((K[context:], ok[context:]), (V[context:], ov[context:])):
-                assert np.mean(a == b) > 0.99
+                assert np.mean(a == b) > 0.97
                 # one bf16 step of the value, or (near zero) a small fraction of the vector's scale
                 tol = np.maximum(2.0 ** -7 * np.abs(b), 1e-4 * np.max(np.abs(b), axis=-1, keepdims=True))
                 assert np.all(np.abs(a - b) <= tol)

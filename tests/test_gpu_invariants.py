@@ -71,7 +71,7 @@ def test_run_twice_identical(dev):
     dev.dc.verify(rc); dev.dc.accept(rc)
     s1 = dev.dc.row_stats.clone()
     dev.dc.verify(rc); dev.dc.accept(rc)
-    assert torch.equal(s1, dev.dc.row_stats)
+    assert torch.equal(s1.view(torch.int32), dev.dc.row_stats.view(torch.int32))   # bitwise (NaN z_next too)
 
 
 def test_lane_rows_independent_of_other_lanes(dev):

@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from speculative_decoding_verify_round_amd import binding as B  # noqa: E402
-from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel  # noqa: E402
+from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel, pack_weight  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "committed tokens/s & verify rows/s at lanes×(k+1); % of HBM roofline"
@@ -43,8 +43,12 @@ def log(msg):
 
 # ---------------------------------------------------------------------------- synthetic inputs on the GPU
 def gpu_weights(cfg, seed: int):
-    """Random N(0, 0.02) bf16 weights generated on the device (seeded per tensor)."""
+    """Random N(0, 0.02) bf16 weights generated on the device (seeded per tensor); every
+    matrix but the embedding table is packed into the library's fragment layout as it is made."""
     dev = torch.device("cuda")
+
+    def packed(tid, shape):
+        return pack_weight(normal(tid, shape))
 
     def normal(tid, shape, std=0.02):
         g = torch.Generator(device=dev)
@@ -58,7 +62,7 @@ def gpu_weights(cfg, seed: int):
         return out
 
     H, F = cfg.hidden, cfg.ffn
-    w = {"embed": normal(0, (cfg.vocab, H)), "lm_head": normal(1, (cfg.vocab, H)),
+    w = {"embed": normal(0, (cfg.vocab, H)), "lm_head": packed(1, (cfg.vocab, H)),
          "final_norm": torch.ones(H, device=dev), "layers": []}
     for i in range(cfg.n_layers):
         base = 100 + 16 * i
@@ -66,8 +70,8 @@ def gpu_weights(cfg, seed: int):
         n_o = cfg.n_q_heads * cfg.head_dim if cfg.layer_kinds[i] == "attn" else cfg.gdn_heads * cfg.gdn_dim
         w["layers"].append({
             "norm1": torch.ones(H, device=dev), "norm2": torch.ones(H, device=dev),
-            "w_in": normal(base, (n_in, H)), "w_o": normal(base + 1, (H, n_o)),
-            "w_gate": normal(base + 2, (F, H)), "w_up": normal(base + 3, (F, H)), "w_down": normal(base + 4, (H, F)),
+            "w_in": packed(base, (n_in, H)), "w_o": packed(base + 1, (H, n_o)),
+            "w_gate": packed(base + 2, (F, H)), "w_up": packed(base + 3, (F, H)), "w_down": packed(base + 4, (H, F)),
         })
     return w
 
@@ -101,7 +105,9 @@ def round_bytes(cfg, lanes, k, context, committed_mean):
 
 
 def gate_up_bytes(cfg, R):
-    return 2 * cfg.ffn * cfg.hidden * 2 + R * cfg.hidden * 2 + R * cfg.ffn * 2
+    """Gate and up weights once, the float32 input rows (two bf16 planes) and the float32
+    SwiGLU output rows (two bf16 planes)."""
+    return 2 * cfg.ffn * cfg.hidden * 2 + R * cfg.hidden * 4 + R * cfg.ffn * 4
 
 
 # ---------------------------------------------------------------------------- CPU baseline (oracle)
@@ -175,7 +181,7 @@ def main():
     max_blocks = (ctx + ref_len + 32) // 16 + 1
     log(f"{cfg.name}: weights on the device")
     w = gpu_weights(cfg, cfg.weight_seed)
-    dm = DeviceModel(cfg, w)
+    dm = DeviceModel(cfg, w, prepacked=True)
     del w
     bt, nb = synth.block_table(cfg, L, max_blocks)
     dc = DeviceCache(dm, L, max_blocks, nb, block_table=bt, kv_len=[ctx] * L)

@@ -80,8 +80,10 @@ enum spec_kernel_class {
   SPEC_K_COUNT = 7
 };
 
-/* Weights of one decoder layer.  Device pointers, row-major [out][in], element
+/* Weights of one decoder layer.  Device pointers to [out][in] matrices, element
  * type = the model dtype unless noted; borrowed, never freed by the library.
+ * An f32 model passes them row-major.  A bf16 model passes every matrix in the
+ * fragment layout written by spec_pack_weight (the embedding table excepted).
  *   norm1, norm2: float [hidden] RMSNorm gains.
  *   w_in:   full attention: [(n_q + 2 n_kv) * head_dim][hidden], rows = q heads,
  *           then k heads, then v heads;
@@ -118,8 +120,8 @@ typedef struct {
   float rope_theta;        /* 0 = no positional encoding */
   int kv_block;            /* must be SPEC_KV_BLOCK */
   int attn_chunk;          /* positions per split-KV chunk (multiple of 256); 0 = 1024 */
-  const void* embed;       /* [vocab][hidden]; may be NULL for a head-only model */
-  const void* lm_head;     /* [vocab][hidden] */
+  const void* embed;       /* [vocab][hidden] row-major; may be NULL for a head-only model */
+  const void* lm_head;     /* [vocab][hidden]: row-major (f32) or packed (bf16) */
   const float* final_norm; /* [hidden]; may be NULL for a head-only model */
   const spec_layer_weights* layers;   /* host [n_layers] */
 } spec_model_desc;
@@ -224,12 +226,28 @@ int spec_debug_logits(const spec_model* model, const spec_round* round, float* l
                       void* stream);
 
 /* Tests and measurement: the skinny projection kernel alone, Y[R][N] = X[R][K] W[N][K]^T
- * (X, W in the model dtype, Y float), with the split and launch shape the round
- * uses for an [N][K] weight.  X is taken as exact (one bf16 plane); inside a
- * round a bf16 model's float32 activations enter the same kernel as two planes.  R <= SPEC_MAX_ROWS.  `workspace` must hold
- * spec_workspace_bytes(model, 1, R, 1) bytes or more. */
+ * (Y float), with the split and launch shape the round uses for an [N][K]
+ * weight.  X is row-major in the model dtype and taken as exact (one bf16
+ * plane; inside a round a bf16 model's float32 activations enter the same
+ * kernel as two planes).  W: packed (bf16) or row-major (f32).
+ * R <= SPEC_MAX_ROWS; bf16 needs K % 256 == 0.  A bf16 model needs a workspace
+ * of at least 32 ceil(R / 16) K + 4 S R N bytes (S <= K / 256 the split, 256-byte
+ * aligned), else SPEC_E_WORKSPACE. */
 int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float* Y, int R,
                     int N, int K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weight fragment layout of a bf16 model.  A row-major bf16 matrix [N][K]
+ * (K % 256 == 0) is stored as 1 KB fragments of 16 rows x 32 consecutive k:
+ * fragment (g, s) (g = row tile, s = k / 32) starts at element (g * K/32 + s) * 512,
+ * and within it lane i (0..63) holds the 8 elements
+ * [16 g + i % 16][32 s + 8 (i / 16) + e], e = 0..7 -- exactly the operand one
+ * lane feeds to a 16x16x32 bf16 MFMA, so a wave loads it as 1 KB contiguous.
+ * Rows past N are zero.  spec_packed_weight_bytes returns the size
+ * (32 ceil(N / 16) K bytes) or SPEC_E_INVAL; spec_pack_weight converts
+ * device src (row-major) into device dst (distinct buffers, the caller's) on
+ * the stream. */
+int64_t spec_packed_weight_bytes(int N, int K);
+int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream);
 
 /* Measurement: record HIP events around every launch of one kernel class
  * (SPEC_K_NONE stops recording), and read back the summed duration of the

@@ -26,7 +26,8 @@ SPEC_GREEDY, SPEC_SAMPLED = 0, 1
 HEADER_SYMBOLS = (
     "spec_status_string", "spec_plan_drafts", "spec_model_create", "spec_model_destroy",
     "spec_workspace_bytes", "spec_verify_round", "spec_verify_head", "spec_accept", "spec_commit",
-    "spec_debug_logits", "spec_debug_gemm", "spec_profile_enable", "spec_profile_collect",
+    "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
+    "spec_profile_enable", "spec_profile_collect",
 )
 
 
@@ -98,6 +99,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_debug_gemm.restype = C.c_int
         lib.spec_debug_gemm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                         C.c_void_p, C.c_size_t, C.c_void_p]
+        lib.spec_packed_weight_bytes.restype = C.c_int64
+        lib.spec_packed_weight_bytes.argtypes = [C.c_int, C.c_int]
+        lib.spec_pack_weight.restype = C.c_int
+        lib.spec_pack_weight.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         lib.spec_profile_enable.restype = C.c_int
         lib.spec_profile_enable.argtypes = [C.c_void_p, C.c_int]
         lib.spec_profile_collect.restype = C.c_int
@@ -165,6 +170,15 @@ def spec_debug_gemm(model, x_ptr: int, w_ptr: int, y_ptr: int, R: int, N: int, K
                     ws_bytes: int, stream: int) -> None:
     _check(load_library().spec_debug_gemm(model, C.c_void_p(x_ptr), C.c_void_p(w_ptr), C.c_void_p(y_ptr), R, N, K,
                                           C.c_void_p(ws_ptr), ws_bytes, C.c_void_p(stream)), "spec_debug_gemm")
+
+
+def spec_packed_weight_bytes(N: int, K: int) -> int:
+    return _check(load_library().spec_packed_weight_bytes(int(N), int(K)), "spec_packed_weight_bytes")
+
+
+def spec_pack_weight(src_ptr: int, dst_ptr: int, N: int, K: int, stream: int) -> None:
+    _check(load_library().spec_pack_weight(C.c_void_p(src_ptr), C.c_void_p(dst_ptr), int(N), int(K),
+                                           C.c_void_p(stream)), "spec_pack_weight")
 
 
 def spec_profile_enable(model, kernel_class: int) -> None:

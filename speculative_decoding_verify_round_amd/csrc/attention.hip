@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
       }
     }
     const int j = m / p.G, hh = m - j * p.G;
-    st_out(o, (size_t)p.ri.R * p.nq * D, ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + dd, (float)(Oc / Lc));
+    st_out(o, act_plane(p.ri.R, p.nq * D), act_index(o, rs + j, (g * p.G + hh) * D + dd, p.nq * D), (float)(Oc / Lc));
   }
 }
 

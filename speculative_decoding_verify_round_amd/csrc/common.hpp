@@ -121,7 +121,28 @@ __device__ __forceinline__ float u01(uint32_t w) {
   return ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
 }
 
-// ----------------------------------------------------------------------------- launch parameters
+// ----------------------------------------------------------------------------- fragment layout
+// bf16 operands of the MFMA projections live in 1 KB fragments: the 16 x 32 slab
+// (16 rows x 32 consecutive k) that one operand of v_mfma_f32_16x16x32_bf16
+// covers, stored lane-major, so a wave fetches an operand with one contiguous
+// 1 KB load (16 B per lane).  Lane i of fragment (g, s) holds elements
+// [16 g + i % 16][32 s + 8 (i / 16) + e], e = 0..7; fragment (g, s) starts at
+// element (g * KS + s) * 512 with KS = K / 32.  Weights [N][K] use it with
+// g = output-feature tile (features past N zero), activations [R][K] with
+// g = row tile; an activation plane holds 16 ceil(R / 16) rows.
+__host__ __device__ __forceinline__ size_t frag_off(int row, int k, int KS) {
+  return ((size_t)((row >> 4) * KS + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+__host__ __device__ __forceinline__ int round16(int r) { return (r + 15) & ~15; }
+
+// Element (r, k) of an [R][K] activation: row-major for float32 storage,
+// fragment order for the bf16 planes.
+__device__ __forceinline__ size_t act_index(const float*, int r, int k, int K) { return (size_t)r * K + k; }
+__device__ __forceinline__ size_t act_index(const bf16_t*, int r, int k, int K) { return frag_off(r, k, K >> 5); }
+// Elements per activation plane of R rows and width K.
+__host__ __device__ __forceinline__ size_t act_plane(int R, int K) { return (size_t)round16(R) * K; }
+
+// ----------------------------------------------------------------------------- activations
 // A float32 activation x is handed to the MFMA projections as two bf16 planes,
 // hi = bf16(x) and lo = bf16(x - hi) (x = hi + lo to 2^-17 relative).
 __device__ __forceinline__ void st_planes(bf16_t* hi, size_t plane, float v) {
@@ -137,16 +158,20 @@ __device__ __forceinline__ void st_out(float* base, size_t plane, size_t i, floa
 }
 __device__ __forceinline__ void st_out(bf16_t* base, size_t plane, size_t i, float v) { st_planes(base + i, plane, v); }
 
-struct GemmParams {
-  const bf16_t* Xh;     // [R][K] activation hi plane
-  const bf16_t* Xl;     // [R][K] lo plane, or null when the activations are exact bf16
-  const bf16_t* W0;     // [N][K]
-  const bf16_t* W1;     // [N][K] second matrix (gate/up) or null
-  int R, N, K;
-  int S;                // k-splits, each a whole number of 256-wide chunks
-  int groups;           // N / 16
-  float* P;             // [S][R][N] fp32 partials
-  bf16_t* Yb;           // SwiGLU output as planes [2][R][N]
+// ----------------------------------------------------------------------------- launch parameters
+// Projection Y = X W^T over packed fragments.  K is a multiple of 256; split s
+// of S covers 256-wide units [s U / S, (s + 1) U / S), U = K / 256.
+struct ProjParams {
+  const bf16_t* W0;     // packed [N][K]
+  const bf16_t* W1;     // packed second matrix of a gate/up pair, or null
+  const bf16_t* X;      // packed activation planes (hi, then lo)
+  size_t xplane;        // elements per activation plane
+  int R, N, K, S;
+  int tiles;            // ceil(N / 16)
+  int cols;             // workgroups per split
+  float* P;             // [S][R][N] float32 partial sums
+  bf16_t* Y;            // SwiGLU output planes, packed with width N
+  size_t yplane;
 };
 
 struct GemmF32Params {
@@ -176,9 +201,10 @@ struct LmPartial {
 };
 
 struct LmParams {
-  const void* X;           // final hidden: planes [2][R][H] (bf16 model) or [R][H] float
+  const void* X;           // final hidden: packed bf16 planes (bf16 model) or [R][H] float
+  size_t xplane;           // elements per plane
   int xs;                  // bf16 planes in use (1: exact bf16 hidden states, 2: hi + lo)
-  const void* W;           // [V][H]
+  const void* W;           // packed [V][H] (bf16) or row-major [V][H] float
   int R, V, H;
   int groups;              // number of partial groups per row
   const int32_t* tokens;   // [R] round tokens (next-draft lookup)
@@ -207,9 +233,11 @@ struct LaneDecision {
 };
 
 struct RaceParams {
-  const void* X;           // planes [2][R][H] (bf16 model) or [R][H] float
+  const void* X;           // bf16: the rejected rows gathered into packed planes (lane l = row l);
+                           // float: the round's hidden rows [R][H]
+  size_t xplane;
   int xs;
-  const void* W;           // [V][H]
+  const void* W;           // packed [V][H] (bf16) or row-major [V][H] float
   int R, V, H, L;
   int groups;
   const float* q;          // [R][V]

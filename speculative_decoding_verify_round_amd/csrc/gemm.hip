@@ -1,165 +1,230 @@
 // Skinny-M projections and the fused LM head of the verify round (gfx950).
 //
 // A verify round multiplies at most 64 rows by every weight matrix of the
-// model; the pass is bound by streaming the weights from HBM once ("that pass
-// is mostly the card streaming the weights from memory", "Speculative
-// decoding", gpillon.github.io/ignis).  Each wave owns 16 output features
-// (16 rows of W, one or two matrices) over a contiguous range of 256-wide K
-// chunks and multiplies them against all rows of X with
-// v_mfma_f32_16x16x32_bf16: W is the A operand (16 features), X the B operand
-// (16 rows per tile, up to four tiles).  Weights are loaded with non-temporal
-// 16-byte loads into an eight-step register ring, so eight MFMA steps of W
-// (and of X, issued at the same distance so the in-order vmcnt counter never
-// makes a step wait on a younger load) are in flight per wave.
+// model, so the pass is bound by streaming the weights from HBM once ("that
+// pass is mostly the card streaming the weights from memory", "Speculative
+// decoding", gpillon.github.io/ignis).  Both operands are stored as 1 KB MFMA
+// fragments (frag_off), so every wave load is one contiguous 1 KB.
 //
-// The K split of a matrix is a function of its shape only, and every output
-// element is one MFMA accumulation chain in a fixed K order, so a row's result
-// never depends on how many rows the round carries.
+// Workgroup = 4 waves on T consecutive 16-feature tiles each, all on the same
+// K split.  The activation rows (B operand, up to four 16-row tiles, one or
+// two bf16 planes) are staged chunk by chunk into a double-buffered LDS ring
+// that the four waves share; the weights (A operand) stream through an
+// eight-step register ring with non-temporal loads.  The X chunk for the next
+// step range is fetched at the start of a chunk and written to LDS at its end,
+// so every global load -- weights and activations alike -- has a whole chunk
+// of MFMA steps to arrive (the in-order vmcnt counter never makes a step wait
+// for a younger load).
+//
+// Numerics: each output element is one fp32 MFMA accumulation chain over its
+// split in a fixed K order (per step the lo plane, then the hi plane); K
+// splits depend on the matrix shape only and partials are summed in order by
+// the consumer, so a row's result never depends on how many rows the round
+// carries.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
-constexpr int kSteps = 8;   // MFMA k-steps (32 each) per 256-wide chunk
-constexpr int kRingW = 8;   // k-steps of W in flight per wave
-constexpr int kRingX = 2;   // k-steps of X in flight per wave (L1/L2 hits)
+constexpr int kUnit = 8;   // MFMA k-steps (32 each) per 256-wide unit; splits are whole units
 
-// acc[m][t][e] += W_m[16 features][k] . X[16 rows of tile t][k] over k-chunks [c0, c1).
-// X arrives as XS bf16 planes (hi, lo); each k-step chains the planes' MFMAs
-// (lo first) from a zero accumulator, and the step's fp32 result is added to a
-// float64 accumulator, so the K sum carries about one fp32 ulp of error.
-// Loads are issued X(step + 2) before W(step + 8) so that waiting for an X
-// step never waits for the younger W loads behind it (vmcnt counts in order).
-template <int RT, int NMAT, int XS>
-__device__ __forceinline__ void gemm_core(const bf16_t* const (&wb)[NMAT], const bf16_t* const (&xb)[XS][RT],
-                                          int c0, int c1, double (&acc)[NMAT][RT][4]) {
-  if (c0 >= c1) return;
-  const int s0 = c0 * kSteps, ns = (c1 - c0) * kSteps;   // a multiple of kRingW
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  u32x4 wr[kRingW][NMAT];
-  u32x4 xr[kRingX][XS][RT];
-  auto loadW = [&](int slot, int st) {
-    const int k = (s0 + st) * 32;
+template <int RT, int T, int XS, int KC>
+struct CoreShape {
+  static constexpr int NC = kUnit / KC;      // X chunks per unit
+  static constexpr int NB = KC * RT * XS;    // 1 KB X fragments per chunk
+  static constexpr int NBW = NB / 4;         // staged per wave
+};
+
+// acc[j][t] += W tile j (16 features) . X row tile t over the unit range
+// [step0 / 8, step0 / 8 + nu).  wp[j] points at tile j's fragment of step
+// step0, lane offset included.  xl: LDS ring [2][NB][64] u32x4.  Every wave of
+// the workgroup must call this with the same step0 and nu.
+template <int RT, int T, int XS, int KC>
+__device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], const bf16_t* __restrict__ X,
+                                          size_t xplane, int KS, int step0, int nu, u32x4* xl,
+                                          f32x4 (&acc)[T][RT]) {
+  using C = CoreShape<RT, T, XS, KC>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // this wave's share of an X chunk: fragment b = (plane * RT + tile) * KC + step
+  uint32_t xoff[C::NBW];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) wr[slot][m] = ld_stream(reinterpret_cast<const u32x4*>(wb[m] + k));
+  for (int i = 0; i < C::NBW; ++i) {
+    const int b = wave * C::NBW + i;
+    const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
+    xoff[i] = (uint32_t)(pl * xplane + ((size_t)t * KS + st) * 512 + lane * 8);
+  }
+  u32x4 sx[C::NBW];
+  auto stage_load = [&](int stepc) {
+#pragma unroll
+    for (int i = 0; i < C::NBW; ++i)
+      sx[i] = *reinterpret_cast<const u32x4*>(X + xoff[i] + (size_t)stepc * 512);
   };
-  auto loadX = [&](int slot, int st) {
-    const int k = (s0 + st) * 32;
+  auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int x = 0; x < XS; ++x)
-#pragma unroll
-      for (int t = 0; t < RT; ++t) xr[slot][x][t] = *reinterpret_cast<const u32x4*>(xb[x][t] + k);
+    for (int i = 0; i < C::NBW; ++i) xl[((size_t)buf * C::NB + wave * C::NBW + i) * 64 + lane] = sx[i];
   };
-  auto step = [&](int ws, int xsl) {
+  u32x4 wr[kUnit][T];
+  stage_load(step0);
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+  for (int k = 0; k < kUnit; ++k)
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        f32x4 d = zero;
+    for (int j = 0; j < T; ++j) wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)k * 512));
+  stage_store(0);
+  __syncthreads();
+  int cb = 0;
+  auto run_unit = [&](auto more_tag, int u) {
+    constexpr bool MORE = decltype(more_tag)::value;
 #pragma unroll
-        for (int x = XS - 1; x >= 0; --x) d = mfma_bf16(wr[ws][m], xr[xsl][x][t], d);
+    for (int h = 0; h < C::NC; ++h) {
+      const bool next = (h + 1 < C::NC) || MORE;
+      if (next) stage_load(step0 + u * kUnit + (h + 1) * KC);
+      // keep the issue order as written: the scheduler would otherwise sink the
+      // prefetches next to their first use and expose the full memory latency
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[m][t][e] += (double)d[e];
+      for (int st = 0; st < KC; ++st) {
+        const int k = h * KC + st;
+        u32x4 xo[XS][RT];
+#pragma unroll
+        for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+          for (int t = 0; t < RT; ++t) xo[pl][t] = xl[((size_t)cb * C::NB + (pl * RT + t) * KC + st) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int pl = XS - 1; pl >= 0; --pl) acc[j][t] = mfma_bf16(wr[k][j], xo[pl][t], acc[j][t]);
+        if constexpr (MORE) {
+#pragma unroll
+          for (int j = 0; j < T; ++j)
+            wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)((u + 1) * kUnit + k) * 512));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-  };
-#pragma unroll
-  for (int u = 0; u < kRingX; ++u) loadX(u, u);
-#pragma unroll
-  for (int u = 0; u < kRingW; ++u) loadW(u, u);
-  for (int i = 0; i < ns - kRingW; i += kRingW) {
-#pragma unroll
-    for (int u = 0; u < kRingW; ++u) {
-      step(u, u % kRingX);
-      loadX(u % kRingX, i + u + kRingX);
-      loadW(u, i + u + kRingW);
+      if (next) stage_store(cb ^ 1);
+      __syncthreads();
+      cb ^= 1;
     }
-  }
-#pragma unroll
-  for (int u = 0; u < kRingW; ++u) {
-    step(u, u % kRingX);
-    if (u + kRingX < kRingW) loadX(u % kRingX, ns - kRingW + u + kRingX);
-  }
+  };
+  for (int u = 0; u + 1 < nu; ++u) run_unit(std::true_type{}, u);
+  run_unit(std::false_type{}, nu - 1);
 }
 
-// float(silu(g) * u) evaluated in float64 from the fp32-rounded projections
-__device__ __forceinline__ float swiglu(double g64, double u64) {
-  const double g = (double)(float)g64, u = (double)(float)u64;
+template <int RT>
+constexpr int chunk_steps() { return RT <= 2 ? 8 : 4; }
+
+// float(silu(g) * u) evaluated in float64 from the fp32 projections
+__device__ __forceinline__ float swiglu(float g32, float u32) {
+  const double g = (double)g32, u = (double)u32;
   return (float)(g / (1.0 + exp(-g)) * u);
 }
 
 // ------------------------------------------------------------------------------- projection
-template <int RT, int NMAT, bool SWIGLU, int XS>
-__global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p) {
+// EPI 0: write split partials P[s][r][n].  EPI 1: gate/up pair (T = 2: the
+// gate and the up tile of the same 16 features, one split), write
+// float(silu(gate) * up) as packed hi/lo planes of width N.
+template <int RT, int T, int XS, int EPI>
+__global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
+  constexpr int KC = chunk_steps<RT>();
+  using C = CoreShape<RT, T, XS, KC>;
+  __shared__ u32x4 xl[2 * C::NB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + wave;
-  if (gw >= p.groups * p.S) return;
-  const int g = gw % p.groups, s = gw / p.groups;
-  const int C = p.K >> 8;
-  const int c0 = (int)((long long)s * C / p.S), c1 = (int)((long long)(s + 1) * C / p.S);
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = g * 16;
-  const int nrow = min(n0 + r16, p.N - 1);   // features past N read a valid row; never stored
-  const bf16_t* wb[NMAT];
-  wb[0] = p.W0 + (size_t)nrow * p.K + kq * 8;
-  if constexpr (NMAT > 1) wb[1] = p.W1 + (size_t)nrow * p.K + kq * 8;
-  const bf16_t* xb[XS][RT];
+  const int col = blockIdx.x % p.cols, s = blockIdx.x / p.cols;
+  const int KS = p.K >> 5, U = p.K >> 8;
+  const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
+  const int blk = col * 4 + wave;
+  int tile[T];
+  const bf16_t* wp[T];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const size_t off = (size_t)min(t * 16 + r16, p.R - 1) * p.K + kq * 8;
-    xb[0][t] = p.Xh + off;
-    if constexpr (XS > 1) xb[1][t] = p.Xl + off;
+  for (int j = 0; j < T; ++j) {
+    tile[j] = EPI == 1 ? blk : blk * T + j;
+    const int tc = min(tile[j], p.tiles - 1);   // past the last tile: re-read a valid one, never stored
+    const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
+    wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
   }
-  double acc[NMAT][RT][4];
+  f32x4 acc[T][RT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int j = 0; j < T; ++j)
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  proj_core<RT, T, XS, KC>(wp, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
+  // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
+  const int r16 = lane & 15, kq = lane >> 4;
+  if constexpr (EPI == 0) {
+    const bool vec = (p.N & 3) == 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[m][t][e] = 0.0;
-  gemm_core<RT, NMAT, XS>(wb, xb, c0, c1, acc);
-  // lane holds D[feature n0 + 4 kq + e][row t * 16 + r16]
-  const size_t plane = (size_t)p.R * p.N;
+    for (int j = 0; j < T; ++j) {
+      if (tile[j] >= p.tiles) continue;
+      const int nf = tile[j] * 16 + 4 * kq;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int r = t * 16 + r16;
-    if (r >= p.R) continue;
-    const int nf = n0 + 4 * kq;
-    if constexpr (!SWIGLU) {
-      if (nf + 4 <= p.N) {
-        *reinterpret_cast<f32x4*>(p.P + ((size_t)s * p.R + r) * p.N + nf) =
-            f32x4{(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
-      } else {
-        for (int e = 0; e < 4 && nf + e < p.N; ++e) p.P[((size_t)s * p.R + r) * p.N + nf + e] = (float)acc[0][t][e];
+      for (int t = 0; t < RT; ++t) {
+        const int r = t * 16 + r16;
+        if (r >= p.R) continue;
+        float* dst = p.P + ((size_t)s * p.R + r) * p.N + nf;
+        if (vec && nf + 4 <= p.N) {
+          *reinterpret_cast<f32x4*>(dst) = acc[j][t];
+        } else {
+          for (int e = 0; e < 4 && nf + e < p.N; ++e) dst[e] = acc[j][t][e];
+        }
       }
-    } else {
+    }
+  } else {
+    if (tile[0] >= p.tiles) return;
+    const int nf = tile[0] * 16 + 4 * kq;
+    const int KSy = p.N >> 5;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (nf + e < p.N) st_planes(p.Yb + (size_t)r * p.N + nf + e, plane, swiglu(acc[0][t][e], acc[1][t][e]));
+    for (int t = 0; t < RT; ++t) {
+      const int r = t * 16 + r16;
+      if (r >= p.R) continue;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float a0 = swiglu(acc[0][t][e], acc[1][t][e]), a1 = swiglu(acc[0][t][e + 1], acc[1][t][e + 1]);
+        const bf16_t h0 = f2bf(a0), h1 = f2bf(a1);
+        const bf16_t l0 = f2bf(a0 - bf2f(h0)), l1 = f2bf(a1 - bf2f(h1));
+        hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      if (nf + 4 <= p.N) {   // four consecutive k of one row: 8 contiguous bytes per plane
+        const size_t o = frag_off(r, nf, KSy);
+        *reinterpret_cast<u32x2*>(p.Y + o) = u32x2{hi[0], hi[1]};
+        *reinterpret_cast<u32x2*>(p.Y + p.yplane + o) = u32x2{lo[0], lo[1]};
+      }
     }
   }
 }
 
-int launch_gemm_bf16(const GemmParams& p, int nmat, bool swiglu, hipStream_t st) {
+// Feature tiles per wave: two once the activation tiles make LDS reads dominate.
+int proj_tiles_per_wave(int R) { return R > 32 ? 2 : 1; }
+
+int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
+  ProjParams p = p0;
   const int RT = (p.R + 15) / 16;
-  const int waves = p.groups * p.S;
-  const bool two = p.Xl != nullptr;
-  dim3 grid((waves + 3) / 4), block(256);
-#define SV_GEMM(RT_, NM_, SW_, XS_) hipLaunchKernelGGL((k_gemm_bf16<RT_, NM_, SW_, XS_>), grid, block, 0, st, p)
-#define SV_GEMM_RT(NM_, SW_, XS_)             \
-  switch (RT) {                               \
-    case 1: SV_GEMM(1, NM_, SW_, XS_); break; \
-    case 2: SV_GEMM(2, NM_, SW_, XS_); break; \
-    case 3: SV_GEMM(3, NM_, SW_, XS_); break; \
-    default: SV_GEMM(4, NM_, SW_, XS_); break; \
+  const int T = swiglu ? 2 : proj_tiles_per_wave(p.R);
+  const int blocks = swiglu ? p.tiles : (p.tiles + T - 1) / T;
+  p.cols = (blocks + 3) / 4;
+  dim3 grid(p.cols * p.S), block(256);
+#define SV_P(RT_, T_, XS_, E_) hipLaunchKernelGGL((k_proj<RT_, T_, XS_, E_>), grid, block, 0, st, p)
+#define SV_P_RT(T_, XS_, E_)             \
+  switch (RT) {                          \
+    case 1: SV_P(1, T_, XS_, E_); break; \
+    case 2: SV_P(2, T_, XS_, E_); break; \
+    case 3: SV_P(3, T_, XS_, E_); break; \
+    default: SV_P(4, T_, XS_, E_); break; \
   }
-  if (nmat == 1) {
-    if (two) { SV_GEMM_RT(1, false, 2); } else { SV_GEMM_RT(1, false, 1); }
+  if (swiglu) {
+    SV_P_RT(2, 2, 1);
+  } else if (xs == 2) {
+    if (T == 2) { SV_P_RT(2, 2, 0); } else { SV_P_RT(1, 2, 0); }
   } else {
-    SV_GEMM_RT(2, true, 2);   // two matrices only ever feed the SwiGLU epilogue
+    if (T == 2) { SV_P_RT(2, 1, 0); } else { SV_P_RT(1, 1, 0); }
   }
-  (void)swiglu;
-#undef SV_GEMM_RT
-#undef SV_GEMM
+#undef SV_P_RT
+#undef SV_P
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -177,13 +242,57 @@ __global__ void k_gemm_f32(GemmF32Params p, int use_swiglu) {
     const float* w1 = p.W1 + (size_t)n * p.K;
     double b = 0.0;
     for (int k = 0; k < p.K; ++k) b += (double)x[k] * (double)w1[k];
-    p.Ya[(size_t)r * p.N + n] = swiglu(a, b);
+    p.Ya[(size_t)r * p.N + n] = swiglu((float)a, (float)b);
   }
 }
 
 int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st) {
   dim3 grid((p.N + 255) / 256, p.R), block(256);
   hipLaunchKernelGGL(k_gemm_f32, grid, block, 0, st, p, swiglu ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------------------- packing
+// Row-major bf16 [N][K] -> fragment order; features past N are zero.
+__global__ void k_pack_weight(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int N, int K) {
+  const int KS = K >> 5;
+  const size_t n16 = (size_t)((N + 15) >> 4) * KS * 64;   // 16-byte lane slots
+  for (size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x; q < n16; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q & 63);
+    const size_t f = q >> 6;
+    const int g = (int)(f / KS), s = (int)(f - (size_t)g * KS);
+    const int row = g * 16 + (lane & 15), k = s * 32 + 8 * (lane >> 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < N) v = *reinterpret_cast<const u32x4*>(src + (size_t)row * K + k);
+    *reinterpret_cast<u32x4*>(dst + q * 8) = v;
+  }
+}
+
+int launch_pack_weight(const void* src, void* dst, int N, int K, hipStream_t st) {
+  const size_t n16 = (size_t)((N + 15) >> 4) * (K >> 5) * 64;
+  const int blocks = (int)std::min<size_t>((n16 + 255) / 256, 16384);
+  hipLaunchKernelGGL(k_pack_weight, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), N, K);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Row-major bf16 rows [R][K] -> packed planes: hi = the rows, lo = 0 when xs == 2.
+__global__ void k_pack_rows(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int R, int K, size_t plane,
+                            int xs) {
+  const size_t n = (size_t)R * K;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / K), k = (int)(i - (size_t)r * K);
+    const size_t o = frag_off(r, k, K >> 5);
+    dst[o] = src[i];
+    if (xs == 2) dst[plane + o] = 0;
+  }
+}
+
+int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, hipStream_t st) {
+  const size_t n = (size_t)R * K;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_pack_rows, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), R, K, plane, xs);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -283,49 +392,49 @@ __device__ __forceinline__ Stat tile_stats(const float z[4], int v0, const RowMe
 
 template <int RT, int XS>
 __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
-  __shared__ Stat sh[4][kMaxRows];
+  constexpr int KC = chunk_steps<RT>(), T = 2;
+  using C = CoreShape<RT, T, XS, KC>;
+  static_assert(2 * C::NB * 64 * sizeof(u32x4) >= 4 * kMaxRows * sizeof(Stat), "stats fit the X ring");
+  __shared__ u32x4 xl[2 * C::NB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int tiles = p.V >> 4;
-  const int tile = blockIdx.x * 4 + wave;
-  const bool valid = tile < tiles;
-  double acc[1][RT][4];
+  const int tiles = p.V >> 4, KS = p.H >> 5;
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+  int tile[T];
+  const bf16_t* wp[T];
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[0][t][e] = 0.0;
-  if (valid) {
-    const bf16_t* X = reinterpret_cast<const bf16_t*>(p.X);
-    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
-    const bf16_t* wb[1] = {W + (size_t)(tile * 16 + r16) * p.H + kq * 8};
-    const bf16_t* xb[XS][RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const size_t off = (size_t)min(t * 16 + r16, p.R - 1) * p.H + kq * 8;
-      xb[0][t] = X + off;
-      if constexpr (XS > 1) xb[1][t] = X + (size_t)p.R * p.H + off;
-    }
-    gemm_core<RT, 1, XS>(wb, xb, 0, p.H >> 8, acc);
+  for (int j = 0; j < T; ++j) {
+    tile[j] = (blockIdx.x * 4 + wave) * T + j;
+    wp[j] = W + (size_t)min(tile[j], tiles - 1) * KS * 512 + lane * 8;
   }
+  f32x4 acc[T][RT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  proj_core<RT, T, XS, KC>(wp, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
+  Stat* sh = reinterpret_cast<Stat*>(xl);   // the core ends on a barrier: the ring is free
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int r = t * 16 + r16;
+    RowMeta rm;
+    rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0;
+    if (r < p.R) rm = row_meta(p, r);
     Stat s = stat_identity();
-    if (valid) {   // wave-uniform; every lane joins tile_stats' cross-lane shuffles
-      RowMeta rm;
-      rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0;
-      if (r < p.R) rm = row_meta(p, r);
-      const float z[4] = {(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
-      s = tile_stats(z, tile * 16 + 4 * kq, rm, p);
-      if (r >= p.R) s = stat_identity();
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      if (tile[j] < tiles) {   // wave-uniform; every lane joins tile_stats' cross-lane shuffles
+        const float z[4] = {acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]};
+        s = stat_merge(s, tile_stats(z, tile[j] * 16 + 4 * kq, rm, p), p.inv_t);
+      }
     }
-    if (kq == 0 && r < p.R) sh[wave][r] = s;
+    if (kq == 0 && r < p.R) sh[wave * kMaxRows + r] = s;
   }
   __syncthreads();
   for (int r = threadIdx.x; r < p.R; r += blockDim.x) {
-    Stat s = sh[0][r];
+    Stat s = sh[r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s = stat_merge(s, sh[w][r], p.inv_t);
+    for (int w = 1; w < 4; ++w) s = stat_merge(s, sh[w * kMaxRows + r], p.inv_t);
     LmPartial o;
     o.m = s.m; o.se = s.se; o.arg = s.arg; o.zn = s.zn; o.gk = s.gk; o.gi = s.gi; o.pad0 = o.pad1 = 0;
     p.part[(size_t)r * p.groups + blockIdx.x] = o;
@@ -386,7 +495,8 @@ int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int lmhead_groups(int V, bool bf16) { return bf16 ? ((V >> 4) + 3) / 4 : (V + 255) / 256; }
+// bf16: one workgroup per 8 token tiles (4 waves x 2 tiles)
+int lmhead_groups(int V, bool bf16) { return bf16 ? ((V >> 4) + 7) / 8 : (V + 255) / 256; }
 
 // ------------------------------------------------------------------------------- residual race
 // Sampled mode, lanes whose draft i was rejected: recompute the logits of the
@@ -440,51 +550,52 @@ __device__ __forceinline__ RaceKey race_xor(RaceKey r, int x) {
 
 template <int RT, int XS>
 __global__ __launch_bounds__(256, 2) void k_race_bf16(RaceParams p) {
-  __shared__ RaceKey sh[4][kMaxLanes];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int tiles = p.V >> 4;
-  const int tile = blockIdx.x * 4 + wave;
-  const bool valid = tile < tiles;
-  // any lane with a rejection?  (uniform across the workgroup)
+  constexpr int KC = chunk_steps<RT>(), T = 2;
+  using C = CoreShape<RT, T, XS, KC>;
+  static_assert(2 * C::NB * 64 * sizeof(u32x4) >= 4 * kMaxLanes * sizeof(RaceKey), "keys fit the X ring");
+  __shared__ u32x4 xl[2 * C::NB * 64];
+  // any lane with a rejection?  (uniform across the grid)
   bool any = false;
   for (int l = 0; l < p.L; ++l) any |= p.dec[l].resid_row >= 0;
   if (!any) return;
-  double acc[1][RT][4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tiles = p.V >> 4, KS = p.H >> 5;
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+  int tile[T];
+  const bf16_t* wp[T];
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[0][t][e] = 0.0;
-  if (valid) {
-    const bf16_t* X = reinterpret_cast<const bf16_t*>(p.X);
-    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
-    const bf16_t* wb[1] = {W + (size_t)(tile * 16 + r16) * p.H + kq * 8};
-    const bf16_t* xb[XS][RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int l = min(t * 16 + r16, p.L - 1);
-      const int row = max(p.dec[l].resid_row, 0);
-      xb[0][t] = X + (size_t)row * p.H + kq * 8;
-      if constexpr (XS > 1) xb[1][t] = X + (size_t)p.R * p.H + (size_t)row * p.H + kq * 8;
-    }
-    gemm_core<RT, 1, XS>(wb, xb, 0, p.H >> 8, acc);
+  for (int j = 0; j < T; ++j) {
+    tile[j] = (blockIdx.x * 4 + wave) * T + j;
+    wp[j] = W + (size_t)min(tile[j], tiles - 1) * KS * 512 + lane * 8;
   }
+  f32x4 acc[T][RT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // X: the rejected rows gathered lane by lane (row tile t holds lanes 16 t ..)
+  proj_core<RT, T, XS, KC>(wp, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
+  RaceKey* sh = reinterpret_cast<RaceKey*>(xl);
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int l = t * 16 + r16;
     RaceKey rk = race_identity();
-    if (valid && l < p.L && p.dec[l].resid_row >= 0) {
-      const float z[4] = {(float)acc[0][t][0], (float)acc[0][t][1], (float)acc[0][t][2], (float)acc[0][t][3]};
-      race_lane(z, tile * 16 + 4 * kq, p, l, rk);
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      if (tile[j] < tiles && l < p.L && p.dec[l].resid_row >= 0) {
+        const float z[4] = {acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]};
+        race_lane(z, tile[j] * 16 + 4 * kq, p, l, rk);
+      }
     }
     rk = race_xor(rk, 16);
     rk = race_xor(rk, 32);
-    if (kq == 0 && l < p.L) sh[wave][l] = rk;
+    if (kq == 0 && l < p.L) sh[wave * kMaxLanes + l] = rk;
   }
   __syncthreads();
   for (int l = threadIdx.x; l < p.L; l += blockDim.x) {
-    RaceKey r = sh[0][l];
-    for (int w = 1; w < 4; ++w) r = race_merge(r, sh[w][l]);
+    RaceKey r = sh[l];
+    for (int w = 1; w < 4; ++w) r = race_merge(r, sh[w * kMaxLanes + l]);
     float* o = p.part + ((size_t)l * p.groups + blockIdx.x) * 4;
     o[0] = r.k; o[1] = __int_as_float(r.i); o[2] = r.fk; o[3] = __int_as_float(r.fi);
   }
@@ -537,6 +648,31 @@ int launch_race(const RaceParams& p, bool bf16, hipStream_t st) {
     dim3 grid(p.groups, p.L), block(256);
     hipLaunchKernelGGL(k_race_f32, grid, block, 0, st, p);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Sampled residual: the rejected row of every lane, gathered into packed planes
+// (lane l -> row l); lanes without a rejection copy row 0 (their keys are discarded).
+__global__ void k_gather_rows(const bf16_t* __restrict__ src, size_t src_plane, bf16_t* __restrict__ dst,
+                              size_t dst_plane, const LaneDecision* dec, int L, int H, int xs) {
+  const int KS = H >> 5;
+  const size_t n = (size_t)L * H;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i / H), k = (int)(i - (size_t)l * H);
+    const int row = max(dec[l].resid_row, 0);
+    const size_t so = frag_off(row, k, KS), d = frag_off(l, k, KS);
+    dst[d] = src[so];
+    if (xs == 2) dst[dst_plane + d] = src[src_plane + so];
+  }
+}
+
+int launch_gather_rows(const void* src, size_t src_plane, void* dst, size_t dst_plane, const LaneDecision* dec,
+                       int L, int H, int xs, hipStream_t st) {
+  const size_t n = (size_t)L * H;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(k_gather_rows, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(src), src_plane, reinterpret_cast<bf16_t*>(dst), dst_plane, dec,
+                     L, H, xs);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

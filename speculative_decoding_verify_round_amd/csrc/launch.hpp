@@ -6,13 +6,20 @@
 namespace sv {
 
 // projections
-int launch_gemm_bf16(const GemmParams& p, int nmat, bool swiglu, hipStream_t st);
+int launch_proj(const ProjParams& p, bool swiglu, int xs, hipStream_t st);
+int proj_tiles_per_wave(int R);
 int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st);
 
 // LM head statistics and the residual race
 int lmhead_groups(int V, bool bf16);
 int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st);
 int launch_race(const RaceParams& p, bool bf16, hipStream_t st);
+int launch_gather_rows(const void* src, size_t src_plane, void* dst, size_t dst_plane, const LaneDecision* dec,
+                       int L, int H, int xs, hipStream_t st);
+
+// fragment packing
+int launch_pack_weight(const void* src, void* dst, int N, int K, hipStream_t st);
+int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, hipStream_t st);
 
 // attention
 int launch_attention(const AttnParams& p, bool bf16, hipStream_t st);
@@ -36,7 +43,6 @@ int launch_commit_kv(const int32_t* committed, const int32_t* kv_len, const int3
                      const void* sv, size_t stage_layer_elems, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_kvlen_update(const int32_t* committed, int32_t* kv_len, const RowInfo& ri, hipStream_t st);
 int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st);
-int launch_hidden_planes(const void* src, void* dst, size_t n, hipStream_t st);
 int launch_copy_rows(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // acceptance

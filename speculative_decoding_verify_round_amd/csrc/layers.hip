@@ -35,16 +35,16 @@ int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float the
 
 // ------------------------------------------------------------------------------- RMSNorm family
 // h = float32(x / sqrt(mean(x^2) + eps) * gain), evaluated in float64; a bf16
-// model stores h as its hi/lo bf16 planes (plane = R * H elements apart).
+// model stores h as its hi/lo bf16 planes in fragment order.
 template <typename T>
-__device__ __forceinline__ void norm_row(const float* x, int H, const float* gain, float eps, T* h, size_t plane,
-                                         double* red) {
+__device__ __forceinline__ void norm_row(const float* x, int r, int H, const float* gain, float eps, T* h,
+                                         size_t plane, double* red) {
   double ss = 0.0;
   for (int i = threadIdx.x; i < H; i += blockDim.x) ss += (double)x[i] * (double)x[i];
   const double tot = block_sum_f64(ss, red);
   const double scale = 1.0 / sqrt(tot / (double)H + (double)eps);
   for (int i = threadIdx.x; i < H; i += blockDim.x)
-    st_out(h, plane, i, (float)((double)x[i] * scale * (double)gain[i]));
+    st_out(h, plane, act_index(h, r, i, H), (float)((double)x[i] * scale * (double)gain[i]));
 }
 
 template <typename T>
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tokens, const
   const T* e = embed + (size_t)tok * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = ld_act(e + i);
   __syncthreads();
-  norm_row(xr, H, gain, eps, h + (size_t)r * H, (size_t)R * H, red);
+  norm_row(xr, r, H, gain, eps, h, act_plane(R, H), red);
 }
 
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_resid_norm(const float* P, int S, int R
     xr[i] = (float)((double)xr[i] + (double)(float)t);   // x + float(projection)
   }
   __syncthreads();
-  norm_row(xr, H, gain, eps, h + (size_t)r * H, (size_t)R * H, red);
+  norm_row(xr, r, H, gain, eps, h, act_plane(R, H), red);
 }
 
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowIn
     if (t == 0) { stg[2 * kGdnDim] = (float)alpha; stg[2 * kGdnDim + 1] = (float)beta; }
     gdn_update(s, kn, half, vv[row_i], alpha, beta);
     const double oi = gdn_rowdot(s, qn, half);
-    if (half == 0) st_out(o, (size_t)R * hg * kGdnDim, ((size_t)r * hg + h) * kGdnDim + row_i, (float)oi);
+    if (half == 0) st_out(o, act_plane(R, hg * kGdnDim), act_index(o, r, h * kGdnDim + row_i, hg * kGdnDim), (float)oi);
     __syncthreads();
   }
 }
@@ -344,21 +344,6 @@ __global__ void k_sum_partials(const float* P, int S, size_t n, float* Y) {
 int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st) {
   const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
   hipLaunchKernelGGL(k_sum_partials, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, P, S, n, Y);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// given bf16 hidden states -> hi plane, zero lo plane
-__global__ void k_hidden_planes(const bf16_t* src, bf16_t* dst, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    dst[i] = src[i];
-    dst[n + i] = 0;
-  }
-}
-
-int launch_hidden_planes(const void* src, void* dst, size_t n, hipStream_t st) {
-  const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
-  hipLaunchKernelGGL(k_hidden_planes, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -56,18 +56,20 @@ struct spec_model {
 
 namespace {
 
+// K splits of a bf16 projection: about 512 workgroups when every wave takes one
+// 16-feature tile (four tiles per workgroup), each split a whole number of
+// 256-wide units.  Depends on (N, K) only, so results never depend on R.
 int split_for(const spec_model* m, int N, int K, bool fused_pair) {
   if (!m->bf16 || fused_pair) return 1;
-  const int groups = (N + 15) / 16;
-  const int chunks = K / 256;
-  // aim for ~2048 waves (8 per CU) of at least one 256-wide chunk each
-  int S = (int)std::lround(2048.0 / groups);
-  S = std::max(1, std::min(S, chunks));
+  const int cols = ((N + 15) / 16 + 3) / 4;
+  const int units = K / 256;
+  int S = (int)std::lround(512.0 / cols);
+  S = std::max(1, std::min(S, units));
   return S;
 }
 
 struct WsLayout {
-  size_t x, h, P, q, o, a, rope, stk, stv, gst, apart, lmp, rstat, dec, racep, total;
+  size_t x, h, P, q, o, a, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, total;
   size_t stage_layer_elems;     // elements per attention layer in stk/stv
   size_t gst_layer_floats;      // floats per gdn layer in gst
   int n_chunks;
@@ -94,14 +96,16 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
     pmax = std::max(pmax, (size_t)m->s_o_gdn.S * H);
   }
   if (d.n_layers) pmax = std::max(pmax, (size_t)m->s_down.S * H);
-  // activations are float32: an fp32 model keeps them as floats, a bf16 model as
-  // hi/lo bf16 planes [2][R][width] (the same four bytes per element)
+  // activations are float32: an fp32 model keeps them as floats [R][width], a
+  // bf16 model as hi/lo bf16 planes in fragment order, 16 ceil(R / 16) rows each
+  // (the same four bytes per element)
+  const size_t R16 = (size_t)sv::round16(R);
   w.x = take((size_t)R * H * 4);
-  w.h = take((size_t)R * H * 4);
+  w.h = take(R16 * H * 4);
   w.P = take((size_t)R * pmax * 4);
   w.q = take((size_t)R * qdim * 4);
-  w.o = take((size_t)R * std::max(qdim, gdim) * 4);
-  w.a = take((size_t)R * d.ffn * 4);
+  w.o = take(R16 * std::max(qdim, gdim) * 4);
+  w.a = take(R16 * d.ffn * 4);
   w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 8);
   w.stage_layer_elems = (size_t)R * d.n_kv_heads * d.head_dim;
   w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
@@ -113,6 +117,7 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.lmp = take((size_t)R * m->lm_groups * sizeof(sv::LmPartial));
   w.rstat = take((size_t)R * sizeof(sv::RowStat));
   w.dec = take((size_t)L * sizeof(sv::LaneDecision));
+  w.racex = take(m->bf16 ? (size_t)sv::round16(L) * H * 4 : 0);
   w.racep = take((size_t)L * m->lm_groups * 16);
   w.total = off;
   return w;
@@ -221,21 +226,23 @@ struct ProfScope {
   } while (0)
 
 // ---------------------------------------------------------------- projections
-// X: an fp32 model's float activations [R][K]; for a bf16 model the hi plane of
-// [2][R][K] bf16 planes (two_planes) or a single exact bf16 plane.
+// X: an fp32 model's float activations [R][K]; for a bf16 model the packed
+// activation planes (hi, then lo when two_planes; one exact bf16 plane otherwise).
+// W: packed fragments (bf16) or row-major [N][K] float.
 int project(const spec_model* m, int cls, const void* X, bool two_planes, const void* W0, const void* W1, int R,
             int N, int K, int S, float* P, void* Y, hipStream_t st) {
   ProfScope ps(m, cls, st);
   if (m->bf16) {
-    sv::GemmParams p{};
-    p.Xh = reinterpret_cast<const sv::bf16_t*>(X);
-    p.Xl = two_planes ? p.Xh + (size_t)R * K : nullptr;
+    sv::ProjParams p{};
+    p.X = reinterpret_cast<const sv::bf16_t*>(X);
+    p.xplane = sv::act_plane(R, K);
     p.W0 = reinterpret_cast<const sv::bf16_t*>(W0);
     p.W1 = reinterpret_cast<const sv::bf16_t*>(W1);
-    p.R = R; p.N = N; p.K = K; p.S = S; p.groups = (N + 15) / 16;
+    p.R = R; p.N = N; p.K = K; p.S = S; p.tiles = (N + 15) / 16;
     p.P = P;
-    p.Yb = reinterpret_cast<sv::bf16_t*>(Y);
-    return sv::launch_gemm_bf16(p, W1 ? 2 : 1, W1 != nullptr, st);
+    p.Y = reinterpret_cast<sv::bf16_t*>(Y);
+    p.yplane = sv::act_plane(R, N);
+    return sv::launch_proj(p, W1 != nullptr, two_planes ? 2 : 1, st);
   }
   sv::GemmF32Params p{};
   p.X = reinterpret_cast<const float*>(X);
@@ -322,6 +329,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
 int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, hipStream_t st) {
   sv::LmParams p{};
   p.X = at<void>(r->workspace, w.h);
+  p.xplane = sv::act_plane(ri.R, m->d.hidden);
   p.xs = m->d.n_layers == 0 ? 1 : 2;
   p.W = m->d.lm_head;
   p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden;
@@ -457,7 +465,8 @@ int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidde
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (m->bf16)
-    SV_CHECK(sv::launch_hidden_planes(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden, s));
+    SV_CHECK(sv::launch_pack_rows(hidden, at<void>(r->workspace, w.h), ri.R, m->d.hidden,
+                                  sv::act_plane(ri.R, m->d.hidden), m->d.n_layers == 0 ? 1 : 2, s));
   else
     SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * 4, s));
   return lm_stats(m, r, ri, w, s);
@@ -483,8 +492,15 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
                                   out_tokens, ri, s));
   if (sampled) {
     sv::RaceParams p{};
-    p.X = at<void>(ws, w.h);
     p.xs = m->d.n_layers == 0 ? 1 : 2;
+    if (m->bf16) {
+      p.X = at<void>(ws, w.racex);
+      p.xplane = sv::act_plane(ri.L, m->d.hidden);
+      SV_CHECK(sv::launch_gather_rows(at<void>(ws, w.h), sv::act_plane(ri.R, m->d.hidden), at<void>(ws, w.racex),
+                                      p.xplane, at<sv::LaneDecision>(ws, w.dec), ri.L, m->d.hidden, p.xs, s));
+    } else {
+      p.X = at<void>(ws, w.h);
+    }
     p.W = m->d.lm_head;
     p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
     p.groups = m->lm_groups;
@@ -543,13 +559,30 @@ int spec_debug_gemm(const spec_model* m, const void* X, const void* W, float* Y,
   if (m->bf16 && (K % 256) != 0) return SPEC_E_UNSUPPORTED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int S = split_for(m, N, K, false);
-  if (S == 1) return project(m, SPEC_K_PROJ_IN, X, false, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
-  const size_t need = (size_t)S * R * N * 4;
-  if (!workspace || workspace_bytes < need) return SPEC_E_WORKSPACE;
-  float* P = reinterpret_cast<float*>(workspace);
-  SV_CHECK(project(m, SPEC_K_PROJ_IN, X, false, W, nullptr, R, N, K, S, P, nullptr, s));
+  if (!m->bf16) return project(m, SPEC_K_PROJ_IN, X, false, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
+  // bf16: the rows are packed into the workspace, then partials follow
+  const size_t xbytes = align_up(sv::act_plane(R, K) * 2);
+  const size_t need = xbytes + (S > 1 ? (size_t)S * R * N * 4 : 0);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return SPEC_E_WORKSPACE;
+  void* xp = workspace;
+  SV_CHECK(sv::launch_pack_rows(X, xp, R, K, sv::act_plane(R, K), 1, s));
+  if (S == 1) return project(m, SPEC_K_PROJ_IN, xp, false, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
+  float* P = at<float>(workspace, xbytes);
+  SV_CHECK(project(m, SPEC_K_PROJ_IN, xp, false, W, nullptr, R, N, K, S, P, nullptr, s));
   SV_CHECK(sv::launch_sum_partials(P, S, (size_t)R * N, Y, s));
   return SPEC_OK;
+}
+
+int64_t spec_packed_weight_bytes(int N, int K) {
+  if (N < 1 || K < 256 || (K % 256) != 0) return SPEC_E_INVAL;
+  return (int64_t)sv::round16(N) * K * 2;
+}
+
+int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream) {
+  if (!src || !dst || N < 1 || K < 256 || (K % 256) != 0) return SPEC_E_INVAL;
+  if (src == dst) return SPEC_E_INVAL;
+  return sv::launch_pack_weight(src, dst, N, K, reinterpret_cast<hipStream_t>(stream)) ? SPEC_E_HIP : SPEC_OK;
 }
 
 int spec_profile_enable(spec_model* m, int kernel_class) {

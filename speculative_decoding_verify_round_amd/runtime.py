@@ -24,15 +24,28 @@ def _upload(a, dtype, device):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dtype).contiguous()
 
 
+def pack_weight(w: torch.Tensor, stream: Optional[int] = None) -> torch.Tensor:
+    """A row-major bf16 device matrix [N][K] in the library's fragment layout (spec_pack_weight)."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.is_cuda
+    w = w.contiguous()
+    N, K = w.shape
+    n = B.spec_packed_weight_bytes(N, K) // 2
+    out = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    st = torch.cuda.current_stream(w.device).cuda_stream if stream is None else stream
+    B.spec_pack_weight(w.data_ptr(), out.data_ptr(), N, K, st)
+    return out
+
+
 class DeviceModel:
     """Weights on the device plus the library's model handle.
 
     cfg: a decoder config (shape attributes); weights: dict with "embed",
     "lm_head", "final_norm" and "layers" (list of dicts with norm1, w_in, w_o,
-    norm2, w_gate, w_up, w_down), numpy or torch.
+    norm2, w_gate, w_up, w_down), numpy or torch, matrices row-major [out][in].
     """
 
-    def __init__(self, cfg, weights: Dict[str, object], device="cuda", attn_chunk: int = 0):
+    def __init__(self, cfg, weights: Dict[str, object], device="cuda", attn_chunk: int = 0,
+                 prepacked: bool = False):
         B.load_library()
         self.cfg = cfg
         self.device = _dev(device)
@@ -40,7 +53,10 @@ class DeviceModel:
         self.t: Dict[str, torch.Tensor] = {}
         up = lambda a: _upload(a, self.tdtype, self.device)
         f32 = lambda a: _upload(a, torch.float32, self.device)
-        self.t["lm_head"] = up(weights["lm_head"])
+        # bf16 matrices go to the device in the fragment layout the projections read
+        # (prepacked: the caller already holds them packed, as flat bf16 device tensors)
+        mat = (lambda a: pack_weight(up(a))) if cfg.dtype == "bf16" and not prepacked else up
+        self.t["lm_head"] = mat(weights["lm_head"])
         if "embed" in weights:
             self.t["embed"] = up(weights["embed"])
         self.t["final_norm"] = f32(weights["final_norm"])
@@ -50,7 +66,7 @@ class DeviceModel:
             lw = weights["layers"][i]
             d = {"norm1": f32(lw["norm1"]), "norm2": f32(lw["norm2"])}
             for k in ("w_in", "w_o", "w_gate", "w_up", "w_down"):
-                d[k] = up(lw[k])
+                d[k] = mat(lw[k])
             self.layers.append(d)
             lw_arr[i] = B.SpecLayerWeights(d["norm1"].data_ptr(), d["w_in"].data_ptr(), d["w_o"].data_ptr(),
                                            d["norm2"].data_ptr(), d["w_gate"].data_ptr(), d["w_up"].data_ptr(),

@@ -168,3 +168,16 @@ def test_other_calls_validate(model):
     assert lib.spec_debug_gemm(model, FAKE, FAKE, FAKE, 0, 16, 256, None, 0, None) == B.SPEC_E_INVAL
     assert lib.spec_debug_gemm(model, FAKE, FAKE, FAKE, 8, 16, 100, None, 0, None) == B.SPEC_E_UNSUPPORTED
     assert lib.spec_profile_enable(model, 99) == B.SPEC_E_INVAL
+
+
+def test_pack_weight_sizes_and_validation():
+    """Packed size = 16 ceil(N / 16) K bf16 elements; bad shapes are refused before any HIP call."""
+    lib = B.load_library()
+    assert lib.spec_packed_weight_bytes(16, 256) == 16 * 256 * 2
+    assert lib.spec_packed_weight_bytes(17, 256) == 32 * 256 * 2
+    assert lib.spec_packed_weight_bytes(151936, 5120) == 151936 * 5120 * 2
+    assert lib.spec_packed_weight_bytes(0, 256) == B.SPEC_E_INVAL
+    assert lib.spec_packed_weight_bytes(16, 300) == B.SPEC_E_INVAL
+    assert lib.spec_pack_weight(None, FAKE, 16, 256, None) == B.SPEC_E_INVAL
+    assert lib.spec_pack_weight(FAKE, FAKE, 16, 256, None) == B.SPEC_E_INVAL      # in place
+    assert lib.spec_pack_weight(FAKE, FAKE + 64, 16, 100, None) == B.SPEC_E_INVAL

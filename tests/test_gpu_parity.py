@@ -30,13 +30,14 @@ def _bf16_head_model(H=256, V=1024):
                                    (64, 7168, 5120), (8, 5120, 17408), (64, 34816, 5120)])
 def test_projection_kernel(R, N, K):
     from speculative_decoding_verify_round_amd import binding as B
+    from speculative_decoding_verify_round_amd.runtime import pack_weight
     log(f"projection R={R} N={N} K={K}")
     dm = _bf16_head_model()
     g = torch.Generator().manual_seed(R * 7919 + N)
     X = torch.randn(R, K, generator=g).to(torch.bfloat16)
     W = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
     ref = (X.double() @ W.double().T).numpy()
-    Xd, Wd = X.cuda(), W.cuda()
+    Xd, Wd = X.cuda(), pack_weight(W.cuda())
     ws = torch.zeros(64 * N * 64 * 4 + 256, dtype=torch.uint8, device="cuda")
     Y = torch.empty(R, N, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream().cuda_stream

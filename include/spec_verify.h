@@ -109,8 +109,8 @@ typedef struct {
  * S_t = alpha S + beta (v - alpha S k) k^T, o_t = S_t q_t. */
 typedef struct {
   int n_layers;            /* >= 0; 0 = LM head only (spec_verify_head) */
-  int hidden;              /* multiple of 32 */
-  int n_q_heads, n_kv_heads, head_dim;   /* head_dim 128 (bf16) or <= 128 (f32) */
+  int hidden;              /* multiple of 4 (bf16: of 256), <= 8192 */
+  int n_q_heads, n_kv_heads, head_dim;   /* head_dim 128 (bf16) or <= 128 and a multiple of 8 (f32) */
   int ffn;                 /* multiple of 32 */
   int vocab;               /* multiple of 16 */
   int dtype;               /* SPEC_F32 | SPEC_BF16: weights, KV, stored activations */
@@ -119,7 +119,7 @@ typedef struct {
   float rms_eps;           /* e.g. 1e-6 */
   float rope_theta;        /* 0 = no positional encoding */
   int kv_block;            /* must be SPEC_KV_BLOCK */
-  int attn_chunk;          /* positions per split-KV chunk (multiple of 256); 0 = 1024 */
+  int attn_chunk;          /* positions per split-KV chunk (multiple of 256, <= 4096); 0 = 256 */
   const void* embed;       /* [vocab][hidden] row-major; may be NULL for a head-only model */
   const void* lm_head;     /* [vocab][hidden]: row-major (f32) or packed (bf16) */
   const float* final_norm; /* [hidden]; may be NULL for a head-only model */

@@ -33,9 +33,10 @@ namespace sv {
 
 template <int QT>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
-  constexpr int D = 128, STEP = 64, KP = D + 8, VP = STEP + 8, PW = D + 2;
+  constexpr int D = 128, STEP = 64, KP = D + 8, VP = STEP + 8, PW = kAttnPartPad + D;
   __shared__ bf16_t Ks[STEP * KP];   // [position][d], rows padded by 16 B
   __shared__ bf16_t Vs[D * VP];      // [d][position], rows padded by 16 B
+  __shared__ int sblk[kMaxChunk / kBlock];   // the chunk's block ids
   const int c = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -49,6 +50,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   const int cend = min(pos0 + p.chunk, end);
   const int nsteps = (cend - pos0 + STEP - 1) / STEP;
   const int* bt = p.block_table + (size_t)l * p.max_blocks;
+  // block ids of the chunk, looked up once (a table entry past the lane's blocks is never used)
+  for (int i = tid; i < p.chunk / kBlock; i += blockDim.x) {
+    const int b = pos0 / kBlock + i;
+    sblk[i] = b < p.max_blocks ? clamp_blk(bt[b], p.n_blocks) : 0;
+  }
+  __syncthreads();
   const float* Qp = p.q;
   const bf16_t* Kp = reinterpret_cast<const bf16_t*>(p.kpool);
   const bf16_t* Vp = reinterpret_cast<const bf16_t*>(p.vpool);
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
     for (int j = 0; j < 4; ++j) {
       const int pos = base + (tid >> 4) + 16 * j, seg = tid & 15;
       const bf16_t* src = nullptr;
-      if (pos < kvl) src = Kp + (((size_t)clamp_blk(bt[pos >> 4], p.n_blocks) * nkv + g) * kBlock + (pos & 15)) * D;
+      if (pos < kvl) src = Kp + (((size_t)sblk[(pos - pos0) >> 4] * nkv + g) * kBlock + (pos & 15)) * D;
       else if (pos < end) src = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D;
       kreg[j] = src ? *reinterpret_cast<const u32x4*>(src + seg * 8) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -72,10 +79,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
     for (int j = 0; j < 4; ++j) {
       const int bpos = base + 16 * j, d = tid >> 1, hf = tid & 1;
       if (bpos + 16 <= kvl) {
-        const int blk = clamp_blk(bt[bpos >> 4], p.n_blocks);
+        const int blk = sblk[(bpos - pos0) >> 4];
         vreg[j] = *reinterpret_cast<const u32x4*>(Vp + (((size_t)blk * nkv + g) * D + d) * kBlock + hf * 8);
       } else {
-        const int blk = bpos < kvl ? clamp_blk(bt[bpos >> 4], p.n_blocks) : 0;
+        const int blk = bpos < kvl ? sblk[(bpos - pos0) >> 4] : 0;
         uint32_t w[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
   extern __shared__ float lds[];   // [4][Mq][d + 2]
   const int c = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int D = p.d, PW = D + 2;
+  const int D = p.d, PW = D + kAttnPartPad;
   const int cols = p.ri.lane_cols[l], rs = p.ri.lane_start[l];
   const int cap = p.max_blocks * kBlock;
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
@@ -325,44 +332,75 @@ int launch_attention(const AttnParams& p, bool bf16, hipStream_t st) {
   } else {
     int maxMq = 0;
     for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
-    const size_t lds = (size_t)4 * maxMq * (p.d + 2) * sizeof(float);
+    const size_t lds = (size_t)4 * maxMq * (p.d + kAttnPartPad) * sizeof(float);
     hipLaunchKernelGGL(k_attn_f32, grid, block, lds, st, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Merge the chunk partials of each (lane, kv head) in chunk order; write o = O / L.
+// Thread = (query row m, four consecutive d); all chunk loads of a thread are
+// issued before the float64 merge, which visits the chunks in order.
+constexpr int kCombineBatch = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
   const int g = blockIdx.x, l = blockIdx.y;
-  const int D = p.d, PW = D + 2;
+  const int D = p.d, PW = D + kAttnPartPad, DQ = D >> 2;
+  const int mpw = blockDim.x / DQ;                       // query rows per workgroup
+  const int m = blockIdx.z * mpw + threadIdx.x / DQ, dq = threadIdx.x - (threadIdx.x / DQ) * DQ;
   const int cols = p.ri.lane_cols[l], rs = p.ri.lane_start[l];
+  const int Mq = cols * p.G;
+  if (threadIdx.x >= mpw * DQ || m >= Mq) return;
   const int cap = p.max_blocks * kBlock;
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
   const int nch = min((end + p.chunk - 1) / p.chunk, p.n_chunks);
-  const int Mq = cols * p.G;
-  const float* base = p.part + (((size_t)l * p.nkv + g) * p.n_chunks) * 64 * PW;
-  for (int idx = threadIdx.x; idx < Mq * D; idx += blockDim.x) {
-    const int m = idx / D, dd = idx - m * D;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, base[((size_t)c * 64 + m) * PW + D]);
-    double Oc = 0.0, Lc = 0.0;
-    for (int c = 0; c < nch; ++c) {
-      const float* src = base + ((size_t)c * 64 + m) * PW;
-      if (src[D] != -INFINITY) {
-        const double f = exp2((double)src[D] - (double)M);
-        Oc += (double)src[dd] * f;
-        Lc += (double)src[D + 1] * f;
+  const float* base = p.part + (((size_t)l * p.nkv + g) * p.n_chunks * 64 + m) * PW;
+  const size_t cstride = (size_t)64 * PW;
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
+    float mv[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) mv[i] = base[min(c0 + i, nch - 1) * cstride + D];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) M = fmaxf(M, mv[i]);
+  }
+  double Oc[4] = {0.0, 0.0, 0.0, 0.0}, Lc = 0.0;
+  for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
+    f32x4 ov[kCombineBatch];
+    float mv[kCombineBatch], lv[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int c = min(c0 + i, nch - 1);
+      const float* src = base + c * cstride;
+      ov[i] = *reinterpret_cast<const f32x4*>(src + 4 * dq);
+      mv[i] = src[D];
+      lv[i] = src[D + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      if (c0 + i < nch && mv[i] != -INFINITY) {
+        const double f = exp2((double)mv[i] - (double)M);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Oc[e] += (double)ov[i][e] * f;
+        Lc += (double)lv[i] * f;
       }
     }
-    const int j = m / p.G, hh = m - j * p.G;
-    st_out(o, act_plane(p.ri.R, p.nq * D), act_index(o, rs + j, (g * p.G + hh) * D + dd, p.nq * D), (float)(Oc / Lc));
   }
+  const int j = m / p.G, hh = m - j * p.G;
+  const int K = p.nq * D;
+  const size_t plane = act_plane(p.ri.R, K);
+  const int k0 = (g * p.G + hh) * D + 4 * dq;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st_out(o, plane, act_index(o, rs + j, k0 + e, K), (float)(Oc[e] / Lc));
 }
 
 int launch_attn_combine(const AttnParams& p, void* o, bool bf16, hipStream_t st) {
-  dim3 grid(p.nkv, p.ri.L), block(256);
+  int maxMq = 0;
+  for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
+  const int mpw = 256 / (p.d / 4);
+  dim3 grid(p.nkv, p.ri.L, (maxMq + mpw - 1) / mpw), block(256);
   if (bf16) hipLaunchKernelGGL(k_attn_combine<bf16_t>, grid, block, 0, st, p, reinterpret_cast<bf16_t*>(o));
   else hipLaunchKernelGGL(k_attn_combine<float>, grid, block, 0, st, p, reinterpret_cast<float*>(o));
   return hipGetLastError() == hipSuccess ? 0 : -1;

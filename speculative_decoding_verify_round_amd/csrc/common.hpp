@@ -10,6 +10,8 @@ constexpr int kMaxCols = 16;
 constexpr int kMaxLanes = 64;
 constexpr int kBlock = 16;       // tokens per paged-KV block
 constexpr int kWave = 64;
+constexpr int kMaxChunk = 4096;     // largest split-KV attention chunk (positions)
+constexpr int kAttnPartPad = 4;     // a chunk partial row: O[d], then m and l, then 2 pad floats
 
 typedef uint16_t bf16_t;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -158,6 +160,25 @@ __device__ __forceinline__ void st_out(float* base, size_t plane, size_t i, floa
 }
 __device__ __forceinline__ void st_out(bf16_t* base, size_t plane, size_t i, float v) { st_planes(base + i, plane, v); }
 
+// Four consecutive activations (r, k0 .. k0 + 3), k0 % 4 == 0, in one go: a float4
+// row-major store, or one 8-byte store per bf16 plane (they share a fragment lane slot).
+__device__ __forceinline__ void st_out4(float* base, size_t plane, int r, int k0, int K, const float (&v)[4]) {
+  (void)plane;
+  *reinterpret_cast<f32x4*>(base + (size_t)r * K + k0) = f32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void st_out4(bf16_t* base, size_t plane, int r, int k0, int K, const float (&v)[4]) {
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bf16_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
+    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[i] = (uint32_t)f2bf(v[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * i + 1] - bf2f(h1)) << 16);
+  }
+  const size_t o = frag_off(r, k0, K >> 5);
+  *reinterpret_cast<u32x2*>(base + o) = u32x2{hi[0], hi[1]};
+  *reinterpret_cast<u32x2*>(base + plane + o) = u32x2{lo[0], lo[1]};
+}
+
 // ----------------------------------------------------------------------------- launch parameters
 // Projection Y = X W^T over packed fragments.  K is a multiple of 256; split s
 // of S covers 256-wide units [s U / S, (s + 1) U / S), U = K / 256.
@@ -262,7 +283,7 @@ struct AttnParams {
   int chunk;              // positions per workgroup chunk
   int n_chunks;           // chunks per lane (grid x)
   float scale_log2;       // log2(e) / sqrt(d)
-  float* part;            // [L][nkv][n_chunks][64][d + 2]
+  float* part;            // [L][nkv][n_chunks][64][d + kAttnPartPad]
   RowInfo ri;
 };
 

@@ -34,116 +34,185 @@ int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float the
 }
 
 // ------------------------------------------------------------------------------- RMSNorm family
-// h = float32(x / sqrt(mean(x^2) + eps) * gain), evaluated in float64; a bf16
-// model stores h as its hi/lo bf16 planes in fragment order.
+// One 1024-thread workgroup per row; thread t owns the float4 groups t and
+// t + 1024 of the row (hidden <= 8192) and issues all of its loads before it
+// uses any.  h = float32(x / sqrt(mean(x^2) + eps) * gain), evaluated in
+// float64; a bf16 model stores h as hi/lo bf16 planes in fragment order.
+constexpr int kRowThreads = 1024;
+constexpr int kRowGroups = 2;     // float4 groups per thread
+constexpr int kSplitBatch = 8;    // split partials loaded per batch
+
 template <typename T>
-__device__ __forceinline__ void norm_row(const float* x, int r, int H, const float* gain, float eps, T* h,
-                                         size_t plane, double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += (double)x[i] * (double)x[i];
+__device__ __forceinline__ void norm_store(const f32x4 (&xn)[kRowGroups], int r, int H, const float* gain, float eps,
+                                           T* h, size_t plane, double ss, double* red) {
   const double tot = block_sum_f64(ss, red);
   const double scale = 1.0 / sqrt(tot / (double)H + (double)eps);
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    st_out(h, plane, act_index(h, r, i, H), (float)((double)x[i] * scale * (double)gain[i]));
+#pragma unroll
+  for (int gi = 0; gi < kRowGroups; ++gi) {
+    const int g = threadIdx.x + gi * kRowThreads;
+    if (4 * g >= H) break;
+    const f32x4 gn = *reinterpret_cast<const f32x4*>(gain + 4 * g);
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (float)((double)xn[gi][e] * scale * (double)gn[e]);
+    st_out4(h, plane, r, 4 * g, H, v);
+  }
+}
+
+__device__ __forceinline__ f32x4 ld_act4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld_act4(const bf16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xffff0000u)};
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tokens, const T* embed, int V, int H,
-                                                     const float* gain, float eps, float* x, T* h, int R) {
+__global__ __launch_bounds__(kRowThreads) void k_embed_norm(const int32_t* tokens, const T* embed, int V, int H,
+                                                             const float* gain, float eps, float* x, T* h, int R) {
   __shared__ double red[32];
   const int r = blockIdx.x;
   int tok = tokens[r];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
   float* xr = x + (size_t)r * H;
   const T* e = embed + (size_t)tok * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = ld_act(e + i);
-  __syncthreads();
-  norm_row(xr, r, H, gain, eps, h, act_plane(R, H), red);
+  f32x4 xn[kRowGroups];
+  double ss = 0.0;
+#pragma unroll
+  for (int gi = 0; gi < kRowGroups; ++gi) {
+    const int g = threadIdx.x + gi * kRowThreads;
+    xn[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (4 * g >= H) continue;
+    xn[gi] = ld_act4(e + 4 * g);
+    *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss += (double)xn[gi][q] * (double)xn[gi][q];
+  }
+  norm_store(xn, r, H, gain, eps, h, act_plane(R, H), ss, red);
 }
 
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
                       float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(ri.R), dim3(256), 0, st, tokens,
+    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, tokens,
                        reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h), ri.R);
   else
-    hipLaunchKernelGGL(k_embed_norm<float>, dim3(ri.R), dim3(256), 0, st, tokens,
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(ri.R), dim3(kRowThreads), 0, st, tokens,
                        reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h), ri.R);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// x[r] += sum_s P[s][r] (s in order), then h[r] = round(rmsnorm(x[r]) * gain)
+// Sum of the S split partials of one float4 of a projection, in split order, in float64.
+__device__ __forceinline__ void sum_splits4(const float* P, size_t split_stride, int S, double (&t)[4]) {
+  for (int s0 = 0; s0 < S; s0 += kSplitBatch) {
+    f32x4 pv[kSplitBatch];
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i)
+      pv[i] = *reinterpret_cast<const f32x4*>(P + (size_t)min(s0 + i, S - 1) * split_stride);
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i) {
+      if (s0 + i >= S) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (s0 + i == 0) ? (double)pv[i][e] : t[e] + (double)pv[i][e];
+    }
+  }
+}
+
+// x[r] += float(sum_s P[s][r]) (s in order), then h[r] = round(rmsnorm(x[r]) * gain)
 template <typename T>
-__global__ __launch_bounds__(256) void k_resid_norm(const float* P, int S, int R, float* x, int H,
-                                                     const float* gain, float eps, T* h) {
+__global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int S, int R, float* x, int H,
+                                                             const float* gain, float eps, T* h) {
   __shared__ double red[32];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    double t = P[(size_t)r * H + i];
-    for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * H + i];
-    xr[i] = (float)((double)xr[i] + (double)(float)t);   // x + float(projection)
+  f32x4 xn[kRowGroups];
+  double ss = 0.0;
+#pragma unroll
+  for (int gi = 0; gi < kRowGroups; ++gi) {
+    const int g = threadIdx.x + gi * kRowThreads;
+    xn[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (4 * g >= H) continue;
+    const f32x4 xo = *reinterpret_cast<const f32x4*>(xr + 4 * g);
+    double t[4];
+    sum_splits4(P + (size_t)r * H + 4 * g, (size_t)R * H, S, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xn[gi][e] = (float)((double)xo[e] + (double)(float)t[e]);   // x + float(projection)
+    *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss += (double)xn[gi][q] * (double)xn[gi][q];
   }
-  __syncthreads();
-  norm_row(xr, r, H, gain, eps, h, act_plane(R, H), red);
+  norm_store(xn, r, H, gain, eps, h, act_plane(R, H), ss, red);
 }
 
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
                       const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, x, H, gain, eps,
+    hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, x, H, gain, eps,
                        reinterpret_cast<bf16_t*>(h));
   else
-    hipLaunchKernelGGL(k_resid_norm<float>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, x, H, gain, eps,
+    hipLaunchKernelGGL(k_resid_norm<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, x, H, gain, eps,
                        reinterpret_cast<float*>(h));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // ------------------------------------------------------------------------------- QKV post
 // Sum the split-K partials of [q | k | v], rotate q and k (rotate-half, pair (i, i + d/2)),
-// round to the storage type, write q and stage K/V of every column.
+// round to the storage type, write q and stage K/V of every column.  One 1024-thread
+// workgroup per row; a thread takes four consecutive pairs of a q or k head, or four
+// consecutive v elements, and loads all splits before summing them.
 template <typename T>
-__global__ __launch_bounds__(256) void k_qkv_post(const float* P, int S, int R, const double* rope, int use_rope,
-                                                   int nq, int nkv, int d, float* q, T* sk, T* sv) {
+__global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S, int R, const double* rope,
+                                                           int use_rope, int nq, int nkv, int d, float* q, T* sk,
+                                                           T* sv) {
   const int r = blockIdx.x;
   const int N = (nq + 2 * nkv) * d, half = d / 2;
-  auto sum = [&](int n) {       // the projection, rounded once to float32
-    double t = P[(size_t)r * N + n];
-    for (int s = 1; s < S; ++s) t += P[((size_t)s * R + r) * N + n];
-    return (double)(float)t;
-  };
-  // rotated heads: q heads then k heads, processed as (head, pair) items
-  const int npairs = (nq + nkv) * half;
-  for (int it = threadIdx.x; it < npairs; it += blockDim.x) {
-    const int hd = it / half, i = it - hd * half;
-    const double a = sum(hd * d + i), b = sum(hd * d + i + half);
-    double ra = a, rb = b;
-    if (use_rope) {
-      const double c = rope[((size_t)r * half + i) * 2], s = rope[((size_t)r * half + i) * 2 + 1];
-      ra = a * c - b * s;
-      rb = b * c + a * s;
-    }
-    if (hd < nq) {
-      float* dst = q + ((size_t)r * nq + hd) * d;
-      dst[i] = (float)ra;
-      dst[i + half] = (float)rb;
+  const size_t sstride = (size_t)R * N;
+  const float* Pr = P + (size_t)r * N;
+  const int nrot = (nq + nkv) * (half / 4), nv = nkv * d / 4;
+  for (int it = threadIdx.x; it < nrot + nv; it += blockDim.x) {
+    if (it < nrot) {
+      const int hd = it / (half / 4), i0 = 4 * (it - hd * (half / 4));
+      double a[4], b[4];
+      sum_splits4(Pr + hd * d + i0, sstride, S, a);
+      sum_splits4(Pr + hd * d + i0 + half, sstride, S, b);
+      float ra[4], rb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double av = (double)(float)a[e], bv = (double)(float)b[e];   // the projection, rounded once
+        double x = av, y = bv;
+        if (use_rope) {
+          const double c = rope[((size_t)r * half + i0 + e) * 2], sn = rope[((size_t)r * half + i0 + e) * 2 + 1];
+          x = av * c - bv * sn;
+          y = bv * c + av * sn;
+        }
+        ra[e] = (float)x;
+        rb[e] = (float)y;
+      }
+      if (hd < nq) {
+        float* dst = q + ((size_t)r * nq + hd) * d;
+        *reinterpret_cast<f32x4*>(dst + i0) = f32x4{ra[0], ra[1], ra[2], ra[3]};
+        *reinterpret_cast<f32x4*>(dst + i0 + half) = f32x4{rb[0], rb[1], rb[2], rb[3]};
+      } else {
+        T* dst = sk + ((size_t)r * nkv + (hd - nq)) * d;     // staged for the cache
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { st_act(dst + i0 + e, ra[e]); st_act(dst + i0 + half + e, rb[e]); }
+      }
     } else {
-      T* dst = sk + ((size_t)r * nkv + (hd - nq)) * d;     // staged for the bf16 cache
-      st_act(dst + i, (float)ra);
-      st_act(dst + i + half, (float)rb);
+      const int i0 = 4 * (it - nrot);
+      double v[4];
+      sum_splits4(Pr + (nq + nkv) * d + i0, sstride, S, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_act(sv + (size_t)r * nkv * d + i0 + e, (float)(double)(float)v[e]);
     }
   }
-  for (int it = threadIdx.x; it < nkv * d; it += blockDim.x)
-    st_act(sv + (size_t)r * nkv * d + it, (float)sum((nq + nkv) * d + it));
 }
 
 int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
                     float* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
+    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
                        q, reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv));
   else
-    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(256), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
+    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
                        q, reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

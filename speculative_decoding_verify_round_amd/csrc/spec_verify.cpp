@@ -19,7 +19,7 @@ static_assert(sizeof(sv::LmPartial) == 32, "partial size");
 
 namespace {
 
-constexpr int kDefaultChunk = 1024;
+constexpr int kDefaultChunk = 256;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -113,7 +113,7 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.gst_layer_floats = (size_t)R * d.gdn_heads * (2 * 128 + 2);
   w.gst = take((size_t)m->n_gdn * w.gst_layer_floats * 4);
   w.n_chunks = m->n_attn ? (max_blocks * SPEC_KV_BLOCK + m->chunk - 1) / m->chunk : 0;
-  w.apart = take((size_t)L * d.n_kv_heads * w.n_chunks * 64 * (d.head_dim + 2) * 4);
+  w.apart = take((size_t)L * d.n_kv_heads * w.n_chunks * 64 * (d.head_dim + sv::kAttnPartPad) * 4);
   w.lmp = take((size_t)R * m->lm_groups * sizeof(sv::LmPartial));
   w.rstat = take((size_t)R * sizeof(sv::RowStat));
   w.dec = take((size_t)L * sizeof(sv::LaneDecision));
@@ -177,7 +177,7 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
       const int G = m->d.n_q_heads / m->d.n_kv_heads;
       const int mq = max_cols(ri) * G;
       if (m->bf16 && mq > 64) return SPEC_E_UNSUPPORTED;
-      if (!m->bf16 && (size_t)4 * mq * (m->d.head_dim + 2) * 4 > 65536) return SPEC_E_UNSUPPORTED;
+      if (!m->bf16 && (size_t)4 * mq * (m->d.head_dim + sv::kAttnPartPad) * 4 > 65536) return SPEC_E_UNSUPPORTED;
       if (r->kv_len_host) {
         for (int l = 0; l < r->lanes; ++l) {
           if (r->kv_len_host[l] < 0) return SPEC_E_INVAL;
@@ -379,8 +379,9 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
   if (!(d.rms_eps >= 0.f) || !(d.rope_theta >= 0.f)) return SPEC_E_INVAL;
   const bool bf = d.dtype == SPEC_BF16;
   if (bf && (d.hidden % 256) != 0) return SPEC_E_UNSUPPORTED;
+  if ((d.hidden % 4) != 0 || d.hidden > 8192) return SPEC_E_UNSUPPORTED;
   const int chunk = d.attn_chunk == 0 ? kDefaultChunk : d.attn_chunk;
-  if (chunk < 256 || (chunk % 256) != 0) return SPEC_E_UNSUPPORTED;
+  if (chunk < 256 || (chunk % 256) != 0 || chunk > sv::kMaxChunk) return SPEC_E_UNSUPPORTED;
   spec_model* m = new (std::nothrow) spec_model();
   if (!m) return SPEC_E_INVAL;
   m->d = d;
@@ -405,7 +406,7 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
       if (d.n_q_heads <= 0 || d.n_kv_heads <= 0 || (d.n_q_heads % d.n_kv_heads) != 0) { delete m; return SPEC_E_INVAL; }
       if (d.head_dim <= 0 || (d.head_dim % 2) != 0) { delete m; return SPEC_E_INVAL; }
       if (bf && (d.head_dim != 128 || ((d.n_q_heads * d.head_dim) % 256) != 0)) { delete m; return SPEC_E_UNSUPPORTED; }
-      if (!bf && d.head_dim > 128) { delete m; return SPEC_E_UNSUPPORTED; }
+      if (!bf && (d.head_dim > 128 || (d.head_dim % 8) != 0)) { delete m; return SPEC_E_UNSUPPORTED; }
     }
     if (m->n_gdn) {
       if (d.gdn_heads <= 0 || d.gdn_dim != 128) { delete m; return SPEC_E_UNSUPPORTED; }

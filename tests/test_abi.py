@@ -82,6 +82,7 @@ def test_model_create_validation():
     assert create_status(kv_block=32) == B.SPEC_E_UNSUPPORTED
     assert create_status(lm_head=None) == B.SPEC_E_INVAL
     assert create_status(hidden=200) == B.SPEC_E_UNSUPPORTED        # bf16 hidden must be a multiple of 256
+    assert create_status(hidden=8448) == B.SPEC_E_UNSUPPORTED       # row kernels hold at most 8192 per row
     assert create_status(head_dim=64) == B.SPEC_E_UNSUPPORTED       # bf16 attention runs head_dim 128
     assert create_status(dtype=B.SPEC_F32, hidden=200, head_dim=64, ffn=100) == B.SPEC_OK
     assert create_status(kinds=[0, 5]) == B.SPEC_E_INVAL

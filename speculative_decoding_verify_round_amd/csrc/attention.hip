@@ -26,6 +26,8 @@
 //   ([d][16 slots]) so that V^T tiles are contiguous; the lane's key order
 //   inside the K = 32 MFMA step equals the order in which the S^T result left
 //   it, so P needs no shuffle.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,25 +66,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   const int nkv = p.nkv;
 
   // ---- cooperative staging of one 64-position step: 4 K items and 4 V items of 16 B per thread
-  u32x4 kreg[4], vreg[4];
-  auto load_step = [&](int s) {
+  u32x4 kreg[1][4], vreg[1][4];
+  // Every load is issued unconditionally from a valid address (a position past the
+  // lane's live range reads a clamped one and is zeroed), so the loads carry no
+  // divergent branches; only the block that straddles the cached/staged boundary
+  // takes the (workgroup-uniform) element-wise V path.
+  auto load_step = [&](int s, auto set_tag) {
+    constexpr int B = decltype(set_tag)::value;
     const int base = pos0 + s * STEP;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pos = base + (tid >> 4) + 16 * j, seg = tid & 15;
-      const bf16_t* src = nullptr;
-      if (pos < kvl) src = Kp + (((size_t)sblk[(pos - pos0) >> 4] * nkv + g) * kBlock + (pos & 15)) * D;
-      else if (pos < end) src = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D;
-      kreg[j] = src ? *reinterpret_cast<const u32x4*>(src + seg * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int srow = min(max(pos - kvl, 0), cols - 1);
+      const bf16_t* kc = Kp + (((size_t)sblk[(pos - pos0) >> 4] * nkv + g) * kBlock + (pos & 15)) * D;
+      const bf16_t* ks = SK + ((size_t)(rs + srow) * nkv + g) * D;
+      const u32x4 v = *reinterpret_cast<const u32x4*>((pos < kvl ? kc : ks) + seg * 8);
+      kreg[B][j] = pos < end ? v : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int bpos = base + 16 * j, d = tid >> 1, hf = tid & 1;
+      const int blk = sblk[(bpos - pos0) >> 4];
+      const bf16_t* vb = Vp + (((size_t)blk * nkv + g) * D + d) * kBlock;
       if (bpos + 16 <= kvl) {
-        const int blk = sblk[(bpos - pos0) >> 4];
-        vreg[j] = *reinterpret_cast<const u32x4*>(Vp + (((size_t)blk * nkv + g) * D + d) * kBlock + hf * 8);
+        vreg[B][j] = *reinterpret_cast<const u32x4*>(vb + hf * 8);
       } else {
-        const int blk = bpos < kvl ? sblk[(bpos - pos0) >> 4] : 0;
         uint32_t w[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -90,22 +98,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int pos = bpos + hf * 8 + 2 * e2 + hh;
-            bf16_t v = 0;
-            if (pos < kvl) v = Vp[(((size_t)blk * nkv + g) * D + d) * kBlock + (pos & 15)];
-            else if (pos < end) v = SV[((size_t)(rs + pos - kvl) * nkv + g) * D + d];
+            const int srow = min(max(pos - kvl, 0), cols - 1);
+            const bf16_t vc = vb[pos & 15];
+            const bf16_t vs = SV[((size_t)(rs + srow) * nkv + g) * D + d];
+            const bf16_t v = pos < kvl ? vc : (pos < end ? vs : (bf16_t)0);
             two |= (uint32_t)v << (16 * hh);
           }
           w[e2] = two;
         }
-        vreg[j] = u32x4{w[0], w[1], w[2], w[3]};
+        vreg[B][j] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   };
-  auto store_step = [&]() {
+  auto store_step = [&](auto set_tag) {
+    constexpr int B = decltype(set_tag)::value;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * j) * KP + (tid & 15) * 8) = kreg[j];
-      *reinterpret_cast<u32x4*>(Vs + (tid >> 1) * VP + 16 * j + (tid & 1) * 8) = vreg[j];
+      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * j) * KP + (tid & 15) * 8) = kreg[B][j];
+      *reinterpret_cast<u32x4*>(Vs + (tid >> 1) * VP + 16 * j + (tid & 1) * 8) = vreg[B][j];
     }
   };
 
@@ -126,9 +136,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
       const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
-        qh[ds][i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        ql[ds][i] = (uint32_t)f2bf(v[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * i + 1] - bf2f(h1)) << 16);
+        uint32_t hw, lw;
+        split2(v[2 * i], v[2 * i + 1], hw, lw);
+        qh[ds][i] = hw;
+        ql[ds][i] = lw;
       }
     }
     lim = kvl + j;
@@ -138,78 +149,88 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_step(0);
-  for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();              // every wave is done reading the previous step
-    store_step();
-    __syncthreads();              // this step is staged
-    if (s + 1 < nsteps) load_step(s + 1);   // in flight during the compute below
-    if (!owner) continue;
+  // One 64-position step: S^T for the four 16-position tiles, one online-softmax
+  // update (max, rescale, exp) for all 64 positions, then O^T += V^T P^T over
+  // two 32-position MFMA steps.
+  auto compute_step = [&](int s) {
+    const int p0 = pos0 + s * STEP;
+    f32x4 sc[4];
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const int p0 = pos0 + s * STEP + ss * 32;
-      f32x4 sc[2];
+    for (int st = 0; st < 4; ++st) {
+      const bf16_t* kr = Ks + (st * 16 + r16) * KP + kq * 8;
+      sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16_t* kr = Ks + (ss * 32 + st * 16 + r16) * KP + kq * 8;
-        sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + ds * 32);
-          sc[st] = mfma_bf16(kf, ql[ds], sc[st]);
-          sc[st] = mfma_bf16(kf, qh[ds], sc[st]);
-        }
+      for (int ds = 0; ds < 4; ++ds) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + ds * 32);
+        sc[st] = mfma_bf16(kf, ql[ds], sc[st]);
+        sc[st] = mfma_bf16(kf, qh[ds], sc[st]);
       }
-      // lane holds S^T[p0 + 16 st + 4 kq + e][query m]
-      float x[8];
-      float mx = -INFINITY;
+    }
+    // lane holds S^T[p0 + 16 st + 4 kq + e][query m]
+    float x[16];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pos = p0 + st * 16 + 4 * kq + e;
-          const float v = pos <= lim ? sc[st][e] * p.scale_log2 : -INFINITY;
-          x[st * 4 + e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun, mx);
-      float pr[8];
-      float alpha = 1.f;
-      if (mnew == -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = 0.f;
-      } else {
-        alpha = exp2f(mrun - mnew);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = exp2f(x[i] - mnew);
+      for (int e = 0; e < 4; ++e) {
+        const int pos = p0 + st * 16 + 4 * kq + e;
+        const float v = pos <= lim ? sc[st][e] * p.scale_log2 : -INFINITY;
+        x[st * 4 + e] = v;
+        mx = fmaxf(mx, v);
       }
-      float ps = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);
+    float pr[16];
+    float alpha = 1.f;
+    if (mnew == -INFINITY) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ps += pr[i];
-      lrun = lrun * alpha + ps;
-      mrun = mnew;
-      // P = hi + lo in bf16 (what is left is below 2^-17 P)
-      u32x4 ph, pl;
+      for (int i = 0; i < 16; ++i) pr[i] = 0.f;
+    } else {
+      // arguments are <= 0: the raw v_exp_f32 (results below 2^-126 flush to 0)
+      alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ps += pr[i];
+    lrun = lrun * alpha + ps;
+    mrun = mnew;
+    // P = hi + lo in bf16 (what is left is below 2^-17 P); MFMA step c covers tiles 2c and 2c + 1
+    u32x4 ph[2], pl[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16_t h0 = f2bf(pr[2 * i]), h1 = f2bf(pr[2 * i + 1]);
-        ph[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        pl[i] = (uint32_t)f2bf(pr[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(pr[2 * i + 1] - bf2f(h1)) << 16);
+        uint32_t hw, lw;
+        split2(pr[8 * c + 2 * i], pr[8 * c + 2 * i + 1], hw, lw);
+        ph[c][i] = hw;
+        pl[c][i] = lw;
       }
-      // O^T[d][m] += V^T[d][keys] P^T[keys][m]; the lane's keys are (tile st, 4 kq .. 4 kq + 3)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+    // O^T[d][m] += V^T[d][keys] P^T[keys][m]; the lane's keys are (tile 2c + h, 4 kq .. 4 kq + 3)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16_t* vr = Vs + (dt * 16 + r16) * VP + ss * 32 + 4 * kq;
+        const bf16_t* vr = Vs + (dt * 16 + r16) * VP + c * 32 + 4 * kq;
         const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr);
         const u32x2 a1 = *reinterpret_cast<const u32x2*>(vr + 16);
         const u32x4 vf = {a0[0], a0[1], a1[0], a1[1]};
-        O[dt] *= alpha;
-        O[dt] = mfma_bf16(vf, pl, O[dt]);
-        O[dt] = mfma_bf16(vf, ph, O[dt]);
+        O[dt] = mfma_bf16(vf, pl[c], O[dt]);
+        O[dt] = mfma_bf16(vf, ph[c], O[dt]);
       }
-    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  load_step(0, I0{});
+  for (int s = 0; s < nsteps; ++s) {
+    __syncthreads();              // every wave is done reading the previous step
+    store_step(I0{});
+    __syncthreads();              // this step is staged
+    if (s + 1 < nsteps) load_step(s + 1, I0{});   // in flight during the compute below
+    if (owner) compute_step(s);
   }
   if (!owner) return;
   // chunk partial of query m: lane holds O^T[d = dt*16 + 4kq + e][m]

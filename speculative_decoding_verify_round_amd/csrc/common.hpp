@@ -32,12 +32,20 @@ struct RowInfo {
 // ----------------------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// float -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays NaN).  pk_bf16 rounds two values into one word, a in
+// the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Two float32 values as bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ float ld_act(const float* p) { return *p; }
@@ -128,9 +136,10 @@ __device__ __forceinline__ float u01(uint32_t w) {
 // (16 rows x 32 consecutive k) that one operand of v_mfma_f32_16x16x32_bf16
 // covers, stored lane-major, so a wave fetches an operand with one contiguous
 // 1 KB load (16 B per lane).  Lane i of fragment (g, s) holds elements
-// [16 g + i % 16][32 s + 8 (i / 16) + e], e = 0..7; fragment (g, s) starts at
-// element (g * KS + s) * 512 with KS = K / 32.  Weights [N][K] use it with
-// g = output-feature tile (features past N zero), activations [R][K] with
+// [16 g + i % 16][32 s + 8 (i / 16) + e], e = 0..7, and fragment (g, s) starts
+// at element (g * KS + s) * 512 with KS = K / 32: a tile's k steps are
+// contiguous, so a wave streams one contiguous region.  Weights [N][K] use it
+// with g = output-feature tile (features past N zero), activations [R][K] with
 // g = row tile; an activation plane holds 16 ceil(R / 16) rows.
 __host__ __device__ __forceinline__ size_t frag_off(int row, int k, int KS) {
   return ((size_t)((row >> 4) * KS + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
@@ -169,11 +178,7 @@ __device__ __forceinline__ void st_out4(float* base, size_t plane, int r, int k0
 __device__ __forceinline__ void st_out4(bf16_t* base, size_t plane, int r, int k0, int K, const float (&v)[4]) {
   uint32_t hi[2], lo[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const bf16_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
-    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[i] = (uint32_t)f2bf(v[2 * i] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * i + 1] - bf2f(h1)) << 16);
-  }
+  for (int i = 0; i < 2; ++i) split2(v[2 * i], v[2 * i + 1], hi[i], lo[i]);
   const size_t o = frag_off(r, k0, K >> 5);
   *reinterpret_cast<u32x2*>(base + o) = u32x2{hi[0], hi[1]};
   *reinterpret_cast<u32x2*>(base + plane + o) = u32x2{lo[0], lo[1]};

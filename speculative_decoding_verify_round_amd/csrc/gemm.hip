@@ -40,10 +40,11 @@ struct CoreShape {
 
 // acc[j][t] += W tile j (16 features) . X row tile t over the unit range
 // [step0 / 8, step0 / 8 + nu).  wp[j] points at tile j's fragment of step
-// step0, lane offset included.  xl: LDS ring [2][NB][64] u32x4.  Every wave of
+// step0, lane offset included; consecutive steps of a tile are wstep elements
+// apart (weights are stored step-major).  xl: LDS ring [2][NB][64] u32x4.  Every wave of
 // the workgroup must call this with the same step0 and nu.
 template <int RT, int T, int XS, int KC>
-__device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], const bf16_t* __restrict__ X,
+__device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t wstep, const bf16_t* __restrict__ X,
                                           size_t xplane, int KS, int step0, int nu, u32x4* xl,
                                           f32x4 (&acc)[T][RT]) {
   using C = CoreShape<RT, T, XS, KC>;
@@ -71,7 +72,7 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], const bf
 #pragma unroll
   for (int k = 0; k < kUnit; ++k)
 #pragma unroll
-    for (int j = 0; j < T; ++j) wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)k * 512));
+    for (int j = 0; j < T; ++j) wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)k * wstep));
   stage_store(0);
   __syncthreads();
   int cb = 0;
@@ -101,13 +102,49 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], const bf
         if constexpr (MORE) {
 #pragma unroll
           for (int j = 0; j < T; ++j)
-            wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)((u + 1) * kUnit + k) * 512));
+            wr[k][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)((u + 1) * kUnit + k) * wstep));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (next) stage_store(cb ^ 1);
       __syncthreads();
       cb ^= 1;
+    }
+  };
+  for (int u = 0; u + 1 < nu; ++u) run_unit(std::true_type{}, u);
+  run_unit(std::false_type{}, nu - 1);
+}
+
+// One row tile (R <= 16), one wave per workgroup: the activation fragments are
+// read straight from memory (they stay in L2) into a ring of the same depth as
+// the weights', so the launch can carry four times as many workgroups (the
+// dispatcher balances them across CUs) and needs neither LDS nor barriers.
+template <int T, int XS>
+__device__ __forceinline__ void proj_core_direct(const bf16_t* const (&wp)[T], size_t wstep,
+                                                 const bf16_t* __restrict__ X, size_t xplane, int step0, int nu,
+                                                 f32x4 (&acc)[T]) {
+  const int lane = threadIdx.x & 63;
+  const bf16_t* xp = X + (size_t)step0 * 512 + lane * 8;   // row tile 0: fragment s at s * 512
+  u32x4 wr[kUnit][T], xr[kUnit][XS];
+  auto load = [&](int slot, int st) {
+#pragma unroll
+    for (int pl = 0; pl < XS; ++pl)
+      xr[slot][pl] = *reinterpret_cast<const u32x4*>(xp + pl * xplane + (size_t)st * 512);
+#pragma unroll
+    for (int j = 0; j < T; ++j) wr[slot][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)st * wstep));
+  };
+#pragma unroll
+  for (int k = 0; k < kUnit; ++k) load(k, k);
+  auto run_unit = [&](auto more_tag, int u) {
+    constexpr bool MORE = decltype(more_tag)::value;
+#pragma unroll
+    for (int k = 0; k < kUnit; ++k) {
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+#pragma unroll
+        for (int pl = XS - 1; pl >= 0; --pl) acc[j] = mfma_bf16(wr[k][j], xr[k][pl], acc[j]);
+      if constexpr (MORE) load(k, (u + 1) * kUnit + k);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int u = 0; u + 1 < nu; ++u) run_unit(std::true_type{}, u);
@@ -151,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
   for (int j = 0; j < T; ++j)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core<RT, T, XS, KC>(wp, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
+  proj_core<RT, T, XS, KC>(wp, 512, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
   // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
   const int r16 = lane & 15, kq = lane >> 4;
   if constexpr (EPI == 0) {
@@ -182,18 +219,60 @@ __global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
       if (r >= p.R) continue;
       uint32_t hi[2], lo[2];
 #pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const float a0 = swiglu(acc[0][t][e], acc[1][t][e]), a1 = swiglu(acc[0][t][e + 1], acc[1][t][e + 1]);
-        const bf16_t h0 = f2bf(a0), h1 = f2bf(a1);
-        const bf16_t l0 = f2bf(a0 - bf2f(h0)), l1 = f2bf(a1 - bf2f(h1));
-        hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
+      for (int e = 0; e < 4; e += 2)
+        split2(swiglu(acc[0][t][e], acc[1][t][e]), swiglu(acc[0][t][e + 1], acc[1][t][e + 1]), hi[e / 2], lo[e / 2]);
       if (nf + 4 <= p.N) {   // four consecutive k of one row: 8 contiguous bytes per plane
         const size_t o = frag_off(r, nf, KSy);
         *reinterpret_cast<u32x2*>(p.Y + o) = u32x2{hi[0], hi[1]};
         *reinterpret_cast<u32x2*>(p.Y + p.yplane + o) = u32x2{lo[0], lo[1]};
       }
+    }
+  }
+}
+
+// R <= 16: one wave per workgroup (T tiles, one split), epilogues as k_proj.
+template <int T, int XS, int EPI>
+__global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
+  const int lane = threadIdx.x & 63;
+  const int col = blockIdx.x % p.cols, s = blockIdx.x / p.cols;
+  const int KS = p.K >> 5, U = p.K >> 8;
+  const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
+  int tile[T];
+  const bf16_t* wp[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    tile[j] = EPI == 1 ? col : col * T + j;
+    const int tc = min(tile[j], p.tiles - 1);
+    const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
+    wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
+  }
+  f32x4 acc[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  proj_core_direct<T, XS>(wp, 512, p.X, p.xplane, u0 * kUnit, u1 - u0, acc);
+  const int r = lane & 15, kq = lane >> 4;
+  if (r >= p.R) return;
+  if constexpr (EPI == 0) {
+    const bool vec = (p.N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      if (tile[j] >= p.tiles) continue;
+      const int nf = tile[j] * 16 + 4 * kq;
+      float* dst = p.P + ((size_t)s * p.R + r) * p.N + nf;
+      if (vec && nf + 4 <= p.N) {
+        *reinterpret_cast<f32x4*>(dst) = acc[j];
+      } else {
+        for (int e = 0; e < 4 && nf + e < p.N; ++e) dst[e] = acc[j][e];
+      }
+    }
+  } else {
+    if (tile[0] >= p.tiles) return;
+    const int nf = tile[0] * 16 + 4 * kq;
+    if (nf + 4 <= p.N) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = swiglu(acc[0][e], acc[1][e]);
+      st_out4(p.Y, p.yplane, r, nf, p.N, v);
     }
   }
 }
@@ -204,6 +283,15 @@ int proj_tiles_per_wave(int R) { return R > 32 ? 2 : 1; }
 int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
   ProjParams p = p0;
   const int RT = (p.R + 15) / 16;
+  if (RT == 1) {   // one wave per workgroup, two tiles per wave
+    constexpr int T = 2;
+    p.cols = swiglu ? p.tiles : (p.tiles + T - 1) / T;
+    dim3 grid(p.cols * p.S), block(64);
+    if (swiglu) hipLaunchKernelGGL((k_proj_direct<2, 2, 1>), grid, block, 0, st, p);
+    else if (xs == 2) hipLaunchKernelGGL((k_proj_direct<2, 2, 0>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((k_proj_direct<2, 1, 0>), grid, block, 0, st, p);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int T = swiglu ? 2 : proj_tiles_per_wave(p.R);
   const int blocks = swiglu ? p.tiles : (p.tiles + T - 1) / T;
   p.cols = (blocks + 3) / 4;
@@ -412,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
   for (int j = 0; j < T; ++j)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core<RT, T, XS, KC>(wp, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
+  proj_core<RT, T, XS, KC>(wp, 512, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
   Stat* sh = reinterpret_cast<Stat*>(xl);   // the core ends on a barrier: the ring is free
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -575,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void k_race_bf16(RaceParams p) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // X: the rejected rows gathered lane by lane (row tile t holds lanes 16 t ..)
-  proj_core<RT, T, XS, KC>(wp, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
+  proj_core<RT, T, XS, KC>(wp, 512, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
   RaceKey* sh = reinterpret_cast<RaceKey*>(xl);
 #pragma unroll
   for (int t = 0; t < RT; ++t) {

@@ -1,7 +1,7 @@
 // C ABI of the verify round: validation, the row-budget planner, workspace
 // layout and the launch sequence on the caller's stream.  No device memory is
 // allocated here; the caller owns every device buffer.
-#include "../../include/spec_verify.h"
+#include "spec_verify.h"
 
 #include <hip/hip_runtime.h>
 

@@ -194,6 +194,7 @@ struct ProjParams {
   size_t xplane;        // elements per activation plane
   int R, N, K, S;
   int tiles;            // ceil(N / 16)
+  int units;            // tile pairs (balanced launch)
   int cols;             // workgroups per split
   float* P;             // [S][R][N] float32 partial sums
   bf16_t* Y;            // SwiGLU output planes, packed with width N

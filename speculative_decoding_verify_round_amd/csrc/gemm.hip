@@ -31,11 +31,11 @@ namespace sv {
 
 constexpr int kUnit = 8;   // MFMA k-steps (32 each) per 256-wide unit; splits are whole units
 
-template <int RT, int T, int XS, int KC>
+template <int RT, int T, int XS, int KC, int NW = 4>
 struct CoreShape {
   static constexpr int NC = kUnit / KC;      // X chunks per unit
   static constexpr int NB = KC * RT * XS;    // 1 KB X fragments per chunk
-  static constexpr int NBW = NB / 4;         // staged per wave
+  static constexpr int NBW = (NB + NW - 1) / NW;   // staged per wave (NW waves per workgroup)
 };
 
 // acc[j][t] += W tile j (16 features) . X row tile t over the unit range
@@ -43,17 +43,18 @@ struct CoreShape {
 // step0, lane offset included; consecutive steps of a tile are wstep elements
 // apart (weights are stored step-major).  xl: LDS ring [2][NB][64] u32x4.  Every wave of
 // the workgroup must call this with the same step0 and nu.
-template <int RT, int T, int XS, int KC>
+template <int RT, int T, int XS, int KC, int NW = 4>
 __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t wstep, const bf16_t* __restrict__ X,
                                           size_t xplane, int KS, int step0, int nu, u32x4* xl,
                                           f32x4 (&acc)[T][RT]) {
-  using C = CoreShape<RT, T, XS, KC>;
+  using C = CoreShape<RT, T, XS, KC, NW>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // this wave's share of an X chunk: fragment b = (plane * RT + tile) * KC + step
+  // (with NB not a multiple of NW the last waves stage fewer; the test is wave-uniform)
   uint32_t xoff[C::NBW];
 #pragma unroll
   for (int i = 0; i < C::NBW; ++i) {
-    const int b = wave * C::NBW + i;
+    const int b = min(wave * C::NBW + i, C::NB - 1);
     const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
     xoff[i] = (uint32_t)(pl * xplane + ((size_t)t * KS + st) * 512 + lane * 8);
   }
@@ -61,11 +62,14 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t w
   auto stage_load = [&](int stepc) {
 #pragma unroll
     for (int i = 0; i < C::NBW; ++i)
-      sx[i] = *reinterpret_cast<const u32x4*>(X + xoff[i] + (size_t)stepc * 512);
+      if (C::NB % NW == 0 || wave * C::NBW + i < C::NB)
+        sx[i] = *reinterpret_cast<const u32x4*>(X + xoff[i] + (size_t)stepc * 512);
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < C::NBW; ++i) xl[((size_t)buf * C::NB + wave * C::NBW + i) * 64 + lane] = sx[i];
+    for (int i = 0; i < C::NBW; ++i)
+      if (C::NB % NW == 0 || wave * C::NBW + i < C::NB)
+        xl[((size_t)buf * C::NB + wave * C::NBW + i) * 64 + lane] = sx[i];
   };
   u32x4 wr[kUnit][T];
   stage_load(step0);
@@ -161,25 +165,30 @@ __device__ __forceinline__ float swiglu(float g32, float u32) {
 }
 
 // ------------------------------------------------------------------------------- projection
-// EPI 0: write split partials P[s][r][n].  EPI 1: gate/up pair (T = 2: the
-// gate and the up tile of the same 16 features, one split), write
-// float(silu(gate) * up) as packed hi/lo planes of width N.
-template <int RT, int T, int XS, int EPI>
-__global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
-  constexpr int KC = chunk_steps<RT>();
-  using C = CoreShape<RT, T, XS, KC>;
+// R > 16: at most 256 workgroups of eight waves per launch.  Units are tile
+// pairs (EPI 0: tiles 2u, 2u + 1; EPI 1: gate and up tile u).  Workgroup b
+// takes split s = b / cols and the units [w P / cols, (w + 1) P / cols) of it
+// (w = b % cols), one unit per wave, so every CU streams the same number of
+// units +-1 whatever the tile count (1088 gate/up pairs become 4 or 5 per CU,
+// where whole 4-pair workgroups leave 16 CUs with twice the work).  Waves
+// without a unit only help stage X; their weight reads all hit one fragment.
+template <int RT, int XS, int EPI>
+__global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
+  constexpr int KC = chunk_steps<RT>(), T = 2, NW = 8;
+  using C = CoreShape<RT, T, XS, KC, NW>;
   __shared__ u32x4 xl[2 * C::NB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = blockIdx.x % p.cols, s = blockIdx.x / p.cols;
+  const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
+  const int unit = (int)((long long)w * p.units / p.cols) + wave;
+  const bool active = unit < (int)((long long)(w + 1) * p.units / p.cols);
   const int KS = p.K >> 5, U = p.K >> 8;
   const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
-  const int blk = col * 4 + wave;
   int tile[T];
   const bf16_t* wp[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) {
-    tile[j] = EPI == 1 ? blk : blk * T + j;
-    const int tc = min(tile[j], p.tiles - 1);   // past the last tile: re-read a valid one, never stored
+    tile[j] = EPI == 1 ? unit : unit * 2 + j;
+    const int tc = active ? min(tile[j], p.tiles - 1) : 0;
     const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
     wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
   }
@@ -188,9 +197,10 @@ __global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
   for (int j = 0; j < T; ++j)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core<RT, T, XS, KC>(wp, 512, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
-  // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
+  proj_core<RT, T, XS, KC, NW>(wp, active ? 512 : 0, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
+  if (!active) return;
   const int r16 = lane & 15, kq = lane >> 4;
+  // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
   if constexpr (EPI == 0) {
     const bool vec = (p.N & 3) == 0;
 #pragma unroll
@@ -212,20 +222,14 @@ __global__ __launch_bounds__(256, 2) void k_proj(ProjParams p) {
   } else {
     if (tile[0] >= p.tiles) return;
     const int nf = tile[0] * 16 + 4 * kq;
-    const int KSy = p.N >> 5;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int r = t * 16 + r16;
-      if (r >= p.R) continue;
-      uint32_t hi[2], lo[2];
+      if (r >= p.R || nf + 4 > p.N) continue;
+      float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; e += 2)
-        split2(swiglu(acc[0][t][e], acc[1][t][e]), swiglu(acc[0][t][e + 1], acc[1][t][e + 1]), hi[e / 2], lo[e / 2]);
-      if (nf + 4 <= p.N) {   // four consecutive k of one row: 8 contiguous bytes per plane
-        const size_t o = frag_off(r, nf, KSy);
-        *reinterpret_cast<u32x2*>(p.Y + o) = u32x2{hi[0], hi[1]};
-        *reinterpret_cast<u32x2*>(p.Y + p.yplane + o) = u32x2{lo[0], lo[1]};
-      }
+      for (int e = 0; e < 4; ++e) v[e] = swiglu(acc[0][t][e], acc[1][t][e]);
+      st_out4(p.Y, p.yplane, r, nf, p.N, v);
     }
   }
 }
@@ -278,7 +282,14 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
 }
 
 // Feature tiles per wave: two once the activation tiles make LDS reads dominate.
-int proj_tiles_per_wave(int R) { return R > 32 ? 2 : 1; }
+
+// Workgroups per split of the balanced launch (at most 256 per launch, at most
+// eight units each); the split count is the host's, a function of the shape.
+static int bal_cols(int units, int S) {
+  int cols = std::min(256 / S, units);
+  if ((units + cols - 1) / cols > 8) cols = (units + 7) / 8;
+  return std::max(cols, 1);
+}
 
 int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
   ProjParams p = p0;
@@ -292,24 +303,22 @@ int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
     else hipLaunchKernelGGL((k_proj_direct<2, 1, 0>), grid, block, 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const int T = swiglu ? 2 : proj_tiles_per_wave(p.R);
-  const int blocks = swiglu ? p.tiles : (p.tiles + T - 1) / T;
-  p.cols = (blocks + 3) / 4;
-  dim3 grid(p.cols * p.S), block(256);
-#define SV_P(RT_, T_, XS_, E_) hipLaunchKernelGGL((k_proj<RT_, T_, XS_, E_>), grid, block, 0, st, p)
-#define SV_P_RT(T_, XS_, E_)             \
-  switch (RT) {                          \
-    case 1: SV_P(1, T_, XS_, E_); break; \
-    case 2: SV_P(2, T_, XS_, E_); break; \
-    case 3: SV_P(3, T_, XS_, E_); break; \
-    default: SV_P(4, T_, XS_, E_); break; \
+  p.units = swiglu ? p.tiles : (p.tiles + 1) / 2;
+  p.cols = bal_cols(p.units, p.S);
+  dim3 grid(p.cols * p.S), block(512);
+#define SV_P(RT_, XS_, E_) hipLaunchKernelGGL((k_proj_bal<RT_, XS_, E_>), grid, block, 0, st, p)
+#define SV_P_RT(XS_, E_)             \
+  switch (RT) {                      \
+    case 2: SV_P(2, XS_, E_); break; \
+    case 3: SV_P(3, XS_, E_); break; \
+    default: SV_P(4, XS_, E_); break; \
   }
   if (swiglu) {
-    SV_P_RT(2, 2, 1);
+    SV_P_RT(2, 1);
   } else if (xs == 2) {
-    if (T == 2) { SV_P_RT(2, 2, 0); } else { SV_P_RT(1, 2, 0); }
+    SV_P_RT(2, 0);
   } else {
-    if (T == 2) { SV_P_RT(2, 1, 0); } else { SV_P_RT(1, 1, 0); }
+    SV_P_RT(1, 0);
   }
 #undef SV_P_RT
 #undef SV_P

@@ -7,7 +7,6 @@ namespace sv {
 
 // projections
 int launch_proj(const ProjParams& p, bool swiglu, int xs, hipStream_t st);
-int proj_tiles_per_wave(int R);
 int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st);
 
 // LM head statistics and the residual race

@@ -56,15 +56,16 @@ struct spec_model {
 
 namespace {
 
-// K splits of a bf16 projection: about 512 workgroups when every wave takes one
-// 16-feature tile (four tiles per workgroup), each split a whole number of
-// 256-wide units.  Depends on (N, K) only, so results never depend on R.
+// K splits of a bf16 projection, a function of (N, K) only so that results never
+// depend on R: the smallest power of two (at most 8, and at most one split per
+// 256-wide unit) that gives the 256-workgroup launch three or more tile pairs per
+// workgroup.  The gate/up pair is never split (its SwiGLU epilogue needs the full sums).
 int split_for(const spec_model* m, int N, int K, bool fused_pair) {
   if (!m->bf16 || fused_pair) return 1;
-  const int cols = ((N + 15) / 16 + 3) / 4;
+  const int pairs = ((N + 15) / 16 + 1) / 2;
   const int units = K / 256;
-  int S = (int)std::lround(512.0 / cols);
-  S = std::max(1, std::min(S, units));
+  int S = 1;
+  while (S < 8 && 2 * S <= units && pairs * S < 3 * 256) S *= 2;
   return S;
 }
 

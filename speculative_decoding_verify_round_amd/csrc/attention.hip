@@ -5,242 +5,378 @@
 // one pass; column j attends to the lane's committed cache and to its own
 // columns 0..j (causal among the columns of the round).
 //
-// One workgroup handles (lane, kv head, chunk of `chunk` absolute positions);
-// its four waves take consecutive quarters of the chunk.  All (k+1) x G query
-// rows of the lane/kv-head pair are processed together, so every K/V byte of
-// the lane is read once per layer.  Positions are tiled by absolute position:
-// a 16-position tile may hold committed keys (paged cache) and this round's
-// own columns (staged in the workspace) side by side, and the online softmax
-// visits tiles, waves and chunks in positional order.  A row's result is
-// therefore independent of how many columns the round carries and of whether
-// a key is still staged or already committed.
+// Split-KV: the positions of a lane are cut into chunks of `chunk` absolute
+// positions, each chunk yields a partial (O, max, sum) per query row, and the
+// combine kernel merges the partials in chunk order.  All (k+1) x G query rows
+// of a lane/kv-head pair are processed together, so every K/V byte of the lane
+// is read once per layer.  The round's own columns are staged in cache-layout
+// blocks aligned to absolute positions, so a 16-position block is either a
+// committed block of the paged cache or a staged block, and the online softmax
+// visits positions in order.  A row's result is therefore independent of how
+// many columns the round carries and of whether a key is still staged or
+// already committed.
 //
-// bf16 path (head_dim 128): the workgroup stages 64-position K and V tiles in
-// LDS (the next tile's loads are in flight while the current one is used);
-// wave w owns query tile w (16 of the lane's (k+1) x G query rows) over the
-// whole chunk.  Per 32 positions:
+// bf16 path (head_dim 128): wave w owns query tile w (16 of the lane's
+// (k+1) x G query rows).  Per 32 positions:
 //   S^T[pos][query] = K . Q^T with v_mfma_f32_16x16x32_bf16 (K rows = A; the
 //   float32 queries = B, as bf16 hi + lo planes);
 //   P = exp2(S * log2(e)/sqrt(d) - m) in fp32, split into bf16 hi + lo;
 //   O^T[d][query] += V^T . P^T.  The V pool is stored d-major inside a block
-//   ([d][16 slots]) so that V^T tiles are contiguous; the lane's key order
-//   inside the K = 32 MFMA step equals the order in which the S^T result left
-//   it, so P needs no shuffle.
-#include <type_traits>
-
+//   ([d][16 slots]) so that V^T rows are contiguous.
+// fp32 path: one workgroup per chunk, its four waves take consecutive quarters.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
+constexpr int kAttnStages = 4;       // LDS ring depth (64-position stages) of the bf16 kernel
+constexpr int kAttnWgBlocks = 2048;  // most cache blocks one workgroup's chunk range may span
+
+// 16 bytes per lane straight into LDS (global_load_lds_dwordx4, non-temporal: the
+// cache is streamed once per layer): lane t of the wave reads base + voff and writes
+// bytes [16 t, 16 t + 16) of the 1 KB LDS segment at the wave-uniform `seg`.  (The
+// instruction's immediate offset would move the LDS destination too, so it is 0.)
+// Issued as inline assembly so that the compiler, which cannot tell the ring's slots
+// apart, does not drain every DMA before each LDS read; completion is tracked with
+// explicit vmcnt waits instead.  The low 32 bits of a flat LDS address are its LDS
+// offset; M0 carries it (one wait state before the load).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* seg) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)seg);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding, and
+// for all LDS reads; the "memory" clobber keeps the compiler from moving memory
+// accesses across it.  Vector memory operations complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4);   // lgkmcnt(0), expcnt unchecked
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt %0" ::"n"(imm) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Values of lanes i and i ^ 16 (x16), i and i ^ 32 (x32), as (lower lane, upper lane).
+__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+// max / sum over the four lanes kq = 0..3 of a query column (lanes r, r + 16, r + 32, r + 48)
+__device__ __forceinline__ float col_max(float v) {
+  float a, b;
+  pair16(v, a, b);
+  v = fmaxf(a, b);
+  pair32(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float col_sum(float v) {
+  float a, b;
+  pair16(v, a, b);
+  v = a + b;
+  pair32(v, a, b);
+  return a + b;
+}
+
+// bf16 verify attention, one workgroup per (chunk range, kv head, lane).  The
+// workgroup streams its range of chunks as 64-position stages through a
+// kAttnStages-deep LDS ring filled by DMA (three stages in flight while one is
+// consumed) and writes a partial at every chunk end, so a row's result depends
+// only on the fixed chunk grid.
+//
+// Work split of a stage (all QT query tiles at once): wave w computes S^T for
+// positions 16 w .. 16 w + 15 and O^T for d rows 32 w .. 32 w + 31.  Each wave DMAs
+// exactly the K rows and V^T rows it reads, so the ring needs no workgroup barrier;
+// two small LDS exchanges per stage (the row maxima, then P) keep the online
+// softmax exact: every wave applies the same running max.
+//
+// LDS stage: K [64 positions][256 B] with 16-byte chunk c of position p stored at
+// chunk c ^ (p & 7); V^T block-major [4 blocks][128 d][32 B] with the two 16-byte
+// halves of row d swapped when d & 4; P [tile][query m][64 positions] as bf16 hi
+// and lo planes, chunk q of row m at q ^ (m & 7).  The MFMA operand reads are free
+// of bank conflicts, and every DMA reads 1 KB from one cache block: a wave-uniform
+// block address plus per-lane offsets fixed for the whole kernel.
 template <int QT>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
-  constexpr int D = 128, STEP = 64, KP = D + 8, VP = STEP + 8, PW = kAttnPartPad + D;
-  __shared__ bf16_t Ks[STEP * KP];   // [position][d], rows padded by 16 B
-  __shared__ bf16_t Vs[D * VP];      // [d][position], rows padded by 16 B
-  __shared__ int sblk[kMaxChunk / kBlock];   // the chunk's block ids
-  const int c = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnParams p) {
+  constexpr int D = 128, STEP = 64, NS = kAttnStages, PW = kAttnPartPad + D;
+  constexpr int KBYTES = STEP * D * 2, SBYTES = 2 * KBYTES;
+  constexpr int NST = 3 * QT;    // store instructions of one chunk partial, per wave
+  __shared__ __attribute__((aligned(1024))) char ring[NS * SBYTES];
+  __shared__ __attribute__((aligned(16))) char pex[2][QT][16][128];   // P hi / lo planes
+  __shared__ float mex[4][QT][16];                                    // per-wave row maxima
+  __shared__ float lex[4][QT][16];                                    // per-wave row sums at chunk ends
+  __shared__ int sblk[kAttnWgBlocks];                                 // committed block ids of the range
+  const int x = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, kq = lane >> 4;
   const int cols = p.ri.lane_cols[l], rs = p.ri.lane_start[l];
   const int cap = p.max_blocks * kBlock;
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
-  const int pos0 = c * p.chunk;
-  if (pos0 >= end) return;
-  const int Mq = cols * p.G;
-  const int cend = min(pos0 + p.chunk, end);
-  const int nsteps = (cend - pos0 + STEP - 1) / STEP;
+  const int nch = (end + p.chunk - 1) / p.chunk;
+  const int c0 = x * nch / (int)gridDim.x, c1 = (x + 1) * nch / (int)gridDim.x;
+  if (c0 >= c1) return;
+  const int first = c0 * p.chunk;                                       // first position of the range
+  const int T = (min(c1 * p.chunk, end) - first + STEP - 1) / STEP;     // stages of the range
+  const int cs = p.chunk / STEP;                                        // stages per chunk
+  const int fb = first >> 4, b0 = kvl >> 4;   // blocks >= b0 come from the staged columns
   const int* bt = p.block_table + (size_t)l * p.max_blocks;
-  // block ids of the chunk, looked up once (a table entry past the lane's blocks is never used)
-  for (int i = tid; i < p.chunk / kBlock; i += blockDim.x) {
-    const int b = pos0 / kBlock + i;
-    sblk[i] = b < p.max_blocks ? clamp_blk(bt[b], p.n_blocks) : 0;
+  const int nkv = p.nkv, Mq = cols * p.G;
+  const float scale = p.scale_log2;
+  const char* Kp = reinterpret_cast<const char*>(p.kpool);
+  const char* Vp = reinterpret_cast<const char*>(p.vpool);
+  const char* SK = reinterpret_cast<const char*>(p.sk);
+  const char* SV = reinterpret_cast<const char*>(p.sv);
+  constexpr int BLOCK_BYTES = kBlock * D * 2;
+
+  // byte offset of absolute block b (head g) in its pool or in the staged blocks; a
+  // block wholly past the lane's end reads staged block 0 (finite, masked)
+  auto block_off = [&](int b, int id) -> size_t {
+    const int sid = kStageBlocks * l + (16 * b < end ? b - b0 : 0);
+    return ((size_t)(b >= b0 ? sid : id) * nkv + g) * BLOCK_BYTES;
+  };
+  // per-lane DMA offsets, fixed for the kernel: K segment i (positions 4 i .. 4 i + 3 of
+  // the block, chunk c of position p read into LDS chunk c ^ (p & 7)) and V^T rows
+  // 32 wave .. +31
+  uint32_t koff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (4 * i + (lane >> 4)) * 256 + (((lane & 15) ^ ((4 * i + (lane >> 4)) & 7)) << 4);
+  const uint32_t voff = 1024 * wave + (lane >> 1) * 32 + ((((lane & 1) ^ ((lane >> 3) & 1))) << 4);
+  // ---- DMA of stage t into ring slot t % NS: this wave's K block and V^T rows, 8 instructions
+  auto issue = [&](int t) {
+    char* sK = ring + (t % NS) * SBYTES;
+    char* sV = sK + KBYTES;
+    const int bb = fb + 4 * t;
+    int id[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) id[j] = __builtin_amdgcn_readfirstlane(bb + j < b0 ? sblk[bb + j - fb] : 0);
+    const int idw = wave == 0 ? id[0] : wave == 1 ? id[1] : wave == 2 ? id[2] : id[3];
+    const bool kst = bb + wave >= b0;
+    const char* kb = (kst ? SK : Kp) + block_off(bb + wave, idw);
+    char* ks = sK + 16 * wave * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(kb, koff[i], ks + 1024 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const char* vb = (bb + j >= b0 ? SV : Vp) + block_off(bb + j, id[j]);
+      dma16(vb, voff, sV + 4096 * j + 1024 * wave);
+    }
+  };
+
+  // block ids of the range and the queries (bf16 hi + lo planes, the B operands): every
+  // load is issued unconditionally from a valid address before any is used
+  constexpr int IPT = kAttnWgBlocks / 256;
+  const int ncommit = min(4 * T, b0 - fb);
+  int idv[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int i = min(tid + 256 * k, max(ncommit - 1, 0));   // fb + i < max_blocks
+    idv[k] = bt[fb + i];
   }
-  __syncthreads();
-  const float* Qp = p.q;
-  const bf16_t* Kp = reinterpret_cast<const bf16_t*>(p.kpool);
-  const bf16_t* Vp = reinterpret_cast<const bf16_t*>(p.vpool);
-  const bf16_t* SK = reinterpret_cast<const bf16_t*>(p.sk);
-  const bf16_t* SV = reinterpret_cast<const bf16_t*>(p.sv);
-  const int nkv = p.nkv;
-
-  // ---- cooperative staging of one 64-position step: 4 K items and 4 V items of 16 B per thread
-  u32x4 kreg[1][4], vreg[1][4];
-  // Every load is issued unconditionally from a valid address (a position past the
-  // lane's live range reads a clamped one and is zeroed), so the loads carry no
-  // divergent branches; only the block that straddles the cached/staged boundary
-  // takes the (workgroup-uniform) element-wise V path.
-  auto load_step = [&](int s, auto set_tag) {
-    constexpr int B = decltype(set_tag)::value;
-    const int base = pos0 + s * STEP;
+  f32x4 qraw[QT][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pos = base + (tid >> 4) + 16 * j, seg = tid & 15;
-      const int srow = min(max(pos - kvl, 0), cols - 1);
-      const bf16_t* kc = Kp + (((size_t)sblk[(pos - pos0) >> 4] * nkv + g) * kBlock + (pos & 15)) * D;
-      const bf16_t* ks = SK + ((size_t)(rs + srow) * nkv + g) * D;
-      const u32x4 v = *reinterpret_cast<const u32x4*>((pos < kvl ? kc : ks) + seg * 8);
-      kreg[B][j] = pos < end ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bpos = base + 16 * j, d = tid >> 1, hf = tid & 1;
-      const int blk = sblk[(bpos - pos0) >> 4];
-      const bf16_t* vb = Vp + (((size_t)blk * nkv + g) * D + d) * kBlock;
-      if (bpos + 16 <= kvl) {
-        vreg[B][j] = *reinterpret_cast<const u32x4*>(vb + hf * 8);
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          uint32_t two = 0;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int pos = bpos + hf * 8 + 2 * e2 + hh;
-            const int srow = min(max(pos - kvl, 0), cols - 1);
-            const bf16_t vc = vb[pos & 15];
-            const bf16_t vs = SV[((size_t)(rs + srow) * nkv + g) * D + d];
-            const bf16_t v = pos < kvl ? vc : (pos < end ? vs : (bf16_t)0);
-            two |= (uint32_t)v << (16 * hh);
-          }
-          w[e2] = two;
-        }
-        vreg[B][j] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-  };
-  auto store_step = [&](auto set_tag) {
-    constexpr int B = decltype(set_tag)::value;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * j) * KP + (tid & 15) * 8) = kreg[B][j];
-      *reinterpret_cast<u32x4*>(Vs + (tid >> 1) * VP + 16 * j + (tid & 1) * 8) = vreg[B][j];
-    }
-  };
-
-  // ---- this wave's query tile: rows m = wave*16 + r16 (column j = m / G, head g*G + m % G)
-  const bool owner = wave < QT && wave * 16 < Mq;
-  const int m = wave * 16 + r16;
-  u32x4 qh[4], ql[4];            // the float32 query as bf16 hi + lo planes
-  int lim = -1;
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds) { qh[ds] = u32x4{0u, 0u, 0u, 0u}; ql[ds] = qh[ds]; }
-  if (owner && m < Mq) {
+  for (int qt = 0; qt < QT; ++qt) {
+    const int m = min(qt * 16 + r16, Mq - 1);
     const int j = m / p.G, hh = m - j * p.G;
-    const float* ptr = Qp + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
+    const float* ptr = p.q + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
+      qraw[qt][2 * ds] = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
+      qraw[qt][2 * ds + 1] = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < IPT; ++k)
+    if (tid + 256 * k < ncommit) sblk[tid + 256 * k] = clamp_blk(idv[k], p.n_blocks);
+  u32x4 qh[QT][4], ql[QT][4];
+  int lim[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int m = qt * 16 + r16;
+    const bool valid = m < Mq;
+    lim[qt] = valid ? kvl + m / p.G : -1;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const f32x4 a = qraw[qt][2 * ds], b = qraw[qt][2 * ds + 1];
       const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t hw, lw;
         split2(v[2 * i], v[2 * i + 1], hw, lw);
-        qh[ds][i] = hw;
-        ql[ds][i] = lw;
+        qh[qt][ds][i] = valid ? hw : 0u;
+        ql[qt][ds][i] = valid ? lw : 0u;
       }
     }
-    lim = kvl + j;
   }
-  float mrun = -INFINITY, lrun = 0.f;
-  f32x4 O[8];
+  // the compiler's waits for the loads above must precede the first DMA (its counts
+  // do not include the DMAs): consume every query register here
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) asm volatile("" ::"v"(qh[qt][ds]), "v"(ql[qt][ds]));
+  wg_barrier();   // block ids staged
+  for (int t = 0; t < NS - 1 && t < T; ++t) issue(t);
 
-  // One 64-position step: S^T for the four 16-position tiles, one online-softmax
-  // update (max, rescale, exp) for all 64 positions, then O^T += V^T P^T over
-  // two 32-position MFMA steps.
-  auto compute_step = [&](int s) {
-    const int p0 = pos0 + s * STEP;
-    f32x4 sc[4];
+  // running max (raw score units), this lane's part of the row sum, O^T of the wave's d rows
+  float mrun[QT], lrun[QT];
+  f32x4 O[QT][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16_t* kr = Ks + (st * 16 + r16) * KP + kq * 8;
-      sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qt = 0; qt < QT; ++qt) {
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+    O[qt][0] = O[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int t) {
+    const char* sK = ring + (t % NS) * SBYTES;
+    const char* sV = sK + KBYTES;
+    const int p0 = first + STEP * t + 16 * wave;   // this wave's positions p0 + 4 kq + e
+    // S^T[pos][m] for the wave's 16 positions, every query tile (K fragments read once)
+    u32x4 kf[4];
+    {
+      const char* kr = sK + (16 * wave + r16) * 256;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + ds * 32);
-        sc[st] = mfma_bf16(kf, ql[ds], sc[st]);
-        sc[st] = mfma_bf16(kf, qh[ds], sc[st]);
-      }
+      for (int ds = 0; ds < 4; ++ds) kf[ds] = *reinterpret_cast<const u32x4*>(kr + (((4 * ds + kq) ^ (r16 & 7)) << 4));
     }
-    // lane holds S^T[p0 + 16 st + 4 kq + e][query m]
-    float x[16];
-    float mx = -INFINITY;
+    f32x4 sc[QT];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int qt = 0; qt < QT; ++qt) sc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = p0 + st * 16 + 4 * kq + e;
-        const float v = pos <= lim ? sc[st][e] * p.scale_log2 : -INFINITY;
-        x[st * 4 + e] = v;
-        mx = fmaxf(mx, v);
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        sc[qt] = mfma_bf16(kf[ds], ql[qt][ds], sc[qt]);
+        sc[qt] = mfma_bf16(kf[ds], qh[qt][ds], sc[qt]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    float pr[16];
-    float alpha = 1.f;
-    if (mnew == -INFINITY) {
+    // positions past a query's own column are masked; a stage below kv_len needs none
+    if (first + STEP * t + STEP > kvl) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pr[i] = 0.f;
-    } else {
-      // arguments are <= 0: the raw v_exp_f32 (results below 2^-126 flush to 0)
-      alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
+        for (int e = 0; e < 4; ++e) sc[qt][e] = p0 + 4 * kq + e <= lim[qt] ? sc[qt][e] : -INFINITY;
     }
-    float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ps += pr[i];
-    lrun = lrun * alpha + ps;
-    mrun = mnew;
-    // P = hi + lo in bf16 (what is left is below 2^-17 P); MFMA step c covers tiles 2c and 2c + 1
-    u32x4 ph[2], pl[2];
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mx = col_max(fmaxf(fmaxf(sc[qt][0], sc[qt][1]), fmaxf(sc[qt][2], sc[qt][3])));
+      if (kq == 0) mex[wave][qt][r16] = mx;
+    }
+    wg_barrier();                          // every wave's maxima are in LDS
+    float alpha[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mnew = fmaxf(fmaxf(fmaxf(mrun[qt], mex[0][qt][r16]), fmaxf(mex[1][qt][r16], mex[2][qt][r16])),
+                               mex[3][qt][r16]);
+      float pr[4];
+      alpha[qt] = 1.f;
+      if (mnew == -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = 0.f;
+      } else {
+        // exp2(scale (s - m)) with the raw v_exp_f32: the arguments are at most a rounding
+        // of m * scale above zero, results below 2^-126 flush to 0
+        const float ms = mnew * scale;
+        alpha[qt] = __builtin_amdgcn_exp2f(fmaf(mrun[qt], scale, -ms));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(sc[qt][e], scale, -ms));
+      }
+      lrun[qt] = lrun[qt] * alpha[qt] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      mrun[qt] = mnew;
+      // P = hi + lo in bf16, row m, positions 16 wave + 4 kq .. +3 (8-position chunk q, half kq & 1)
+      uint32_t h0, l0, h1, l1;
+      split2(pr[0], pr[1], h0, l0);
+      split2(pr[2], pr[3], h1, l1);
+      const int q = 2 * wave + (kq >> 1);
+      const int off = ((q ^ (r16 & 7)) << 4) + ((kq & 1) << 3);
+      *reinterpret_cast<u32x2*>(&pex[0][qt][r16][off]) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(&pex[1][qt][r16][off]) = u32x2{l0, l1};
+    }
+    wg_barrier();                          // P of all 64 positions is in LDS
+    // O^T[d][m] += V^T[d][keys] P^T[keys][m] over two 32-position steps; the lane's keys
+    // 32 c + 8 kq .. +7 are half kq & 1 of block 2 c + kq / 2
+    u32x4 vf[2][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t hw, lw;
-        split2(pr[8 * c + 2 * i], pr[8 * c + 2 * i + 1], hw, lw);
-        ph[c][i] = hw;
-        pl[c][i] = lw;
-      }
+      for (int h = 0; h < 2; ++h)
+        vf[c][h] = *reinterpret_cast<const u32x4*>(sV + 4096 * (2 * c + (kq >> 1)) + (32 * wave + 16 * h + r16) * 32 +
+                                                   (((kq & 1) ^ ((r16 >> 2) & 1)) << 4));
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
-    // O^T[d][m] += V^T[d][keys] P^T[keys][m]; the lane's keys are (tile 2c + h, 4 kq .. 4 kq + 3)
+    for (int qt = 0; qt < QT; ++qt) {
+      O[qt][0] *= alpha[qt];
+      O[qt][1] *= alpha[qt];
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16_t* vr = Vs + (dt * 16 + r16) * VP + c * 32 + 4 * kq;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vr + 16);
-        const u32x4 vf = {a0[0], a0[1], a1[0], a1[1]};
-        O[dt] = mfma_bf16(vf, pl[c], O[dt]);
-        O[dt] = mfma_bf16(vf, ph[c], O[dt]);
+      for (int qt = 0; qt < QT; ++qt) {
+        const int off = ((4 * c + kq) ^ (r16 & 7)) << 4;
+        const u32x4 ph = *reinterpret_cast<const u32x4*>(&pex[0][qt][r16][off]);
+        const u32x4 pl = *reinterpret_cast<const u32x4*>(&pex[1][qt][r16][off]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          O[qt][h] = mfma_bf16(vf[c][h], pl, O[qt][h]);
+          O[qt][h] = mfma_bf16(vf[c][h], ph, O[qt][h]);
+        }
       }
   };
-  using I0 = std::integral_constant<int, 0>;
-  load_step(0, I0{});
-  for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();              // every wave is done reading the previous step
-    store_step(I0{});
-    __syncthreads();              // this step is staged
-    if (s + 1 < nsteps) load_step(s + 1, I0{});   // in flight during the compute below
-    if (owner) compute_step(s);
-  }
-  if (!owner) return;
-  // chunk partial of query m: lane holds O^T[d = dt*16 + 4kq + e][m]
-  float lt = lrun + __shfl_xor(lrun, 16);
-  lt += __shfl_xor(lt, 32);
-  if (m >= Mq) return;
-  float* out = p.part + ((((size_t)l * nkv + g) * p.n_chunks + c) * 64 + m) * PW;
+
+  int t_store = -NS;     // iteration of the last chunk-partial stores
+  for (int t = 0; t < T; ++t) {
+    // stage t is complete once at most (stages issued after it) x 8 DMAs, plus
+    // chunk-partial stores issued after it, are outstanding
+    const int after = min(T, t + NS - 1) - (t + 1);
+    if (t - t_store <= NS - 1) {
+      if (after >= 2) wait_vm<16 + NST>();
+      else if (after == 1) wait_vm<8 + NST>();
+      else wait_vm<NST>();
+    } else {
+      if (after >= 2) wait_vm<16>();
+      else if (after == 1) wait_vm<8>();
+      else wait_vm<0>();
+    }
+    if (t + NS - 1 < T) issue(t + NS - 1);   // into the slot stage t - 1 used
+    compute(t);
+    if (t % cs == cs - 1 || t == T - 1) {
+      // chunk partial: the wave's row sums, then O rows 32 wave .. 32 wave + 31, m and l
+      const int c = c0 + t / cs;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * kq) = O[dt];
-  if (kq == 0) { out[D] = mrun; out[D + 1] = lt; }
+      for (int qt = 0; qt < QT; ++qt) {
+        const float lw = col_sum(lrun[qt]);
+        if (kq == 0) lex[wave][qt][r16] = lw;
+      }
+      wg_barrier();
+      float* slot = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float lt = ((lex[0][qt][r16] + lex[1][qt][r16]) + lex[2][qt][r16]) + lex[3][qt][r16];
+        const int m = qt * 16 + r16;
+        // rows past the lane's queries are skipped; row 16 qt is always written (never
+        // read when invalid) so that every store instruction has an active lane
+        if (m < Mq || r16 == 0) {
+          *reinterpret_cast<f32x4*>(slot + part_index(m, 32 * wave + 4 * kq)) = O[qt][0];
+          *reinterpret_cast<f32x4*>(slot + part_index(m, 32 * wave + 16 + 4 * kq)) = O[qt][1];
+          *reinterpret_cast<f32x4*>(slot + part_index(m, D)) = f32x4{mrun[qt] * scale, lt, 0.f, 0.f};
+        }
+        mrun[qt] = -INFINITY;
+        lrun[qt] = 0.f;
+        O[qt][0] = O[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      t_store = t;
+    }
+  }
 }
 
 // fp32 model: VALU, one query row at a time per wave, 64 positions per step (lane = position).
@@ -278,7 +414,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
       if (valid) {
         const float* kr;
         if (pos < kvl) kr = Kp + (((size_t)clamp_blk(bt[pos >> 4], p.n_blocks) * nkv + g) * kBlock + (pos & 15)) * D;
-        else kr = SK + ((size_t)(rs + pos - kvl) * nkv + g) * D;
+        else kr = SK + (((size_t)(kStageBlocks * l + (pos >> 4) - (kvl >> 4)) * nkv + g) * kBlock + (pos & 15)) * D;
         double a = 0.0;
         for (int i = 0; i < D; ++i) a += (double)q[i] * (double)kr[i];
         s = (float)(a * p.scale_log2);
@@ -297,17 +433,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
       for (int t = 0; t < nval; ++t) {
         const double pt = __shfl(pr, t);
         const int vp = p0 + t;
-        const float* vrow;
-        size_t stride;
-        if (vp < kvl) {
-          vrow = Vp + ((size_t)clamp_blk(bt[vp >> 4], p.n_blocks) * nkv + g) * D * kBlock + (vp & 15);
-          stride = kBlock;
-        } else {
-          vrow = SV + ((size_t)(rs + vp - kvl) * nkv + g) * D;
-          stride = 1;
-        }
-        if (lane < D) o0 += pt * (double)vrow[(size_t)lane * stride];
-        if (lane + 64 < D) o1 += pt * (double)vrow[(size_t)(lane + 64) * stride];
+        const float* vrow =
+            vp < kvl ? Vp + ((size_t)clamp_blk(bt[vp >> 4], p.n_blocks) * nkv + g) * D * kBlock + (vp & 15)
+                     : SV + ((size_t)(kStageBlocks * l + (vp >> 4) - (kvl >> 4)) * nkv + g) * D * kBlock + (vp & 15);
+        if (lane < D) o0 += pt * (double)vrow[(size_t)lane * kBlock];
+        if (lane + 64 < D) o1 += pt * (double)vrow[(size_t)(lane + 64) * kBlock];
       }
       mr = mnew;
     }
@@ -333,14 +463,31 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         }
       }
     }
-    out[(size_t)m * PW + dd] = (float)Oc;
-    if (dd == 0) { out[(size_t)m * PW + D] = M; out[(size_t)m * PW + D + 1] = (float)Lc; }
+    out[part_index(m, dd)] = (float)Oc;
+    if (dd == 0) { out[part_index(m, D)] = M; out[part_index(m, D + 1)] = (float)Lc; }
   }
 }
 
+// Workgroups per (lane, kv head) of the bf16 kernel: the count that minimises
+// (launch waves of one workgroup per CU) x (chunks per workgroup + the ring's fill,
+// about 3/4 of a chunk), within the block-id capacity of a workgroup.
+static int attn_ranges(const AttnParams& p) {
+  const long pairs = (long)p.nkv * p.ri.L;
+  int best = p.n_chunks;
+  long best_cost = -1;
+  for (int gx = 1; gx <= p.n_chunks; ++gx) {
+    const long per = (p.n_chunks + gx - 1) / gx;
+    if (per * (p.chunk / kBlock) > kAttnWgBlocks) continue;
+    const long cost = (pairs * gx + kCUs - 1) / kCUs * (4 * per + 3);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = gx; }
+  }
+  return best;
+}
+
 int launch_attention(const AttnParams& p, bool bf16, hipStream_t st) {
-  dim3 grid(p.n_chunks, p.nkv, p.ri.L), block(256);
+  dim3 block(256);
   if (bf16) {
+    dim3 grid(attn_ranges(p), p.nkv, p.ri.L);
     int maxMq = 0;
     for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
     const int QT = (maxMq + 15) / 16;
@@ -354,7 +501,7 @@ int launch_attention(const AttnParams& p, bool bf16, hipStream_t st) {
     int maxMq = 0;
     for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
     const size_t lds = (size_t)4 * maxMq * (p.d + kAttnPartPad) * sizeof(float);
-    hipLaunchKernelGGL(k_attn_f32, grid, block, lds, st, p);
+    hipLaunchKernelGGL(k_attn_f32, dim3(p.n_chunks, p.nkv, p.ri.L), block, lds, st, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -377,13 +524,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
   const int nch = min((end + p.chunk - 1) / p.chunk, p.n_chunks);
-  const float* base = p.part + (((size_t)l * p.nkv + g) * p.n_chunks * 64 + m) * PW;
+  const float* base = p.part + ((size_t)l * p.nkv + g) * p.n_chunks * 64 * PW;
   const size_t cstride = (size_t)64 * PW;
+  const size_t io = part_index(m, 4 * dq), im = part_index(m, D);
   float M = -INFINITY;
   for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
     float mv[kCombineBatch];
 #pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i) mv[i] = base[min(c0 + i, nch - 1) * cstride + D];
+    for (int i = 0; i < kCombineBatch; ++i) mv[i] = base[min(c0 + i, nch - 1) * cstride + im];
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) M = fmaxf(M, mv[i]);
   }
@@ -395,9 +543,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
     for (int i = 0; i < kCombineBatch; ++i) {
       const int c = min(c0 + i, nch - 1);
       const float* src = base + c * cstride;
-      ov[i] = *reinterpret_cast<const f32x4*>(src + 4 * dq);
-      mv[i] = src[D];
-      lv[i] = src[D + 1];
+      ov[i] = *reinterpret_cast<const f32x4*>(src + io);
+      mv[i] = src[im];
+      lv[i] = src[im + 1];
     }
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {

@@ -12,6 +12,13 @@ constexpr int kBlock = 16;       // tokens per paged-KV block
 constexpr int kWave = 64;
 constexpr int kMaxChunk = 4096;     // largest split-KV attention chunk (positions)
 constexpr int kAttnPartPad = 4;     // a chunk partial row: O[d], then m and l, then 2 pad floats
+constexpr int kCUs = 256;           // compute units of an MI355X (workgroup slots of one-per-CU launches)
+// The round's own K/V columns are staged per lane in kStageBlocks cache-layout blocks
+// aligned to absolute positions: staged block v of lane l covers positions
+// 16 (kv_len / 16 + v) .. +15.  Slots before kv_len hold a copy of the committed
+// prefix of that block, slots after the lane's last column hold zeros (V) or are
+// unused (K); ceil((15 + kMaxCols) / 16) = 2 blocks hold any lane.
+constexpr int kStageBlocks = 2;
 
 typedef uint16_t bf16_t;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -276,10 +283,27 @@ struct RaceParams {
   RowInfo ri;
 };
 
+// Where the QKV epilogue stages a round's own K/V columns from: the lanes' cache
+// lengths and the committed prefix of each lane's first staged block (layer slices).
+struct KvStage {
+  const int32_t* kv_len;
+  const int32_t* block_table;   // [L][max_blocks]
+  int max_blocks, n_blocks;
+  const void* kpool;            // [n_blocks][nkv][16][d]
+  const void* vpool;            // [n_blocks][nkv][d][16]
+};
+
+// Float index of (query row m, column f) in a chunk partial slot: four-float granules,
+// granule-major over the slot's 64 rows, so a wave's 16-byte stores of 16 consecutive
+// rows are 256 contiguous bytes.  Columns d .. d + 1 hold the row's max and sum.
+__host__ __device__ __forceinline__ size_t part_index(int m, int f) {
+  return ((size_t)(f >> 2) * 64 + m) * 4 + (f & 3);
+}
+
 struct AttnParams {
   const float* q;         // [R][nq][d] float32 queries
-  const void* sk;         // staged K [R][nkv][d]
-  const void* sv;         // staged V [R][nkv][d]
+  const void* sk;         // staged K [L][kStageBlocks][nkv][16][d] (cache block layout)
+  const void* sv;         // staged V [L][kStageBlocks][nkv][d][16]
   const void* kpool;      // layer slice [n_blocks][nkv][16][d]
   const void* vpool;      // layer slice [n_blocks][nkv][d][16]
   const int32_t* block_table;
@@ -287,9 +311,9 @@ struct AttnParams {
   const int32_t* kv_len;
   int nq, nkv, G, d;
   int chunk;              // positions per workgroup chunk
-  int n_chunks;           // chunks per lane (grid x)
+  int n_chunks;           // chunks per lane (partial slots)
   float scale_log2;       // log2(e) / sqrt(d)
-  float* part;            // [L][nkv][n_chunks][64][d + kAttnPartPad]
+  float* part;            // [L][nkv][n_chunks] slots of 64 rows x (d + kAttnPartPad) floats, part_index order
   RowInfo ri;
 };
 

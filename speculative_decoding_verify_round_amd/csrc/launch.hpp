@@ -32,7 +32,7 @@ int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, co
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
                       const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
-                    float* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st);
+                    float* q, void* sk, void* sv, const KvStage& ks, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state, int n_gdn, int gi,
                       float* stage, void* o, const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg, int dg, const float* stage,

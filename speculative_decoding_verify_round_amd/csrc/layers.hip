@@ -160,10 +160,15 @@ int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain,
 // workgroup per row; a thread takes four consecutive pairs of a q or k head, or four
 // consecutive v elements, and loads all splits before summing them.
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S, int R, const double* rope,
+__global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S, RowInfo ri, const double* rope,
                                                            int use_rope, int nq, int nkv, int d, float* q, T* sk,
-                                                           T* sv) {
-  const int r = blockIdx.x;
+                                                           T* sv, KvStage ks) {
+  const int r = blockIdx.x, R = ri.R;
+  const int l = ri.row_lane[r], j = ri.row_col[r], cols = ri.lane_cols[l];
+  const int kvl = max(0, min(ks.kv_len[l], ks.max_blocks * kBlock - cols));
+  const int pre = kvl & 15, slot = pre + j;   // column j sits at position kvl + j: staged block slot / 16
+  const size_t sb = (size_t)kStageBlocks * l + (slot >> 4);
+  const int sl = slot & 15;
   const int N = (nq + 2 * nkv) * d, half = d / 2;
   const size_t sstride = (size_t)R * N;
   const float* Pr = P + (size_t)r * N;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S,
         *reinterpret_cast<f32x4*>(dst + i0) = f32x4{ra[0], ra[1], ra[2], ra[3]};
         *reinterpret_cast<f32x4*>(dst + i0 + half) = f32x4{rb[0], rb[1], rb[2], rb[3]};
       } else {
-        T* dst = sk + ((size_t)r * nkv + (hd - nq)) * d;     // staged for the cache
+        T* dst = sk + ((sb * nkv + (hd - nq)) * kBlock + sl) * d;     // staged for the cache
 #pragma unroll
         for (int e = 0; e < 4; ++e) { st_act(dst + i0 + e, ra[e]); st_act(dst + i0 + half + e, rb[e]); }
       }
@@ -201,19 +206,48 @@ __global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S,
       double v[4];
       sum_splits4(Pr + (nq + nkv) * d + i0, sstride, S, v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st_act(sv + (size_t)r * nkv * d + i0 + e, (float)(double)(float)v[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int g = (i0 + e) / d, i = i0 + e - g * d;
+        st_act(sv + ((sb * nkv + g) * d + i) * kBlock + sl, (float)(double)(float)v[e]);
+      }
+    }
+  }
+  // The lane's staged slots that are not its own columns, shared out among its rows:
+  // the committed prefix of the first staged block (K and V), zeros after the last
+  // column (V; K there is masked and never combined with a zero weight).
+  const int nf = kStageBlocks * kBlock - cols;
+  const size_t EK = (size_t)pre * nkv * d, E = EK + (size_t)nf * nkv * d;
+  const size_t e0 = E * j / cols, e1 = E * (j + 1) / cols;
+  const int blk = clamp_blk(ks.block_table[(size_t)l * ks.max_blocks + (kvl >> 4)], ks.n_blocks);
+  const T* Kc = reinterpret_cast<const T*>(ks.kpool);
+  const T* Vc = reinterpret_cast<const T*>(ks.vpool);
+  const size_t sb0 = (size_t)kStageBlocks * l;
+  for (size_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+    if (e < EK) {   // (g, slot < pre, i)
+      const int i = (int)(e % d);
+      const size_t gs = e / d;
+      const int sp = (int)(gs % pre), g = (int)(gs / pre);
+      sk[((sb0 * nkv + g) * kBlock + sp) * d + i] = Kc[(((size_t)blk * nkv + g) * kBlock + sp) * d + i];
+    } else {        // (g, i, filler slot)
+      const size_t e2 = e - EK;
+      const int s2 = (int)(e2 % nf);
+      const size_t gi = e2 / nf;
+      const int i = (int)(gi % d), g = (int)(gi / d);
+      const int sp = s2 < pre ? s2 : s2 + cols;   // slot of the lane's staged blocks, 0 .. 31
+      const T v = sp < pre ? Vc[(((size_t)blk * nkv + g) * d + i) * kBlock + sp] : T(0);
+      sv[(((sb0 + (sp >> 4)) * nkv + g) * d + i) * kBlock + (sp & 15)] = v;
     }
   }
 }
 
 int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
-                    float* q, void* sk, void* sv, const RowInfo& ri, bool bf16, hipStream_t st) {
+                    float* q, void* sk, void* sv, const KvStage& ks, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
-                       q, reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv));
+    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
+                       q, reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv), ks);
   else
-    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, rope, use_rope, nq, nkv, d,
-                       q, reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv));
+    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
+                       q, reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv), ks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -346,7 +380,8 @@ int launch_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg,
 }
 
 // ------------------------------------------------------------------------------- KV compaction
-// Staged K/V of columns 0 .. c-1 -> paged cache at positions kv_len .. kv_len + c - 1.
+// Staged K/V of columns 0 .. c-1 (staged block slots kv_len % 16 + j) -> paged cache at
+// positions kv_len .. kv_len + c - 1.
 // K blocks are [slot][d], V blocks are [d][slot].
 template <typename T>
 __global__ __launch_bounds__(256) void k_commit_kv(const int32_t* committed, const int32_t* kv_len,
@@ -354,7 +389,7 @@ __global__ __launch_bounds__(256) void k_commit_kv(const int32_t* committed, con
                                                     T* kpool, T* vpool, int nkv, int d, const T* sk, const T* sv,
                                                     size_t stage_layer_elems, RowInfo ri) {
   const int l = blockIdx.x, li = blockIdx.y;
-  const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
+  const int cols = ri.lane_cols[l];
   const int c = max(1, min(committed[l], cols));
   const int cap = max_blocks * kBlock;
   const int kvl = max(0, min(kv_len[l], cap - cols));
@@ -369,9 +404,10 @@ __global__ __launch_bounds__(256) void k_commit_kv(const int32_t* committed, con
     const int g = rem / d, dd = rem - g * d;
     const int pos = kvl + j;
     const int blk = clamp_blk(block_table[(size_t)l * max_blocks + (pos >> 4)], n_blocks);
-    const size_t src = ((size_t)(rs + j) * nkv + g) * d + dd;
-    kp[(((size_t)blk * nkv + g) * kBlock + (pos & 15)) * d + dd] = skl[src];
-    vp[(((size_t)blk * nkv + g) * d + dd) * kBlock + (pos & 15)] = svl[src];
+    const int slot = (kvl & 15) + j;
+    const size_t sb = (size_t)kStageBlocks * l + (slot >> 4);
+    kp[(((size_t)blk * nkv + g) * kBlock + (pos & 15)) * d + dd] = skl[((sb * nkv + g) * kBlock + (slot & 15)) * d + dd];
+    vp[(((size_t)blk * nkv + g) * d + dd) * kBlock + (pos & 15)] = svl[((sb * nkv + g) * d + dd) * kBlock + (slot & 15)];
   }
 }
 

@@ -108,7 +108,7 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.o = take(R16 * std::max(qdim, gdim) * 4);
   w.a = take(R16 * d.ffn * 4);
   w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 8);
-  w.stage_layer_elems = (size_t)R * d.n_kv_heads * d.head_dim;
+  w.stage_layer_elems = (size_t)L * sv::kStageBlocks * SPEC_KV_BLOCK * d.n_kv_heads * d.head_dim;
   w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
   w.stv = take((size_t)m->n_attn * w.stage_layer_elems * ab);
   w.gst_layer_floats = (size_t)R * d.gdn_heads * (2 * 128 + 2);
@@ -283,11 +283,13 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       void* sk = at<char>(ws, w.stk) + (size_t)L.attn_index * w.stage_layer_elems * ab;
       void* svp = at<char>(ws, w.stv) + (size_t)L.attn_index * w.stage_layer_elems * ab;
       float* q = at<float>(ws, w.q);
-      SV_CHECK(sv::launch_qkv_post(P, S_in, at<double>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ri, bf, st));
       sv::AttnParams ap{};
       ap.q = q; ap.sk = sk; ap.sv = svp;
       ap.kpool = reinterpret_cast<const char*>(r->k_pool) + (size_t)L.attn_index * apool;
       ap.vpool = reinterpret_cast<const char*>(r->v_pool) + (size_t)L.attn_index * apool;
+      const sv::KvStage ks{r->kv_len, r->block_table, r->max_blocks, r->n_blocks, ap.kpool, ap.vpool};
+      SV_CHECK(sv::launch_qkv_post(P, S_in, at<double>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ks, ri, bf,
+                                   st));
       ap.block_table = r->block_table; ap.max_blocks = r->max_blocks; ap.n_blocks = r->n_blocks;
       ap.kv_len = r->kv_len;
       ap.nq = nq; ap.nkv = nkv; ap.G = nq / nkv; ap.d = hd;

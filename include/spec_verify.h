@@ -119,7 +119,7 @@ typedef struct {
   float rms_eps;           /* e.g. 1e-6 */
   float rope_theta;        /* 0 = no positional encoding */
   int kv_block;            /* must be SPEC_KV_BLOCK */
-  int attn_chunk;          /* positions per split-KV chunk (multiple of 256, <= 4096); 0 = 256 */
+  int attn_chunk;          /* positions per split-KV chunk (multiple of 256, <= 4096); 0 = 512 */
   const void* embed;       /* [vocab][hidden] row-major; may be NULL for a head-only model */
   const void* lm_head;     /* [vocab][hidden]: row-major (f32) or packed (bf16) */
   const float* final_norm; /* [hidden]; may be NULL for a head-only model */
@@ -191,7 +191,8 @@ int64_t spec_workspace_bytes(const spec_model* model, int max_lanes, int max_col
  * recurrent inputs in the workspace.  Errors: SPEC_E_INVAL (lanes, cols,
  * NULL buffers, sampled without q_probs or with T <= 0), SPEC_E_RANGE
  * (kv_len_host + cols exceeds 16 * max_blocks), SPEC_E_UNSUPPORTED (recurrent
- * layers with gdn_state == NULL), SPEC_E_WORKSPACE. */
+ * layers with gdn_state == NULL; a lane whose cols x (n_q_heads / n_kv_heads)
+ * query rows exceed 64), SPEC_E_WORKSPACE. */
 int spec_verify_round(const spec_model* model, const spec_round* round, void* stream);
 
 /* The LM head and row statistics alone, on caller-given final hidden states

@@ -507,19 +507,20 @@ int launch_attention(const AttnParams& p, bool bf16, hipStream_t st) {
 }
 
 // Merge the chunk partials of each (lane, kv head) in chunk order; write o = O / L.
-// Thread = (query row m, four consecutive d); all chunk loads of a thread are
-// issued before the float64 merge, which visits the chunks in order.
-constexpr int kCombineBatch = 8;
+// Thread = (query row m, four consecutive d), rows fastest: `rp` rows (a power of two
+// covering the lane's queries) by 256 / rp four-float granules per workgroup, so a
+// chunk's granule is read as one contiguous run.  Chunk loads are issued in batches of
+// kCombineBatch before the float64 merge, which visits the chunks in order.
+constexpr int kCombineBatch = 16;
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
+__global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o, int rp) {
   const int g = blockIdx.x, l = blockIdx.y;
-  const int D = p.d, PW = D + kAttnPartPad, DQ = D >> 2;
-  const int mpw = blockDim.x / DQ;                       // query rows per workgroup
-  const int m = blockIdx.z * mpw + threadIdx.x / DQ, dq = threadIdx.x - (threadIdx.x / DQ) * DQ;
+  const int D = p.d, PW = D + kAttnPartPad;
+  const int m = threadIdx.x & (rp - 1), dq = blockIdx.z * (256 / rp) + threadIdx.x / rp;
   const int cols = p.ri.lane_cols[l], rs = p.ri.lane_start[l];
   const int Mq = cols * p.G;
-  if (threadIdx.x >= mpw * DQ || m >= Mq) return;
+  if (m >= Mq || dq >= D / 4) return;
   const int cap = p.max_blocks * kBlock;
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
@@ -527,30 +528,33 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
   const float* base = p.part + ((size_t)l * p.nkv + g) * p.n_chunks * 64 * PW;
   const size_t cstride = (size_t)64 * PW;
   const size_t io = part_index(m, 4 * dq), im = part_index(m, D);
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
-    float mv[kCombineBatch];
-#pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i) mv[i] = base[min(c0 + i, nch - 1) * cstride + im];
-#pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i) M = fmaxf(M, mv[i]);
-  }
-  double Oc[4] = {0.0, 0.0, 0.0, 0.0}, Lc = 0.0;
+  // one pass in chunk order with a running max M: acc = sum_c O_c 2^(m_c - M), rescaled
+  // (in float64) whenever M grows
+  double M = -INFINITY, Oc[4] = {0.0, 0.0, 0.0, 0.0}, Lc = 0.0;
   for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
     f32x4 ov[kCombineBatch];
     float mv[kCombineBatch], lv[kCombineBatch];
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
-      const int c = min(c0 + i, nch - 1);
-      const float* src = base + c * cstride;
+      const float* src = base + (size_t)min(c0 + i, nch - 1) * cstride;
       ov[i] = *reinterpret_cast<const f32x4*>(src + io);
       mv[i] = src[im];
       lv[i] = src[im + 1];
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) bm = fmaxf(bm, mv[i]);
+    if ((double)bm > M) {
+      const double r = M == -INFINITY ? 0.0 : exp2(M - (double)bm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Oc[e] *= r;
+      Lc *= r;
+      M = bm;
+    }
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
       if (c0 + i < nch && mv[i] != -INFINITY) {
-        const double f = exp2((double)mv[i] - (double)M);
+        const double f = exp2((double)mv[i] - M);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Oc[e] += (double)ov[i][e] * f;
         Lc += (double)lv[i] * f;
@@ -568,10 +572,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o) {
 int launch_attn_combine(const AttnParams& p, void* o, bool bf16, hipStream_t st) {
   int maxMq = 0;
   for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
-  const int mpw = 256 / (p.d / 4);
-  dim3 grid(p.nkv, p.ri.L, (maxMq + mpw - 1) / mpw), block(256);
-  if (bf16) hipLaunchKernelGGL(k_attn_combine<bf16_t>, grid, block, 0, st, p, reinterpret_cast<bf16_t*>(o));
-  else hipLaunchKernelGGL(k_attn_combine<float>, grid, block, 0, st, p, reinterpret_cast<float*>(o));
+  int rp = 1;
+  while (rp < maxMq) rp *= 2;                 // maxMq <= 64
+  const int gpw = 256 / rp;                   // granules per workgroup
+  dim3 grid(p.nkv, p.ri.L, (p.d / 4 + gpw - 1) / gpw), block(256);
+  if (bf16) hipLaunchKernelGGL(k_attn_combine<bf16_t>, grid, block, 0, st, p, reinterpret_cast<bf16_t*>(o), rp);
+  else hipLaunchKernelGGL(k_attn_combine<float>, grid, block, 0, st, p, reinterpret_cast<float*>(o), rp);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

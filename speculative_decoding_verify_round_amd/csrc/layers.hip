@@ -163,7 +163,56 @@ template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S, RowInfo ri, const double* rope,
                                                            int use_rope, int nq, int nkv, int d, float* q, T* sk,
                                                            T* sv, KvStage ks) {
-  const int r = blockIdx.x, R = ri.R;
+  const int R = ri.R;
+  if ((int)blockIdx.x >= R) {
+    // The lane's staged slots that are not its own columns: the committed prefix of the
+    // first staged block (K and V) and zeros after the last column (V; K there is masked
+    // and never meets a nonzero weight).  Every load is issued (from a valid address)
+    // before the first store.
+    const int l = blockIdx.x - R, cols = ri.lane_cols[l];
+    const int kvl = max(0, min(ks.kv_len[l], ks.max_blocks * kBlock - cols));
+    const int pre = kvl & 15;
+    const int blk = clamp_blk(ks.block_table[(size_t)l * ks.max_blocks + (kvl >> 4)], ks.n_blocks);
+    const T* Kc = reinterpret_cast<const T*>(ks.kpool);
+    const T* Vc = reinterpret_cast<const T*>(ks.vpool);
+    const size_t sb0 = (size_t)kStageBlocks * l;
+    constexpr int E = 16 / sizeof(T);            // elements per 16-byte chunk
+    typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));
+    // K prefix: thread = (head, slot < 16, 16-byte chunk of the d row)
+    const int kchunks = nkv * kBlock * (d / E);
+    for (int it = threadIdx.x; it < kchunks; it += blockDim.x) {
+      const int c = it % (d / E), gs = it / (d / E), sp = gs % kBlock, g = gs / kBlock;
+      const size_t o = ((size_t)g * kBlock + sp) * d + c * E;
+      const chunk_t v = *reinterpret_cast<const chunk_t*>(Kc + (size_t)blk * nkv * kBlock * d + o);
+      if (sp < pre) *reinterpret_cast<chunk_t*>(sk + sb0 * nkv * kBlock * d + o) = v;
+    }
+    // V rows: thread = (head, d); slots [0, pre) from the cache, [pre + cols, 32) zero,
+    // written in whole 16-byte groups except where a group holds own columns
+    for (int it = threadIdx.x; it < nkv * d; it += blockDim.x) {
+      const int g = it / d, i = it - g * d;
+      const T* vrow = Vc + (((size_t)blk * nkv + g) * d + i) * kBlock;
+      T row[kBlock];
+#pragma unroll
+      for (int h = 0; h < kBlock / E; ++h) *reinterpret_cast<chunk_t*>(row + h * E) = *reinterpret_cast<const chunk_t*>(vrow + h * E);
+#pragma unroll
+      for (int grp = 0; grp < kStageBlocks * kBlock / E; ++grp) {
+        const int s0 = grp * E;
+        T* dst = sv + (((sb0 + s0 / kBlock) * nkv + g) * d + i) * kBlock + (s0 % kBlock);
+        T w[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[e] = s0 + e < pre ? row[(s0 + e) % kBlock] : T(0);
+        if (s0 + E <= pre || s0 >= pre + cols) {
+          *reinterpret_cast<chunk_t*>(dst) = *reinterpret_cast<const chunk_t*>(w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (s0 + e < pre || s0 + e >= pre + cols) dst[e] = w[e];
+        }
+      }
+    }
+    return;
+  }
+  const int r = blockIdx.x;
   const int l = ri.row_lane[r], j = ri.row_col[r], cols = ri.lane_cols[l];
   const int kvl = max(0, min(ks.kv_len[l], ks.max_blocks * kBlock - cols));
   const int pre = kvl & 15, slot = pre + j;   // column j sits at position kvl + j: staged block slot / 16
@@ -205,37 +254,9 @@ __global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S,
       const int i0 = 4 * (it - nrot);
       double v[4];
       sum_splits4(Pr + (nq + nkv) * d + i0, sstride, S, v);
+      const int g = i0 / d, i = i0 - g * d;   // d % 4 == 0: the four elements share a head
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int g = (i0 + e) / d, i = i0 + e - g * d;
-        st_act(sv + ((sb * nkv + g) * d + i) * kBlock + sl, (float)(double)(float)v[e]);
-      }
-    }
-  }
-  // The lane's staged slots that are not its own columns, shared out among its rows:
-  // the committed prefix of the first staged block (K and V), zeros after the last
-  // column (V; K there is masked and never combined with a zero weight).
-  const int nf = kStageBlocks * kBlock - cols;
-  const size_t EK = (size_t)pre * nkv * d, E = EK + (size_t)nf * nkv * d;
-  const size_t e0 = E * j / cols, e1 = E * (j + 1) / cols;
-  const int blk = clamp_blk(ks.block_table[(size_t)l * ks.max_blocks + (kvl >> 4)], ks.n_blocks);
-  const T* Kc = reinterpret_cast<const T*>(ks.kpool);
-  const T* Vc = reinterpret_cast<const T*>(ks.vpool);
-  const size_t sb0 = (size_t)kStageBlocks * l;
-  for (size_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-    if (e < EK) {   // (g, slot < pre, i)
-      const int i = (int)(e % d);
-      const size_t gs = e / d;
-      const int sp = (int)(gs % pre), g = (int)(gs / pre);
-      sk[((sb0 * nkv + g) * kBlock + sp) * d + i] = Kc[(((size_t)blk * nkv + g) * kBlock + sp) * d + i];
-    } else {        // (g, i, filler slot)
-      const size_t e2 = e - EK;
-      const int s2 = (int)(e2 % nf);
-      const size_t gi = e2 / nf;
-      const int i = (int)(gi % d), g = (int)(gi / d);
-      const int sp = s2 < pre ? s2 : s2 + cols;   // slot of the lane's staged blocks, 0 .. 31
-      const T v = sp < pre ? Vc[(((size_t)blk * nkv + g) * d + i) * kBlock + sp] : T(0);
-      sv[(((sb0 + (sp >> 4)) * nkv + g) * d + i) * kBlock + (sp & 15)] = v;
+      for (int e = 0; e < 4; ++e) st_act(sv + ((sb * nkv + g) * d + i + e) * kBlock + sl, (float)(double)(float)v[e]);
     }
   }
 }
@@ -243,10 +264,10 @@ __global__ __launch_bounds__(kRowThreads) void k_qkv_post(const float* P, int S,
 int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,
                     float* q, void* sk, void* sv, const KvStage& ks, const RowInfo& ri, bool bf16, hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
+    hipLaunchKernelGGL(k_qkv_post<bf16_t>, dim3(ri.R + ri.L), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
                        q, reinterpret_cast<bf16_t*>(sk), reinterpret_cast<bf16_t*>(sv), ks);
   else
-    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
+    hipLaunchKernelGGL(k_qkv_post<float>, dim3(ri.R + ri.L), dim3(kRowThreads), 0, st, P, S, ri, rope, use_rope, nq, nkv, d,
                        q, reinterpret_cast<float*>(sk), reinterpret_cast<float*>(sv), ks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

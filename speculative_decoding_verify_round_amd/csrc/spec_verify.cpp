@@ -19,7 +19,7 @@ static_assert(sizeof(sv::LmPartial) == 32, "partial size");
 
 namespace {
 
-constexpr int kDefaultChunk = 256;
+constexpr int kDefaultChunk = 512;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -177,7 +177,7 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
         return SPEC_E_INVAL;
       const int G = m->d.n_q_heads / m->d.n_kv_heads;
       const int mq = max_cols(ri) * G;
-      if (m->bf16 && mq > 64) return SPEC_E_UNSUPPORTED;
+      if (mq > 64) return SPEC_E_UNSUPPORTED;   // a chunk partial holds 64 query rows
       if (!m->bf16 && (size_t)4 * mq * (m->d.head_dim + sv::kAttnPartPad) * 4 > 65536) return SPEC_E_UNSUPPORTED;
       if (r->kv_len_host) {
         for (int l = 0; l < r->lanes; ++l) {

@@ -50,7 +50,8 @@ FAKE = 0x1000   # never dereferenced: every call here fails validation before an
 def make_desc(**kw):
     d = B.SpecModelDesc()
     d.n_layers = kw.get("n_layers", 2)
-    d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim = kw.get("hidden", 256), 4, 2, kw.get("head_dim", 128)
+    d.hidden, d.head_dim = kw.get("hidden", 256), kw.get("head_dim", 128)
+    d.n_q_heads, d.n_kv_heads = kw.get("q_heads", 4), kw.get("kv_heads", 2)
     d.ffn, d.vocab = kw.get("ffn", 512), kw.get("vocab", 1024)
     d.dtype = kw.get("dtype", B.SPEC_BF16)
     kinds = kw.get("kinds", [B.SPEC_LAYER_ATTN] * d.n_layers)
@@ -154,6 +155,17 @@ def test_round_validation_errors(model):
     assert verify_status(model, workspace_bytes=16) == B.SPEC_E_WORKSPACE
     assert verify_status(model, workspace=None) == B.SPEC_E_WORKSPACE
     assert verify_status(model, workspace=0x100010) == B.SPEC_E_WORKSPACE        # misaligned
+
+
+def test_query_rows_per_lane_limit():
+    # a chunk partial holds 64 query rows: cols x (q heads per kv head) above 64 is refused
+    h = C.c_void_p()
+    desc = make_desc(dtype=B.SPEC_F32, head_dim=8, q_heads=32, kv_heads=2)   # 16 q heads per kv head
+    assert B.load_library().spec_model_create(C.byref(desc), C.byref(h)) == 0
+    try:
+        assert verify_status(h, cols=[5, 1]) == B.SPEC_E_UNSUPPORTED            # 80 query rows
+    finally:
+        B.spec_model_destroy(h)
 
 
 def test_other_calls_validate(model):

@@ -126,14 +126,19 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t w
 template <int T, int XS>
 __device__ __forceinline__ void proj_core_direct(const bf16_t* const (&wp)[T], size_t wstep,
                                                  const bf16_t* __restrict__ X, size_t xplane, int step0, int nu,
-                                                 f32x4 (&acc)[T]) {
+                                                 int rows, f32x4 (&acc)[T]) {
   const int lane = threadIdx.x & 63;
   const bf16_t* xp = X + (size_t)step0 * 512 + lane * 8;   // row tile 0: fragment s at s * 512
+  // lane i carries row i % 16 of an X fragment: lanes of the tile's padding rows
+  // (zeros) load nothing, so a round of R < 16 rows reads R / 16 of every fragment
+  const bool xrow = (lane & 15) < rows;
   u32x4 wr[kUnit][T], xr[kUnit][XS];
   auto load = [&](int slot, int st) {
 #pragma unroll
-    for (int pl = 0; pl < XS; ++pl)
-      xr[slot][pl] = *reinterpret_cast<const u32x4*>(xp + pl * xplane + (size_t)st * 512);
+    for (int pl = 0; pl < XS; ++pl) {
+      xr[slot][pl] = u32x4{0u, 0u, 0u, 0u};
+      if (xrow) xr[slot][pl] = *reinterpret_cast<const u32x4*>(xp + pl * xplane + (size_t)st * 512);
+    }
 #pragma unroll
     for (int j = 0; j < T; ++j) wr[slot][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)st * wstep));
   };
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
   f32x4 acc[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core_direct<T, XS>(wp, 512, p.X, p.xplane, u0 * kUnit, u1 - u0, acc);
+  proj_core_direct<T, XS>(wp, 512, p.X, p.xplane, u0 * kUnit, u1 - u0, p.R, acc);
   const int r = lane & 15, kq = lane >> 4;
   if (r >= p.R) return;
   if constexpr (EPI == 0) {

@@ -32,37 +32,6 @@ namespace sv {
 constexpr int kAttnStages = 4;       // LDS ring depth (64-position stages) of the bf16 kernel
 constexpr int kAttnWgBlocks = 2048;  // most cache blocks one workgroup's chunk range may span
 
-// 16 bytes per lane straight into LDS (global_load_lds_dwordx4, non-temporal: the
-// cache is streamed once per layer): lane t of the wave reads base + voff and writes
-// bytes [16 t, 16 t + 16) of the 1 KB LDS segment at the wave-uniform `seg`.  (The
-// instruction's immediate offset would move the LDS destination too, so it is 0.)
-// Issued as inline assembly so that the compiler, which cannot tell the ring's slots
-// apart, does not drain every DMA before each LDS read; completion is tracked with
-// explicit vmcnt waits instead.  The low 32 bits of a flat LDS address are its LDS
-// offset; M0 carries it (one wait state before the load).
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* seg) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)seg);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding, and
-// for all LDS reads; the "memory" clobber keeps the compiler from moving memory
-// accesses across it.  Vector memory operations complete in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4);   // lgkmcnt(0), expcnt unchecked
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt %0" ::"n"(imm) : "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Values of lanes i and i ^ 16 (x16), i and i ^ 32 (x32), as (lower lane, upper lane).
 __device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -168,11 +137,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnParams p) {
     const char* kb = (kst ? SK : Kp) + block_off(bb + wave, idw);
     char* ks = sK + 16 * wave * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(kb, koff[i], ks + 1024 * i);
+    for (int i = 0; i < 4; ++i) dma16<true>(kb, koff[i], ks + 1024 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const char* vb = (bb + j >= b0 ? SV : Vp) + block_off(bb + j, id[j]);
-      dma16(vb, voff, sV + 4096 * j + 1024 * wave);
+      dma16<true>(vb, voff, sV + 4096 * j + 1024 * wave);
     }
   };
 

@@ -72,6 +72,46 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 
+// ----------------------------------------------------------------------------- LDS DMA
+// 16 bytes per lane straight into LDS (global_load_lds_dwordx4): lane t of the wave
+// reads base + voff and writes bytes [16 t, 16 t + 16) of the 1 KB LDS segment at the
+// wave-uniform `seg`; NT marks data streamed once (non-temporal).  The instruction's
+// immediate offset would move the LDS destination too, so it is 0.  Issued as inline
+// assembly so that the compiler, which cannot tell LDS ring slots apart, does not
+// drain every DMA before each LDS read; completion is tracked with explicit vmcnt
+// waits (wait_vm) instead.  The low 32 bits of a flat LDS address are its LDS
+// offset; M0 carries it (one wait state before the load).
+template <bool NT>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* seg) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)seg);
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding, and
+// for all LDS reads; the "memory" clobber keeps the compiler from moving memory
+// accesses across it.  Vector memory operations complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4);   // lgkmcnt(0), expcnt unchecked
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt %0" ::"n"(imm) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses but not for its vector
+// memory loads (__syncthreads would wait for every outstanding load).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);

@@ -119,6 +119,120 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t w
   run_unit(std::false_type{}, nu - 1);
 }
 
+// R > 16, split roles: compute waves 0 .. NWC-1 stream weights and run the MFMAs;
+// the remaining kXWaves waves only copy X chunks into a kXSlots-deep LDS ring by DMA.
+// Each wave's in-order vmcnt counter then holds one kind of load: the compute waves
+// never wait for an X load behind their weights, so their weight ring can run
+// kWRing steps (two units) ahead, and the loaders keep the X ring kXSlots - 1 chunks
+// ahead.  One workgroup barrier per chunk publishes it (and frees the slot the
+// previous chunk used); it waits for LDS accesses only.
+constexpr int kXSlots = 4;
+constexpr int kXWaves = 2;
+constexpr int kWRing = 2 * kUnit;
+
+template <int RT, int T, int XS, int KC, int NWC>
+__device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, bool wactive,
+                                             const bf16_t* __restrict__ X, size_t xplane, int KS, int step0,
+                                             int nu, char* xring, f32x4 (&acc)[T][RT]) {
+  constexpr int NB = KC * RT * XS;           // 1 KB X fragments per chunk: b = (plane * RT + tile) * KC + step
+  constexpr int NC = kUnit / KC;             // chunks per unit
+  constexpr int CHUNK = NB * 1024;
+  constexpr int PER = NB / kXWaves;          // DMAs per loader wave per chunk
+  static_assert(NB % kXWaves == 0 && (NC == 1 || NC == 2), "chunk shape");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int G = nu * NC;
+  if (wave >= NWC) {
+    const int lw = wave - NWC;
+    auto issue = [&](int g) {
+      char* slot = xring + (g % kXSlots) * CHUNK;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int b = lw + kXWaves * i;
+        const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
+        const bf16_t* src = X + pl * xplane + ((size_t)t * KS + step0 + g * KC + st) * 512;
+        dma16<false>(src, lane * 16, slot + b * 1024);
+      }
+    };
+    for (int g = 0; g < kXSlots - 1 && g < G; ++g) issue(g);
+    for (int g = 0; g < G; ++g) {
+      const int after = min(G - 1, g + kXSlots - 2) - g;   // chunks issued after g
+      if (after >= 2) wait_vm<2 * PER>();
+      else if (after == 1) wait_vm<PER>();
+      else wait_vm<0>();
+      wg_barrier();                                        // chunk g is in LDS
+      if (g + kXSlots - 1 < G) issue(g + kXSlots - 1);     // into the slot chunk g - 1 used
+    }
+    return;
+  }
+  // compute waves without a unit only keep the barrier count
+  if (!wactive) {
+    for (int g = 0; g < G; ++g) wg_barrier();
+    return;
+  }
+  // weight ring over two units: slot PAR * 8 + k holds step k of a unit of parity PAR;
+  // a unit with MORE refills its slots with the unit two ahead.  The loads sit on
+  // straight-line paths, so the compiler's waits are exact (the ring stays full).
+  u32x4 wr[kWRing][T];
+  auto load = [&](int slot, int step) {
+#pragma unroll
+    for (int j = 0; j < T; ++j) wr[slot][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)step * wstep));
+  };
+  auto run_unit = [&](auto par_tag, auto more_tag, int u) {
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool MORE = decltype(more_tag)::value;
+    auto chunk = [&](auto h_tag) {
+      constexpr int h = decltype(h_tag)::value;
+      const int g = u * NC + h;
+      wg_barrier();                                        // chunk g is in LDS
+      const char* slot = xring + (g % kXSlots) * CHUNK + lane * 16;
+#pragma unroll
+      for (int st = 0; st < KC; ++st) {
+        const int k = h * KC + st;
+        u32x4 xo[XS][RT];
+#pragma unroll
+        for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            xo[pl][t] = *reinterpret_cast<const u32x4*>(slot + ((pl * RT + t) * KC + st) * 1024);
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int pl = XS - 1; pl >= 0; --pl)
+              acc[j][t] = mfma_bf16(wr[PAR * kUnit + k][j], xo[pl][t], acc[j][t]);
+        if constexpr (MORE) load(PAR * kUnit + k, (u + 2) * kUnit + k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    chunk(std::integral_constant<int, 0>{});
+    if constexpr (NC == 2) chunk(std::integral_constant<int, 1>{});
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (nu == 1) {
+#pragma unroll
+    for (int k = 0; k < kUnit; ++k) load(k, k);
+    run_unit(P0{}, std::false_type{}, 0);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kWRing; ++k) load(k, k);
+  int u = 0;
+  for (; u + 3 < nu; u += 2) {
+    run_unit(P0{}, std::true_type{}, u);
+    run_unit(P1{}, std::true_type{}, u + 1);
+  }
+  if (nu - u == 3) {
+    run_unit(P0{}, std::true_type{}, u);
+    run_unit(P1{}, std::false_type{}, u + 1);
+    run_unit(P0{}, std::false_type{}, u + 2);
+  } else {
+    run_unit(P0{}, std::false_type{}, u);
+    run_unit(P1{}, std::false_type{}, u + 1);
+  }
+}
+
 // One row tile (R <= 16), one wave per workgroup: the activation fragments are
 // read straight from memory (they stay in L2) into a ring of the same depth as
 // the weights', so the launch can carry four times as many workgroups (the
@@ -179,13 +293,12 @@ __device__ __forceinline__ float swiglu(float g32, float u32) {
 // without a unit only help stage X; their weight reads all hit one fragment.
 template <int RT, int XS, int EPI>
 __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
-  constexpr int KC = chunk_steps<RT>(), T = 2, NW = 8;
-  using C = CoreShape<RT, T, XS, KC, NW>;
-  __shared__ u32x4 xl[2 * C::NB * 64];
+  constexpr int KC = chunk_steps<RT>(), T = 2, NWC = 8 - kXWaves;
+  __shared__ __attribute__((aligned(1024))) char xring[kXSlots * KC * RT * XS * 1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
   const int unit = (int)((long long)w * p.units / p.cols) + wave;
-  const bool active = unit < (int)((long long)(w + 1) * p.units / p.cols);
+  const bool active = wave < NWC && unit < (int)((long long)(w + 1) * p.units / p.cols);
   const int KS = p.K >> 5, U = p.K >> 8;
   const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
   int tile[T];
@@ -202,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   for (int j = 0; j < T; ++j)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core<RT, T, XS, KC, NW>(wp, active ? 512 : 0, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xl, acc);
+  proj_core_xw<RT, T, XS, KC, NWC>(wp, 512, active, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xring, acc);
   if (!active) return;
   const int r16 = lane & 15, kq = lane >> 4;
   // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
@@ -291,8 +404,9 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
 // Workgroups per split of the balanced launch (at most 256 per launch, at most
 // eight units each); the split count is the host's, a function of the shape.
 static int bal_cols(int units, int S) {
-  int cols = std::min(256 / S, units);
-  if ((units + cols - 1) / cols > 8) cols = (units + 7) / 8;
+  constexpr int NWC = 8 - kXWaves;   // compute waves per workgroup
+  int cols = std::min(kCUs / S, units);
+  if ((units + cols - 1) / cols > NWC) cols = (units + NWC - 1) / NWC;
   return std::max(cols, 1);
 }
 

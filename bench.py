@@ -34,6 +34,12 @@ from speculative_decoding_verify_round_amd import binding as B  # noqa: E402
 from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel, pack_weight  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# measured HBM traffic of the gate/up kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
+# calibrated against a plain copy); reported only while that kernel's sources are unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic_dense27b.md")
+GATEUP_SOURCES = ("gemm.hip", "common.hpp")
+COPY_CALIBRATION_BYTES = 512 << 20
 METRIC = "committed tokens/s & verify rows/s at lanes×(k+1); % of HBM roofline"
 
 
@@ -74,6 +80,30 @@ def gpu_weights(cfg, seed: int):
             "w_gate": packed(base + 2, (F, H)), "w_up": packed(base + 3, (F, H)), "w_down": packed(base + 4, (H, F)),
         })
     return w
+
+
+def gateup_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GATEUP_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_verify_round_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per gate/up launch from the committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("source_hash") == gateup_source_hash():
+                        return rec
+    except OSError:
+        pass
+    return None
 
 
 def fill_pools(dc: DeviceCache, seed: int):
@@ -163,6 +193,8 @@ def main():
     ap.add_argument("--context", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--plain-steps", type=int, default=10, help="plain one-row rounds timed for comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 512 MiB (the reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; the verify round does not shard "
@@ -187,6 +219,13 @@ def main():
     dc = DeviceCache(dm, L, max_blocks, nb, block_table=bt, kv_len=[ctx] * L)
     log("KV context")
     fill_pools(dc, cfg.input_seed)
+    if args.copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if dc.gdn is not None:
         dc.gdn.normal_(0.0, 1.0 / np.sqrt(128.0))
     torch.cuda.synchronize()
@@ -272,6 +311,8 @@ def main():
     gu_avg_ms = gu_ms / max(gu_n, 1)
     gu_bytes = gate_up_bytes(cfg, R)
     gu_gbs = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
+    tr = measured_traffic()
+    traffic_bytes = int(tr["fetch_bytes"] + tr["write_bytes"]) if tr else None
     result = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -295,7 +336,7 @@ def main():
         "round_roofline_frac": round(rbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "gate/up projection (SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_bytes,
                      "avg_launch_ms": round(gu_avg_ms, 5), "launches": gu_n, "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:

@@ -192,14 +192,7 @@ int64_t spec_workspace_bytes(const spec_model* model, int max_lanes, int max_col
  * NULL buffers, sampled without q_probs or with T <= 0), SPEC_E_RANGE
  * (kv_len_host + cols exceeds 16 * max_blocks), SPEC_E_UNSUPPORTED (recurrent
  * layers with gdn_state == NULL; a lane whose cols x (n_q_heads / n_kv_heads)
- * query rows exceed 64), SPEC_E_WORKSPACE.
- * A call whose round equals the previous call's in every pointer, scalar and
- * column count captures the forward once into a HIP graph (on a private stream)
- * and from then on replays it on `stream` (device memory is read at execution
- * time, so new contents at the same addresses are fine); environment variable
- * SPEC_VERIFY_GRAPHS=0 keeps every call kernel by kernel.  Calls on one model
- * handle are serialised by a lock.  With profiling enabled the timing events are
- * part of the graph, and a replay re-records them. */
+ * query rows exceed 64), SPEC_E_WORKSPACE. */
 int spec_verify_round(const spec_model* model, const spec_round* round, void* stream);
 
 /* The LM head and row statistics alone, on caller-given final hidden states

@@ -7,9 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <new>
 #include <vector>
 
@@ -54,17 +52,6 @@ struct spec_model {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_events;
   std::vector<hipEvent_t> prof_pool;
   size_t prof_used = 0;
-  // the verify forward of the last round shape, replayed as one HIP graph: a round
-  // equal in every pointer, scalar and column count to the previous call is captured
-  // once (on a private stream) and replayed on the caller's stream afterwards
-  struct GraphCache {
-    std::mutex mu;
-    bool enabled = true;
-    std::vector<uint8_t> key, last_key;
-    hipGraphExec_t exec = nullptr;
-    hipStream_t cap = nullptr;
-  };
-  mutable GraphCache graph;
 };
 
 namespace {
@@ -403,7 +390,6 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
   m->d = d;
   m->bf16 = bf;
   m->chunk = chunk;
-  if (const char* e = std::getenv("SPEC_VERIFY_GRAPHS")) m->graph.enabled = std::strcmp(e, "0") != 0;
   if (d.n_layers > 0) {
     if (!d.layer_kind || !d.layers || !d.embed || !d.final_norm || d.ffn <= 0) { delete m; return SPEC_E_INVAL; }
     if (bf && (d.ffn % 256) != 0) { delete m; return SPEC_E_UNSUPPORTED; }
@@ -453,8 +439,6 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
 void spec_model_destroy(spec_model* m) {
   if (!m) return;
   for (hipEvent_t e : m->prof_pool) hipEventDestroy(e);
-  if (m->graph.exec) hipGraphExecDestroy(m->graph.exec);
-  if (m->graph.cap) hipStreamDestroy(m->graph.cap);
   delete m;
 }
 
@@ -466,79 +450,15 @@ int64_t spec_workspace_bytes(const spec_model* m, int max_lanes, int max_cols, i
   return (int64_t)layout(m, R, max_lanes, std::max(max_blocks, 1)).total;
 }
 
-namespace {
-// Everything of a round that reaches a kernel argument: pointers, scalars, the row layout.
-std::vector<uint8_t> round_key(const spec_round* r, int prof_class) {
-  std::vector<uint8_t> k;
-  auto put = [&](const void* p, size_t n) {
-    const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
-    k.insert(k.end(), b, b + n);
-  };
-  const void* ptrs[] = {r->tokens, r->kv_len, r->block_table, r->k_pool, r->v_pool,
-                        r->gdn_state, r->q_probs, r->workspace};
-  put(ptrs, sizeof(ptrs));
-  const int ints[] = {r->lanes, r->max_blocks, r->n_blocks, r->mode};
-  put(ints, sizeof(ints));
-  put(&r->temperature, sizeof(r->temperature));
-  put(&r->seed, sizeof(r->seed));
-  put(r->cols_host, sizeof(int32_t) * r->lanes);
-  put(&prof_class, sizeof(prof_class));
-  int dev = -1;
-  hipGetDevice(&dev);
-  put(&dev, sizeof(dev));
-  return k;
-}
-
-int verify_eager(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w,
-                 hipStream_t s) {
-  const int st = forward(m, r, ri, w, s);
-  if (st) return st;
-  return lm_stats(m, r, ri, w, s);
-}
-}  // namespace
-
 int spec_verify_round(const spec_model* m, const spec_round* r, void* stream) {
   sv::RowInfo ri;
   WsLayout w;
   int st = check_round(m, r, false, ri, w);
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto& g = m->graph;
-  if (!g.enabled) return verify_eager(m, r, ri, w, s);
-  std::lock_guard<std::mutex> lock(g.mu);
-  // a profiled round captures its timing events as event-record nodes; a replay
-  // re-records them, so the profile then holds the last replay's launches
-  std::vector<uint8_t> key = round_key(r, m->prof_class);
-  if (g.exec && key == g.key) return hipGraphLaunch(g.exec, s) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
-  if (key != g.last_key) {   // a new shape: run it as is, capture if it comes again
-    g.last_key = std::move(key);
-    return verify_eager(m, r, ri, w, s);
-  }
-  // second call in a row with this round: capture it on the private stream
-  if (!g.cap && hipStreamCreateWithFlags(&g.cap, hipStreamNonBlocking) != hipSuccess) {
-    g.cap = nullptr;
-    return verify_eager(m, r, ri, w, s);
-  }
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-  bool ok = hipStreamBeginCapture(g.cap, hipStreamCaptureModeThreadLocal) == hipSuccess;
-  if (ok) {
-    const int cst = verify_eager(m, r, ri, w, g.cap);
-    ok = hipStreamEndCapture(g.cap, &graph) == hipSuccess && cst == SPEC_OK && graph;
-  }
-  ok = ok && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
-  if (graph) hipGraphDestroy(graph);
-  (void)hipGetLastError();
-  if (!ok) {
-    if (exec) hipGraphExecDestroy(exec);
-    if (m->prof_class == SPEC_K_NONE) g.enabled = false;   // capture is not available here: stay eager
-    g.last_key.clear();
-    return verify_eager(m, r, ri, w, s);
-  }
-  if (g.exec) hipGraphExecDestroy(g.exec);
-  g.exec = exec;
-  g.key = g.last_key;
-  return hipGraphLaunch(g.exec, s) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
+  st = forward(m, r, ri, w, s);
+  if (st) return st;
+  return lm_stats(m, r, ri, w, s);
 }
 
 int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidden, void* stream) {
@@ -674,13 +594,6 @@ int spec_profile_enable(spec_model* m, int kernel_class) {
   m->prof_class = kernel_class;
   m->prof_events.clear();
   m->prof_used = 0;
-  {   // a cached graph may hold events of the pool: drop it
-    std::lock_guard<std::mutex> lock(m->graph.mu);
-    if (m->graph.exec) hipGraphExecDestroy(m->graph.exec);
-    m->graph.exec = nullptr;
-    m->graph.key.clear();
-    m->graph.last_key.clear();
-  }
   return SPEC_OK;
 }
 

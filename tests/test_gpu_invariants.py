@@ -132,34 +132,3 @@ def test_rejected_columns_leave_no_trace(dev):
     Kb = before_k[0][[int(dev.bt[0][(dev.context + 2 + j) // 16]) for j in range(4)], :,
                      [(dev.context + 2 + j) % 16 for j in range(4)], :].float().cpu().numpy()
     assert np.array_equal(K, Kb)
-
-
-def test_graph_replay_matches_eager(dev):
-    """The second identical call captures the forward into a HIP graph and later calls
-    replay it; every replay (with other rounds and torch work between them) gives the
-    first, kernel-by-kernel call's bits."""
-    toks, other = [[1, 2, 3, 4, 5], [6, 7, 8]], [[9, 10], [11, 12, 13, 14]]
-    A = dev.fresh()
-    rc = A.round(toks)
-
-    R = sum(len(t) for t in toks)
-
-    def run(r):
-        A.verify(r)
-        A.accept(r)
-        torch.cuda.synchronize()
-        c = A.committed.clone()
-        toks_out = [A.out_tokens[l, :int(c[l])].clone() for l in range(len(toks))]
-        return [A.row_stats[:R].clone().view(torch.int32), c] + toks_out
-
-    ref = run(rc)                       # eager
-    for it in range(4):                 # capture + replay, then replays
-        got = run(rc)
-        for x, y in zip(ref, got):
-            assert torch.equal(x, y), it
-        ro = A.round(other)             # a different shape in between: kernel by kernel
-        run(ro)
-        junk = torch.randn(1 << 20, device="cuda").sum()
-        torch.cuda.synchronize()
-        del junk
-    log("graph replays match the eager round bitwise")

@@ -213,7 +213,10 @@ def main():
     max_blocks = (ctx + ref_len + 32) // 16 + 1
     log(f"{cfg.name}: weights on the device")
     w = gpu_weights(cfg, cfg.weight_seed)
-    dm = DeviceModel(cfg, w, prepacked=True)
+    # split-KV chunks of 1024 positions: at 8K context that halves the chunk partials the
+    # combine merges (the chunk grid is a per-model setting; results depend on it only
+    # through the fixed order of the merge)
+    dm = DeviceModel(cfg, w, prepacked=True, attn_chunk=1024)
     del w
     bt, nb = synth.block_table(cfg, L, max_blocks)
     dc = DeviceCache(dm, L, max_blocks, nb, block_table=bt, kv_len=[ctx] * L)

@@ -24,6 +24,8 @@
 //   O^T[d][query] += V^T . P^T.  The V pool is stored d-major inside a block
 //   ([d][16 slots]) so that V^T rows are contiguous.
 // fp32 path: one workgroup per chunk, its four waves take consecutive quarters.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -438,16 +440,24 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
 }
 
 // Workgroups per (lane, kv head) of the bf16 kernel: the count that minimises
-// (launch waves of one workgroup per CU) x (chunks per workgroup + the ring's fill,
-// about 3/4 of a chunk), within the block-id capacity of a workgroup.
+// (launch waves of one workgroup per CU) x (the longest range in 64-position stages
+// at full capacity + the ring's fill, about 3 stages), within the block-id capacity of
+// a workgroup.  Ties go to fewer ranges.
 static int attn_ranges(const AttnParams& p) {
   const long pairs = (long)p.nkv * p.ri.L;
+  const long cap = (long)p.max_blocks * kBlock;
   int best = p.n_chunks;
   long best_cost = -1;
   for (int gx = 1; gx <= p.n_chunks; ++gx) {
     const long per = (p.n_chunks + gx - 1) / gx;
     if (per * (p.chunk / kBlock) > kAttnWgBlocks) continue;
-    const long cost = (pairs * gx + kCUs - 1) / kCUs * (4 * per + 3);
+    long longest = 0;
+    for (int x = 0; x < gx; ++x) {
+      const long c0 = (long)x * p.n_chunks / gx, c1 = (long)(x + 1) * p.n_chunks / gx;
+      const long pos = std::min(c1 * p.chunk, cap) - c0 * p.chunk;
+      longest = std::max(longest, (pos + 63) / 64);
+    }
+    const long cost = (pairs * gx + kCUs - 1) / kCUs * (longest + 3);
     if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = gx; }
   }
   return best;

@@ -122,13 +122,14 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t w
 // R > 16, split roles: compute waves 0 .. NWC-1 stream weights and run the MFMAs;
 // the remaining kXWaves waves only copy X chunks into a kXSlots-deep LDS ring by DMA.
 // Each wave's in-order vmcnt counter then holds one kind of load: the compute waves
-// never wait for an X load behind their weights, so their weight ring can run
-// kWRing steps (two units) ahead, and the loaders keep the X ring kXSlots - 1 chunks
+// never wait for an X load behind their weights, so their weight ring runs a whole
+// unit (eight steps) ahead, and the loaders keep the X ring kXSlots - 1 chunks
 // ahead.  One workgroup barrier per chunk publishes it (and frees the slot the
-// previous chunk used); it waits for LDS accesses only.
+// previous chunk used); it waits for LDS accesses only.  (A two-unit weight ring
+// measured slower: four compute waves with eight steps of 2 KB in flight each
+// already cover the memory latency, and the deeper ring only adds registers.)
 constexpr int kXSlots = 4;
 constexpr int kXWaves = 2;
-constexpr int kWRing = 2 * kUnit;
 
 template <int RT, int T, int XS, int KC, int NWC>
 __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, bool wactive,
@@ -169,16 +170,15 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
     for (int g = 0; g < G; ++g) wg_barrier();
     return;
   }
-  // weight ring over two units: slot PAR * 8 + k holds step k of a unit of parity PAR;
-  // a unit with MORE refills its slots with the unit two ahead.  The loads sit on
-  // straight-line paths, so the compiler's waits are exact (the ring stays full).
-  u32x4 wr[kWRing][T];
+  // weight ring over one unit: slot k holds step k of the current unit; a unit with
+  // MORE refills each slot with the next unit's step once its MFMAs have read it.  The
+  // loads sit on straight-line paths, so the compiler's waits are exact.
+  u32x4 wr[kUnit][T];
   auto load = [&](int slot, int step) {
 #pragma unroll
     for (int j = 0; j < T; ++j) wr[slot][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)step * wstep));
   };
-  auto run_unit = [&](auto par_tag, auto more_tag, int u) {
-    constexpr int PAR = decltype(par_tag)::value;
+  auto run_unit = [&](auto more_tag, int u) {
     constexpr bool MORE = decltype(more_tag)::value;
     auto chunk = [&](auto h_tag) {
       constexpr int h = decltype(h_tag)::value;
@@ -200,37 +200,18 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
           for (int t = 0; t < RT; ++t)
 #pragma unroll
             for (int pl = XS - 1; pl >= 0; --pl)
-              acc[j][t] = mfma_bf16(wr[PAR * kUnit + k][j], xo[pl][t], acc[j][t]);
-        if constexpr (MORE) load(PAR * kUnit + k, (u + 2) * kUnit + k);
+              acc[j][t] = mfma_bf16(wr[k][j], xo[pl][t], acc[j][t]);
+        if constexpr (MORE) load(k, (u + 1) * kUnit + k);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     chunk(std::integral_constant<int, 0>{});
     if constexpr (NC == 2) chunk(std::integral_constant<int, 1>{});
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  if (nu == 1) {
 #pragma unroll
-    for (int k = 0; k < kUnit; ++k) load(k, k);
-    run_unit(P0{}, std::false_type{}, 0);
-    return;
-  }
-#pragma unroll
-  for (int k = 0; k < kWRing; ++k) load(k, k);
-  int u = 0;
-  for (; u + 3 < nu; u += 2) {
-    run_unit(P0{}, std::true_type{}, u);
-    run_unit(P1{}, std::true_type{}, u + 1);
-  }
-  if (nu - u == 3) {
-    run_unit(P0{}, std::true_type{}, u);
-    run_unit(P1{}, std::false_type{}, u + 1);
-    run_unit(P0{}, std::false_type{}, u + 2);
-  } else {
-    run_unit(P0{}, std::false_type{}, u);
-    run_unit(P1{}, std::false_type{}, u + 1);
-  }
+  for (int k = 0; k < kUnit; ++k) load(k, k);
+  for (int u = 0; u + 1 < nu; ++u) run_unit(std::true_type{}, u);
+  run_unit(std::false_type{}, nu - 1);
 }
 
 // One row tile (R <= 16), one wave per workgroup: the activation fragments are
@@ -399,10 +380,8 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
   }
 }
 
-// Feature tiles per wave: two once the activation tiles make LDS reads dominate.
-
-// Workgroups per split of the balanced launch (at most 256 per launch, at most
-// eight units each); the split count is the host's, a function of the shape.
+// Workgroups per split of the balanced launch (at most 256 per launch, at most one
+// unit per compute wave); the split count is the host's, a function of the shape.
 static int bal_cols(int units, int S) {
   constexpr int NWC = 8 - kXWaves;   // compute waves per workgroup
   int cols = std::min(kCUs / S, units);

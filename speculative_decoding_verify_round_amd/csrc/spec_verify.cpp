@@ -57,15 +57,18 @@ struct spec_model {
 namespace {
 
 // K splits of a bf16 projection, a function of (N, K) only so that results never
-// depend on R: the smallest power of two (at most 8, and at most one split per
-// 256-wide unit) that gives the 256-workgroup launch three or more tile pairs per
-// workgroup.  The gate/up pair is never split (its SwiGLU epilogue needs the full sums).
+// depend on R: the largest S (at most 8, with at least two 256-wide units per split)
+// for which the tile pairs of all splits fit four to a workgroup of the one-per-CU
+// launch.  Four pairs keep one weight-streaming wave per SIMD; a fifth pair would
+// share a SIMD with another MFMA-heavy wave, and the younger of the two is starved
+// of MFMA issue until the older one ends.  The gate/up pair is never split (its
+// SwiGLU epilogue needs the full sums).
 int split_for(const spec_model* m, int N, int K, bool fused_pair) {
   if (!m->bf16 || fused_pair) return 1;
   const int pairs = ((N + 15) / 16 + 1) / 2;
   const int units = K / 256;
   int S = 1;
-  while (S < 8 && 2 * S <= units && pairs * S < 3 * 256) S *= 2;
+  while (S < 8 && 2 * (S + 1) <= units && pairs * (S + 1) <= 4 * sv::kCUs) ++S;
   return S;
 }
 

@@ -67,28 +67,35 @@ __device__ __forceinline__ float col_sum(float v) {
 // consumed) and writes a partial at every chunk end, so a row's result depends
 // only on the fixed chunk grid.
 //
-// Work split of a stage (all QT query tiles at once): wave w computes S^T for
-// positions 16 w .. 16 w + 15 and O^T for d rows 32 w .. 32 w + 31.  Each wave DMAs
-// exactly the K rows and V^T rows it reads, so the ring needs no workgroup barrier;
-// two small LDS exchanges per stage (the row maxima, then P) keep the online
-// softmax exact: every wave applies the same running max.
+// Work split: eight waves, two per query tile q (rows 16 q .. 16 q + 15 of the
+// lane's (k+1) x G query rows): half h = 0, 1 of the tile takes positions
+// 32 h .. 32 h + 31 of every stage with an online softmax of its own, so no wave
+// needs anything from another within a stage and P never leaves registers.  The two
+// halves are merged exactly at the chunk end.  Half 0 of tile q runs on wave q and
+// half 1 on wave 4 + (q + 2) % 4, so one or two tiles occupy distinct SIMDs.  Waves
+// past the lane's query tiles only copy.
+//
+// The S^T tiles are arranged so that their MFMA output is the B operand of the PV
+// product as is: for half h, tile X takes A-operand row r from position
+// 32 h + 8 (r / 4) + r % 4 and tile Y from the same plus 4, so lane i receives
+// positions 32 h + 8 (i / 16) + e (X) and + 4 + e (Y), e = 0..3 -- exactly the K
+// indices 8 (i / 16) .. + 7 it supplies to the PV MFMA, in position order.
 //
 // LDS stage: K [64 positions][256 B] with 16-byte chunk c of position p stored at
-// chunk c ^ (p & 7); V^T block-major [4 blocks][128 d][32 B] with the two 16-byte
-// halves of row d swapped when d & 4; P [tile][query m][64 positions] as bf16 hi
-// and lo planes, chunk q of row m at q ^ (m & 7).  The MFMA operand reads are free
-// of bank conflicts, and every DMA reads 1 KB from one cache block: a wave-uniform
+// chunk c ^ f(p), f(p) = (p & 3) | ((p >> 3) & 3) << 2, which is r for the row r of
+// every S^T tile, so the A-operand reads are free of bank conflicts; V^T block-major
+// [4 blocks][128 d][32 B] with the two 16-byte halves of row d swapped when d & 4.
+// Wave w < 4 DMAs the K rows of block w of each stage, wave 4 + b the V^T rows of
+// block b; one workgroup barrier per stage publishes the stage and frees the slot the
+// previous stage used.  Every DMA reads 1 KB from one cache block: a wave-uniform
 // block address plus per-lane offsets fixed for the whole kernel.
-template <int QT>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnParams p) {
+__global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
   constexpr int D = 128, STEP = 64, NS = kAttnStages, PW = kAttnPartPad + D;
   constexpr int KBYTES = STEP * D * 2, SBYTES = 2 * KBYTES;
-  constexpr int NST = 3 * QT;    // store instructions of one chunk partial, per wave
+  constexpr int NST = 9;    // store instructions of one chunk partial (half-0 waves)
   __shared__ __attribute__((aligned(1024))) char ring[NS * SBYTES];
-  __shared__ __attribute__((aligned(16))) char pex[2][QT][16][128];   // P hi / lo planes
-  __shared__ float mex[4][QT][16];                                    // per-wave row maxima
-  __shared__ float lex[4][QT][16];                                    // per-wave row sums at chunk ends
   __shared__ int sblk[kAttnWgBlocks];                                 // committed block ids of the range
+  __shared__ float2 mlx[4][16];                                       // half 1's (max, sum) at chunk ends
   const int x = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,6 +113,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnParams p) {
   const int fb = first >> 4, b0 = kvl >> 4;   // blocks >= b0 come from the staged columns
   const int* bt = p.block_table + (size_t)l * p.max_blocks;
   const int nkv = p.nkv, Mq = cols * p.G;
+  const int h = wave >> 2;                    // half of the stage's positions
+  const int qtile = h ? ((wave + 2) & 3) : wave;
+  const bool active = 16 * qtile < Mq;        // the wave has query rows (wave-uniform)
   const float scale = p.scale_log2;
   const char* Kp = reinterpret_cast<const char*>(p.kpool);
   const char* Vp = reinterpret_cast<const char*>(p.vpool);
@@ -119,233 +129,213 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnParams p) {
     const int sid = kStageBlocks * l + (16 * b < end ? b - b0 : 0);
     return ((size_t)(b >= b0 ? sid : id) * nkv + g) * BLOCK_BYTES;
   };
-  // per-lane DMA offsets, fixed for the kernel: K segment i (positions 4 i .. 4 i + 3 of
-  // the block, chunk c of position p read into LDS chunk c ^ (p & 7)) and V^T rows
-  // 32 wave .. +31
-  uint32_t koff[4];
+  // per-lane DMA offsets, fixed for the kernel.  K waves: segment i holds positions
+  // 4 i .. 4 i + 3 of block w (stage position p = 16 w + 4 i + lane / 16; LDS chunk
+  // lane % 16 receives chunk (lane % 16) ^ f(p)).  V waves: segment i holds rows
+  // 32 i .. 32 i + 31 of block w - 4 (lane t: row t / 2, LDS half t & 1 receives half
+  // (t & 1) ^ (row / 4 & 1)).
+  const int bw = wave & 3;                    // the block this wave copies
+  const char* pool = h ? Vp : Kp;             // its committed pool and its staged blocks
+  const char* stg = h ? SV : SK;
+  uint32_t off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) koff[i] = (4 * i + (lane >> 4)) * 256 + (((lane & 15) ^ ((4 * i + (lane >> 4)) & 7)) << 4);
-  const uint32_t voff = 1024 * wave + (lane >> 1) * 32 + ((((lane & 1) ^ ((lane >> 3) & 1))) << 4);
-  // ---- DMA of stage t into ring slot t % NS: this wave's K block and V^T rows, 8 instructions
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * i + (lane >> 4), ps = 16 * bw + q;
+    const int f = (ps & 3) | (((ps >> 3) & 3) << 2);
+    off[i] = h ? 1024 * i + (lane >> 1) * 32 + ((((lane & 1) ^ ((lane >> 3) & 1))) << 4)
+               : q * 256 + (((lane & 15) ^ f) << 4);
+  }
+  // ---- DMA of this wave's part of stage t into ring slot t % NS, 4 instructions
   auto issue = [&](int t) {
-    char* sK = ring + (t % NS) * SBYTES;
-    char* sV = sK + KBYTES;
-    const int bb = fb + 4 * t;
-    int id[4];
+    char* dst = ring + (t % NS) * SBYTES + h * KBYTES + 4096 * bw;
+    const int b = fb + 4 * t + bw;
+    const int id = __builtin_amdgcn_readfirstlane(b < b0 ? sblk[b - fb] : 0);
+    const char* src = (b >= b0 ? stg : pool) + block_off(b, id);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) id[j] = __builtin_amdgcn_readfirstlane(bb + j < b0 ? sblk[bb + j - fb] : 0);
-    const int idw = wave == 0 ? id[0] : wave == 1 ? id[1] : wave == 2 ? id[2] : id[3];
-    const bool kst = bb + wave >= b0;
-    const char* kb = (kst ? SK : Kp) + block_off(bb + wave, idw);
-    char* ks = sK + 16 * wave * 256;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16<true>(kb, koff[i], ks + 1024 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const char* vb = (bb + j >= b0 ? SV : Vp) + block_off(bb + j, id[j]);
-      dma16<true>(vb, voff, sV + 4096 * j + 1024 * wave);
-    }
+    for (int i = 0; i < 4; ++i) dma16<true>(src, off[i], dst + 1024 * i);
   };
 
-  // block ids of the range and the queries (bf16 hi + lo planes, the B operands): every
-  // load is issued unconditionally from a valid address before any is used
-  constexpr int IPT = kAttnWgBlocks / 256;
+  // block ids of the range and the wave's queries (bf16 hi + lo planes, the B operands):
+  // every load is issued unconditionally from a valid address before any is used
+  constexpr int IPT = kAttnWgBlocks / 512;
   const int ncommit = min(4 * T, b0 - fb);
   int idv[IPT];
 #pragma unroll
   for (int k = 0; k < IPT; ++k) {
-    const int i = min(tid + 256 * k, max(ncommit - 1, 0));   // fb + i < max_blocks
+    const int i = min(tid + 512 * k, max(ncommit - 1, 0));   // fb + i < max_blocks
     idv[k] = bt[fb + i];
   }
-  f32x4 qraw[QT][8];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int m = min(qt * 16 + r16, Mq - 1);
-    const int j = m / p.G, hh = m - j * p.G;
+  const int m = 16 * qtile + r16;              // the lane's query row
+  f32x4 qraw[8];
+  {
+    const int mc = min(m, Mq - 1);
+    const int j = mc / p.G, hh = mc - j * p.G;
     const float* ptr = p.q + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-      qraw[qt][2 * ds] = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
-      qraw[qt][2 * ds + 1] = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
+      qraw[2 * ds] = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
+      qraw[2 * ds + 1] = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
     }
   }
 #pragma unroll
   for (int k = 0; k < IPT; ++k)
-    if (tid + 256 * k < ncommit) sblk[tid + 256 * k] = clamp_blk(idv[k], p.n_blocks);
-  u32x4 qh[QT][4], ql[QT][4];
-  int lim[QT];
+    if (tid + 512 * k < ncommit) sblk[tid + 512 * k] = clamp_blk(idv[k], p.n_blocks);
+  const bool valid = m < Mq;
+  const int lim = valid ? kvl + m / p.G : -1;  // last position the row attends to
+  u32x4 qh[4], ql[4];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int m = qt * 16 + r16;
-    const bool valid = m < Mq;
-    lim[qt] = valid ? kvl + m / p.G : -1;
+  for (int ds = 0; ds < 4; ++ds) {
+    const f32x4 a = qraw[2 * ds], b = qraw[2 * ds + 1];
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      const f32x4 a = qraw[qt][2 * ds], b = qraw[qt][2 * ds + 1];
-      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t hw, lw;
-        split2(v[2 * i], v[2 * i + 1], hw, lw);
-        qh[qt][ds][i] = valid ? hw : 0u;
-        ql[qt][ds][i] = valid ? lw : 0u;
-      }
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hw, lw;
+      split2(v[2 * i], v[2 * i + 1], hw, lw);
+      qh[ds][i] = valid ? hw : 0u;
+      ql[ds][i] = valid ? lw : 0u;
     }
   }
   // the compiler's waits for the loads above must precede the first DMA (its counts
   // do not include the DMAs): consume every query register here
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) asm volatile("" ::"v"(qh[qt][ds]), "v"(ql[qt][ds]));
+  for (int ds = 0; ds < 4; ++ds) asm volatile("" ::"v"(qh[ds]), "v"(ql[ds]));
   wg_barrier();   // block ids staged
   for (int t = 0; t < NS - 1 && t < T; ++t) issue(t);
 
-  // running max (raw score units), this lane's part of the row sum, O^T of the wave's d rows
-  float mrun[QT], lrun[QT];
-  f32x4 O[QT][2];
+  // running max (raw score units), this lane's part of the row sum, O^T[16 dt + 4 kq + e][m]
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 O[8];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = -INFINITY;
-    lrun[qt] = 0.f;
-    O[qt][0] = O[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int t) {
     const char* sK = ring + (t % NS) * SBYTES;
     const char* sV = sK + KBYTES;
-    const int p0 = first + STEP * t + 16 * wave;   // this wave's positions p0 + 4 kq + e
-    // S^T[pos][m] for the wave's 16 positions, every query tile (K fragments read once)
-    u32x4 kf[4];
-    {
-      const char* kr = sK + (16 * wave + r16) * 256;
+    // S^T tiles X (y = 0) and Y (y = 1) of the half: lane i reads row r16 = position
+    // 32 h + 8 (r16 / 4) + r16 % 4 + 4 y, whose chunks are swizzled by f = r16
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const char* kr = sK + (32 * h + 8 * (r16 >> 2) + (r16 & 3)) * 256;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[ds] = *reinterpret_cast<const u32x4*>(kr + (((4 * ds + kq) ^ (r16 & 7)) << 4));
-    }
-    f32x4 sc[QT];
+    for (int ds = 0; ds < 4; ++ds) {
+      u32x4 kf[2];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) sc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int y = 0; y < 2; ++y) kf[y] = *reinterpret_cast<const u32x4*>(kr + 4 * y * 256 + (((4 * ds + kq) ^ r16) << 4));
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        sc[qt] = mfma_bf16(kf[ds], ql[qt][ds], sc[qt]);
-        sc[qt] = mfma_bf16(kf[ds], qh[qt][ds], sc[qt]);
+      for (int y = 0; y < 2; ++y) {
+        sc[y] = mfma_bf16(kf[y], ql[ds], sc[y]);
+        sc[y] = mfma_bf16(kf[y], qh[ds], sc[y]);
       }
-    // positions past a query's own column are masked; a stage below kv_len needs none
+    }
+    // lane value e of tile y is position 32 h + 8 kq + 4 y + e; positions past a query's
+    // own column are masked, and a stage below kv_len needs none
+    const int p0 = first + STEP * t + 32 * h + 8 * kq;
     if (first + STEP * t + STEP > kvl) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+      for (int y = 0; y < 2; ++y)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sc[qt][e] = p0 + 4 * kq + e <= lim[qt] ? sc[qt][e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) sc[y][e] = p0 + 4 * y + e <= lim ? sc[y][e] : -INFINITY;
     }
+    const float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    const float mnew = fmaxf(mrun, col_max(mx));
+    float pr[2][4];
+    float alpha = 1.f;
+    if (mnew == -INFINITY) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mx = col_max(fmaxf(fmaxf(sc[qt][0], sc[qt][1]), fmaxf(sc[qt][2], sc[qt][3])));
-      if (kq == 0) mex[wave][qt][r16] = mx;
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[y][e] = 0.f;
+    } else {
+      // exp2(scale (s - m)) with the raw v_exp_f32: the arguments are at most a rounding
+      // of m * scale above zero, results below 2^-126 flush to 0
+      const float ms = mnew * scale;
+      alpha = __builtin_amdgcn_exp2f(fmaf(mrun, scale, -ms));
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[y][e] = __builtin_amdgcn_exp2f(fmaf(sc[y][e], scale, -ms));
     }
-    wg_barrier();                          // every wave's maxima are in LDS
-    float alpha[QT];
+    lrun = lrun * alpha + (((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3])));
+    mrun = mnew;
+    // P^T as bf16 hi + lo B operands: K index 8 kq + e from X, 8 kq + 4 + e from Y
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mnew = fmaxf(fmaxf(fmaxf(mrun[qt], mex[0][qt][r16]), fmaxf(mex[1][qt][r16], mex[2][qt][r16])),
-                               mex[3][qt][r16]);
-      float pr[4];
-      alpha[qt] = 1.f;
-      if (mnew == -INFINITY) {
+    for (int i = 0; i < 4; ++i) split2(pr[i >> 1][2 * (i & 1)], pr[i >> 1][2 * (i & 1) + 1], hw[i], lw[i]);
+    const u32x4 ph = u32x4{hw[0], hw[1], hw[2], hw[3]}, pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    // O *= alpha, skipped when no row of the wave has a new maximum (alpha is then 1)
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = 0.f;
-      } else {
-        // exp2(scale (s - m)) with the raw v_exp_f32: the arguments are at most a rounding
-        // of m * scale above zero, results below 2^-126 flush to 0
-        const float ms = mnew * scale;
-        alpha[qt] = __builtin_amdgcn_exp2f(fmaf(mrun[qt], scale, -ms));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(sc[qt][e], scale, -ms));
-      }
-      lrun[qt] = lrun[qt] * alpha[qt] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      mrun[qt] = mnew;
-      // P = hi + lo in bf16, row m, positions 16 wave + 4 kq .. +3 (8-position chunk q, half kq & 1)
-      uint32_t h0, l0, h1, l1;
-      split2(pr[0], pr[1], h0, l0);
-      split2(pr[2], pr[3], h1, l1);
-      const int q = 2 * wave + (kq >> 1);
-      const int off = ((q ^ (r16 & 7)) << 4) + ((kq & 1) << 3);
-      *reinterpret_cast<u32x2*>(&pex[0][qt][r16][off]) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(&pex[1][qt][r16][off]) = u32x2{l0, l1};
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
     }
-    wg_barrier();                          // P of all 64 positions is in LDS
-    // O^T[d][m] += V^T[d][keys] P^T[keys][m] over two 32-position steps; the lane's keys
-    // 32 c + 8 kq .. +7 are half kq & 1 of block 2 c + kq / 2
-    u32x4 vf[2][2];
+    // O^T[d][m] += V^T[d][keys] P^T[keys][m]: lane i supplies row d = 16 dt + r16 of V^T at
+    // positions 32 h + 8 kq .. +7 (half kq & 1 of block 2 h + kq / 2)
+    const char* vr = sV + 4096 * (2 * h + (kq >> 1)) + r16 * 32 + (((kq & 1) ^ ((r16 >> 2) & 1)) << 4);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        vf[c][h] = *reinterpret_cast<const u32x4*>(sV + 4096 * (2 * c + (kq >> 1)) + (32 * wave + 16 * h + r16) * 32 +
-                                                   (((kq & 1) ^ ((r16 >> 2) & 1)) << 4));
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      O[qt][0] *= alpha[qt];
-      O[qt][1] *= alpha[qt];
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x4 vf = *reinterpret_cast<const u32x4*>(vr + 16 * dt * 32);
+      O[dt] = mfma_bf16(vf, pl, O[dt]);
+      O[dt] = mfma_bf16(vf, ph, O[dt]);
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const int off = ((4 * c + kq) ^ (r16 & 7)) << 4;
-        const u32x4 ph = *reinterpret_cast<const u32x4*>(&pex[0][qt][r16][off]);
-        const u32x4 pl = *reinterpret_cast<const u32x4*>(&pex[1][qt][r16][off]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          O[qt][h] = mfma_bf16(vf[c][h], pl, O[qt][h]);
-          O[qt][h] = mfma_bf16(vf[c][h], ph, O[qt][h]);
-        }
-      }
   };
 
-  int t_store = -NS;     // iteration of the last chunk-partial stores
+  int t_store = -NS;     // iteration of this wave's last chunk-partial stores
+  const bool stores = active && h == 0;
   for (int t = 0; t < T; ++t) {
-    // stage t is complete once at most (stages issued after it) x 8 DMAs, plus
-    // chunk-partial stores issued after it, are outstanding
+    // this wave's DMAs of stage t are complete once at most (stages issued after it)
+    // x 4 DMAs, plus chunk-partial stores issued after it, are outstanding
     const int after = min(T, t + NS - 1) - (t + 1);
     if (t - t_store <= NS - 1) {
-      if (after >= 2) wait_vm<16 + NST>();
-      else if (after == 1) wait_vm<8 + NST>();
+      if (after >= 2) wait_vm<8 + NST>();
+      else if (after == 1) wait_vm<4 + NST>();
       else wait_vm<NST>();
     } else {
-      if (after >= 2) wait_vm<16>();
-      else if (after == 1) wait_vm<8>();
+      if (after >= 2) wait_vm<8>();
+      else if (after == 1) wait_vm<4>();
       else wait_vm<0>();
     }
+    wg_barrier();                            // stage t is in LDS; stage t - 1 is consumed
     if (t + NS - 1 < T) issue(t + NS - 1);   // into the slot stage t - 1 used
-    compute(t);
+    if (active) compute(t);
     if (t % cs == cs - 1 || t == T - 1) {
-      // chunk partial: the wave's row sums, then O rows 32 wave .. 32 wave + 31, m and l
-      const int c = c0 + t / cs;
+      // chunk end: half 1 hands its (O, max, sum) to half 0 through the slot of stage t
+      // (free once every wave is past this barrier; the next issue into it follows the
+      // next stage's barrier), half 0 merges and writes the tile's partial
+      wg_barrier();
+      float* xo = reinterpret_cast<float*>(ring + (t % NS) * SBYTES) + qtile * 2048;
+      const float lt = col_sum(lrun);
+      if (active && h == 1) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float lw = col_sum(lrun[qt]);
-        if (kq == 0) lex[wave][qt][r16] = lw;
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(xo + (dt * 64 + lane) * 4) = O[dt];
+        if (kq == 0) mlx[qtile][r16] = float2{mrun, lt};
       }
       wg_barrier();
-      float* slot = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float lt = ((lex[0][qt][r16] + lex[1][qt][r16]) + lex[2][qt][r16]) + lex[3][qt][r16];
-        const int m = qt * 16 + r16;
-        // rows past the lane's queries are skipped; row 16 qt is always written (never
-        // read when invalid) so that every store instruction has an active lane
-        if (m < Mq || r16 == 0) {
-          *reinterpret_cast<f32x4*>(slot + part_index(m, 32 * wave + 4 * kq)) = O[qt][0];
-          *reinterpret_cast<f32x4*>(slot + part_index(m, 32 * wave + 16 + 4 * kq)) = O[qt][1];
-          *reinterpret_cast<f32x4*>(slot + part_index(m, D)) = f32x4{mrun[qt] * scale, lt, 0.f, 0.f};
+      if (stores) {
+        const float2 o1 = mlx[qtile][r16];
+        const float M = fmaxf(mrun, o1.x);
+        float f0 = 0.f, f1 = 0.f;
+        if (M != -INFINITY) {
+          const float ms = M * scale;
+          f0 = __builtin_amdgcn_exp2f(fmaf(mrun, scale, -ms));
+          f1 = __builtin_amdgcn_exp2f(fmaf(o1.x, scale, -ms));
         }
-        mrun[qt] = -INFINITY;
-        lrun[qt] = 0.f;
-        O[qt][0] = O[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int c = c0 + t / cs;
+        float* slot = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
+        // rows past the lane's queries are skipped; row 16 q is always written (never
+        // read when invalid) so that every store instruction has an active lane
+        if (valid || r16 == 0) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(xo + (dt * 64 + lane) * 4);
+            *reinterpret_cast<f32x4*>(slot + part_index(m, 16 * dt + 4 * kq)) = O[dt] * f0 + b1 * f1;
+          }
+          *reinterpret_cast<f32x4*>(slot + part_index(m, D)) = f32x4{M * scale, lt * f0 + o1.y * f1, 0.f, 0.f};
+        }
+        t_store = t;
       }
-      t_store = t;
+      mrun = -INFINITY;
+      lrun = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -467,15 +457,7 @@ int launch_attention(const AttnParams& p, bool bf16, hipStream_t st) {
   dim3 block(256);
   if (bf16) {
     dim3 grid(attn_ranges(p), p.nkv, p.ri.L);
-    int maxMq = 0;
-    for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;
-    const int QT = (maxMq + 15) / 16;
-    switch (QT) {
-      case 1: hipLaunchKernelGGL(k_attn_bf16<1>, grid, block, 0, st, p); break;
-      case 2: hipLaunchKernelGGL(k_attn_bf16<2>, grid, block, 0, st, p); break;
-      case 3: hipLaunchKernelGGL(k_attn_bf16<3>, grid, block, 0, st, p); break;
-      default: hipLaunchKernelGGL(k_attn_bf16<4>, grid, block, 0, st, p); break;
-    }
+    hipLaunchKernelGGL(k_attn_bf16, grid, dim3(512), 0, st, p);
   } else {
     int maxMq = 0;
     for (int l = 0; l < p.ri.L; ++l) maxMq = p.ri.lane_cols[l] * p.G > maxMq ? p.ri.lane_cols[l] * p.G : maxMq;

@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # measured HBM traffic of the gate/up kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
 # calibrated against a plain copy); reported only while that kernel's sources are unchanged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic_dense27b.md")
+PROFILE_EVERY = 8     # gate/up launches per recorded one (64 layers: 8 per round)
 GATEUP_SOURCES = ("gemm.hip", "common.hpp")
 COPY_CALIBRATION_BYTES = 512 << 20
 METRIC = "committed tokens/s & verify rows/s at lanes×(k+1); % of HBM roofline"
@@ -293,7 +294,9 @@ def main():
         step()
     torch.cuda.synchronize()
     committed_log.clear()
-    B.spec_profile_enable(dm.handle, B.SPEC_K_GATE_UP)
+    # every 8th gate/up launch carries a pair of HIP events (8 per round): an event pair
+    # around every launch would add its queue gap to 64 launches per round
+    B.spec_profile_enable(dm.handle, B.SPEC_K_GATE_UP, PROFILE_EVERY)
     log(f"timed {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()

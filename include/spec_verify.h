@@ -250,10 +250,13 @@ int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float
 int64_t spec_packed_weight_bytes(int N, int K);
 int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream);
 
-/* Measurement: record HIP events around every launch of one kernel class
- * (SPEC_K_NONE stops recording), and read back the summed duration of the
- * launches recorded since the last enable (synchronises on those events). */
-int spec_profile_enable(spec_model* model, int kernel_class);
+/* Measurement: record HIP events around launches 0, every, 2 every, ... of one
+ * kernel class, counted from this call (SPEC_K_NONE stops recording; every >= 1,
+ * else SPEC_E_INVAL), and read back the summed duration and the number of the
+ * launches recorded since the last enable (synchronises on those events).  Each
+ * recorded launch pays for its two event records (a few microseconds of queue
+ * gap), so a sparse stride keeps the measurement from slowing what it measures. */
+int spec_profile_enable(spec_model* model, int kernel_class, int every);
 int spec_profile_collect(spec_model* model, double* total_ms, int* launches);
 
 #ifdef __cplusplus

@@ -104,7 +104,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_pack_weight.restype = C.c_int
         lib.spec_pack_weight.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         lib.spec_profile_enable.restype = C.c_int
-        lib.spec_profile_enable.argtypes = [C.c_void_p, C.c_int]
+        lib.spec_profile_enable.argtypes = [C.c_void_p, C.c_int, C.c_int]
         lib.spec_profile_collect.restype = C.c_int
         lib.spec_profile_collect.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int)]
         _lib = lib
@@ -181,8 +181,8 @@ def spec_pack_weight(src_ptr: int, dst_ptr: int, N: int, K: int, stream: int) ->
                                            C.c_void_p(stream)), "spec_pack_weight")
 
 
-def spec_profile_enable(model, kernel_class: int) -> None:
-    _check(load_library().spec_profile_enable(model, kernel_class), "spec_profile_enable")
+def spec_profile_enable(model, kernel_class: int, every: int = 1) -> None:
+    _check(load_library().spec_profile_enable(model, kernel_class, every), "spec_profile_enable")
 
 
 def spec_profile_collect(model):

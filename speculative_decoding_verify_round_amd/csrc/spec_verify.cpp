@@ -49,6 +49,8 @@ struct spec_model {
   int lm_groups = 1;
   // profiling
   int prof_class = SPEC_K_NONE;
+  int prof_every = 1;             // record launches 0, every, 2 every, ... of the class
+  long prof_seen = 0;             // launches of the class since the last enable
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_events;
   std::vector<hipEvent_t> prof_pool;
   size_t prof_used = 0;
@@ -206,7 +208,7 @@ struct ProfScope {
   bool on;
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(const spec_model* mc, int cls, hipStream_t s) : m(const_cast<spec_model*>(mc)), st(s) {
-    on = m->prof_class == cls && cls != SPEC_K_NONE;
+    on = m->prof_class == cls && cls != SPEC_K_NONE && m->prof_seen++ % m->prof_every == 0;
     if (!on) return;
     while (m->prof_pool.size() < m->prof_used + 2) {
       hipEvent_t e;
@@ -592,9 +594,11 @@ int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream) {
   return sv::launch_pack_weight(src, dst, N, K, reinterpret_cast<hipStream_t>(stream)) ? SPEC_E_HIP : SPEC_OK;
 }
 
-int spec_profile_enable(spec_model* m, int kernel_class) {
-  if (!m || kernel_class < SPEC_K_NONE || kernel_class >= SPEC_K_COUNT) return SPEC_E_INVAL;
+int spec_profile_enable(spec_model* m, int kernel_class, int every) {
+  if (!m || kernel_class < SPEC_K_NONE || kernel_class >= SPEC_K_COUNT || every < 1) return SPEC_E_INVAL;
   m->prof_class = kernel_class;
+  m->prof_every = every;
+  m->prof_seen = 0;
   m->prof_events.clear();
   m->prof_used = 0;
   return SPEC_OK;

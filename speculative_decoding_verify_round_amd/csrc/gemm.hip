@@ -119,64 +119,85 @@ __device__ __forceinline__ void proj_core(const bf16_t* const (&wp)[T], size_t w
   run_unit(std::false_type{}, nu - 1);
 }
 
-// R > 16, split roles: compute waves 0 .. NWC-1 stream weights and run the MFMAs;
-// the remaining kXWaves waves only copy X chunks into a kXSlots-deep LDS ring by DMA.
+// R > 16, split roles in an eight-wave workgroup of up to five units:
+//  * main waves 0..3 own units 0..3: they stream their unit's weights and run its MFMAs
+//    for every row tile;
+//  * helper waves 4, 5 share a fifth unit: helper h runs its MFMAs for row tiles h and
+//    h + 2 only (both load the unit's weights, the second from L2), so no SIMD carries
+//    two full units -- waves w and w + 4 share a SIMD, and of two MFMA-heavy waves on
+//    one SIMD the younger is starved of MFMA issue until the older one ends;
+//  * loader waves 6, 7 copy X chunks into a kXSlots-deep LDS ring by DMA.
 // Each wave's in-order vmcnt counter then holds one kind of load: the compute waves
 // never wait for an X load behind their weights, so their weight ring runs a whole
-// unit (eight steps) ahead, and the loaders keep the X ring kXSlots - 1 chunks
-// ahead.  One workgroup barrier per chunk publishes it (and frees the slot the
-// previous chunk used); it waits for LDS accesses only.  (A two-unit weight ring
-// measured slower: four compute waves with eight steps of 2 KB in flight each
-// already cover the memory latency, and the deeper ring only adds registers.)
+// unit (eight steps) ahead, and the loaders keep the X ring kXSlots - 1 chunks ahead.
+// One workgroup barrier per chunk publishes it (and frees the slot the previous chunk
+// used); it waits for LDS accesses only.  (A two-unit weight ring measured slower:
+// four compute waves with eight steps of 2 KB in flight each already cover the memory
+// latency, and the deeper ring only adds registers.)
 constexpr int kXSlots = 4;
 constexpr int kXWaves = 2;
+constexpr int kMainWaves = 4;
+constexpr int kHelpers = 2;
+constexpr int kMaxUnits = kMainWaves + 1;   // units per workgroup
 
-template <int RT, int T, int XS, int KC, int NWC>
-__device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, bool wactive,
-                                             const bf16_t* __restrict__ X, size_t xplane, int KS, int step0,
-                                             int nu, char* xring, f32x4 (&acc)[T][RT]) {
+// Loader waves: X chunk g of the unit range into ring slot g % kXSlots, then the
+// chunk's barrier once it has landed.
+template <int RT, int XS, int KC>
+__device__ __forceinline__ void x_loader(const bf16_t* __restrict__ X, size_t xplane, int KS, int step0, int nu,
+                                         char* xring, int lw) {
   constexpr int NB = KC * RT * XS;           // 1 KB X fragments per chunk: b = (plane * RT + tile) * KC + step
   constexpr int NC = kUnit / KC;             // chunks per unit
   constexpr int CHUNK = NB * 1024;
   constexpr int PER = NB / kXWaves;          // DMAs per loader wave per chunk
   static_assert(NB % kXWaves == 0 && (NC == 1 || NC == 2), "chunk shape");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int G = nu * NC;
-  if (wave >= NWC) {
-    const int lw = wave - NWC;
-    auto issue = [&](int g) {
-      char* slot = xring + (g % kXSlots) * CHUNK;
+  auto issue = [&](int g) {
+    char* slot = xring + (g % kXSlots) * CHUNK;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int b = lw + kXWaves * i;
-        const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
-        const bf16_t* src = X + pl * xplane + ((size_t)t * KS + step0 + g * KC + st) * 512;
-        dma16<false>(src, lane * 16, slot + b * 1024);
-      }
-    };
-    for (int g = 0; g < kXSlots - 1 && g < G; ++g) issue(g);
-    for (int g = 0; g < G; ++g) {
-      const int after = min(G - 1, g + kXSlots - 2) - g;   // chunks issued after g
-      if (after >= 2) wait_vm<2 * PER>();
-      else if (after == 1) wait_vm<PER>();
-      else wait_vm<0>();
-      wg_barrier();                                        // chunk g is in LDS
-      if (g + kXSlots - 1 < G) issue(g + kXSlots - 1);     // into the slot chunk g - 1 used
+    for (int i = 0; i < PER; ++i) {
+      const int b = lw + kXWaves * i;
+      const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
+      const bf16_t* src = X + pl * xplane + ((size_t)t * KS + step0 + g * KC + st) * 512;
+      dma16<false>(src, lane * 16, slot + b * 1024);
     }
-    return;
+  };
+  for (int g = 0; g < kXSlots - 1 && g < G; ++g) issue(g);
+  for (int g = 0; g < G; ++g) {
+    const int after = min(G - 1, g + kXSlots - 2) - g;   // chunks issued after g
+    if (after >= 2) wait_vm<2 * PER>();
+    else if (after == 1) wait_vm<PER>();
+    else wait_vm<0>();
+    wg_barrier();                                        // chunk g is in LDS
+    if (g + kXSlots - 1 < G) issue(g + kXSlots - 1);     // into the slot chunk g - 1 used
   }
-  // compute waves without a unit only keep the barrier count
-  if (!wactive) {
-    for (int g = 0; g < G; ++g) wg_barrier();
-    return;
-  }
+}
+
+// Compute waves: acc[j][i] += W tile j . X row tile rt(i) over the unit range, i < NR,
+// with row tile rt(i) = r0 + RS i (main waves: r0 = 0, RS = 1, NR = RT; helpers:
+// r0 = h, RS = 2, NR = 2, a row tile past RT reads a valid slot and is discarded).
+// NT: non-temporal weight loads (data read once); helpers share a unit and load it
+// cacheable so that the second one finds it in L2.
+template <int RT, int T, int XS, int KC, int NR, bool NT>
+__device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, int r0, int RS, int nu,
+                                             const char* xring, f32x4 (&acc)[T][NR]) {
+  constexpr int NB = KC * RT * XS;
+  constexpr int NC = kUnit / KC;
+  constexpr int CHUNK = NB * 1024;
+  const int lane = threadIdx.x & 63;
+  int rt[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) rt[i] = min(r0 + RS * i, RT - 1);
   // weight ring over one unit: slot k holds step k of the current unit; a unit with
   // MORE refills each slot with the next unit's step once its MFMAs have read it.  The
   // loads sit on straight-line paths, so the compiler's waits are exact.
   u32x4 wr[kUnit][T];
   auto load = [&](int slot, int step) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) wr[slot][j] = ld_stream(reinterpret_cast<const u32x4*>(wp[j] + (size_t)step * wstep));
+    for (int j = 0; j < T; ++j) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(wp[j] + (size_t)step * wstep);
+      wr[slot][j] = NT ? ld_stream(src) : *src;
+    }
   };
   auto run_unit = [&](auto more_tag, int u) {
     constexpr bool MORE = decltype(more_tag)::value;
@@ -188,19 +209,19 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
 #pragma unroll
       for (int st = 0; st < KC; ++st) {
         const int k = h * KC + st;
-        u32x4 xo[XS][RT];
+        u32x4 xo[XS][NR];
 #pragma unroll
         for (int pl = 0; pl < XS; ++pl)
 #pragma unroll
-          for (int t = 0; t < RT; ++t)
-            xo[pl][t] = *reinterpret_cast<const u32x4*>(slot + ((pl * RT + t) * KC + st) * 1024);
+          for (int i = 0; i < NR; ++i)
+            xo[pl][i] = *reinterpret_cast<const u32x4*>(slot + ((pl * RT + rt[i]) * KC + st) * 1024);
 #pragma unroll
         for (int j = 0; j < T; ++j)
 #pragma unroll
-          for (int t = 0; t < RT; ++t)
+          for (int i = 0; i < NR; ++i)
 #pragma unroll
             for (int pl = XS - 1; pl >= 0; --pl)
-              acc[j][t] = mfma_bf16(wr[k][j], xo[pl][t], acc[j][t]);
+              acc[j][i] = mfma_bf16(wr[k][j], xo[pl][i], acc[j][i]);
         if constexpr (MORE) load(k, (u + 1) * kUnit + k);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -268,53 +289,31 @@ __device__ __forceinline__ float swiglu(float g32, float u32) {
 // R > 16: at most 256 workgroups of eight waves per launch.  Units are tile
 // pairs (EPI 0: tiles 2u, 2u + 1; EPI 1: gate and up tile u).  Workgroup b
 // takes split s = b / cols and the units [w P / cols, (w + 1) P / cols) of it
-// (w = b % cols), one unit per wave, so every CU streams the same number of
-// units +-1 whatever the tile count (1088 gate/up pairs become 4 or 5 per CU,
-// where whole 4-pair workgroups leave 16 CUs with twice the work).  Waves
-// without a unit only help stage X; their weight reads all hit one fragment.
-template <int RT, int XS, int EPI>
-__global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
-  constexpr int KC = chunk_steps<RT>(), T = 2, NWC = 8 - kXWaves;
-  __shared__ __attribute__((aligned(1024))) char xring[kXSlots * KC * RT * XS * 1024];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
-  const int unit = (int)((long long)w * p.units / p.cols) + wave;
-  const bool active = wave < NWC && unit < (int)((long long)(w + 1) * p.units / p.cols);
-  const int KS = p.K >> 5, U = p.K >> 8;
-  const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
-  int tile[T];
-  const bf16_t* wp[T];
-#pragma unroll
-  for (int j = 0; j < T; ++j) {
-    tile[j] = EPI == 1 ? unit : unit * 2 + j;
-    const int tc = active ? min(tile[j], p.tiles - 1) : 0;
-    const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
-    wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
-  }
-  f32x4 acc[T][RT];
-#pragma unroll
-  for (int j = 0; j < T; ++j)
-#pragma unroll
-    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core_xw<RT, T, XS, KC, NWC>(wp, 512, active, p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xring, acc);
-  if (!active) return;
-  const int r16 = lane & 15, kq = lane >> 4;
-  // lane holds D[feature 16 tile + 4 kq + e][row 16 t + r16]
+// (w = b % cols), at most five: units 0..3 to the main waves, a fifth to the two
+// helpers, so every CU streams the same number of units +-1 whatever the tile count
+// (1088 gate/up pairs become 4 or 5 per CU, where whole 4-pair workgroups leave 16
+// CUs with twice the work).
+template <int RT, int XS, int EPI, int NR>
+__device__ __forceinline__ void bal_epilogue(const ProjParams& p, const int (&tile)[2], int s, int r0, int RS,
+                                             const f32x4 (&acc)[2][NR]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
+  // lane holds D[feature 16 tile + 4 kq + e][row 16 rt + r16]
   if constexpr (EPI == 0) {
     const bool vec = (p.N & 3) == 0;
 #pragma unroll
-    for (int j = 0; j < T; ++j) {
+    for (int j = 0; j < 2; ++j) {
       if (tile[j] >= p.tiles) continue;
       const int nf = tile[j] * 16 + 4 * kq;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
+      for (int i = 0; i < NR; ++i) {
+        const int t = r0 + RS * i;
         const int r = t * 16 + r16;
-        if (r >= p.R) continue;
+        if (t >= RT || r >= p.R) continue;
         float* dst = p.P + ((size_t)s * p.R + r) * p.N + nf;
         if (vec && nf + 4 <= p.N) {
-          *reinterpret_cast<f32x4*>(dst) = acc[j][t];
+          *reinterpret_cast<f32x4*>(dst) = acc[j][i];
         } else {
-          for (int e = 0; e < 4 && nf + e < p.N; ++e) dst[e] = acc[j][t][e];
+          for (int e = 0; e < 4 && nf + e < p.N; ++e) dst[e] = acc[j][i][e];
         }
       }
     }
@@ -322,14 +321,61 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
     if (tile[0] >= p.tiles) return;
     const int nf = tile[0] * 16 + 4 * kq;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
+    for (int i = 0; i < NR; ++i) {
+      const int t = r0 + RS * i;
       const int r = t * 16 + r16;
-      if (r >= p.R || nf + 4 > p.N) continue;
+      if (t >= RT || r >= p.R || nf + 4 > p.N) continue;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = swiglu(acc[0][t][e], acc[1][t][e]);
+      for (int e = 0; e < 4; ++e) v[e] = swiglu(acc[0][i][e], acc[1][i][e]);
       st_out4(p.Y, p.yplane, r, nf, p.N, v);
     }
+  }
+}
+
+template <int RT, int XS, int EPI>
+__global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
+  constexpr int KC = chunk_steps<RT>(), T = 2;
+  __shared__ __attribute__((aligned(1024))) char xring[kXSlots * KC * RT * XS * 1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
+  const int ub = (int)((long long)w * p.units / p.cols), ue = (int)((long long)(w + 1) * p.units / p.cols);
+  const int KS = p.K >> 5, U = p.K >> 8;
+  const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
+  if (wave >= kMainWaves + kHelpers) {
+    x_loader<RT, XS, KC>(p.X, p.xplane, KS, u0 * kUnit, u1 - u0, xring, wave - kMainWaves - kHelpers);
+    return;
+  }
+  const bool helper = wave >= kMainWaves;
+  const int unit = helper ? ub + kMainWaves : ub + wave;
+  if (unit >= ue) {   // no unit: keep the barrier count
+    for (int g = 0; g < (u1 - u0) * (kUnit / KC); ++g) wg_barrier();
+    return;
+  }
+  int tile[T];
+  const bf16_t* wp[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    tile[j] = EPI == 1 ? unit : unit * 2 + j;
+    const int tc = min(tile[j], p.tiles - 1);
+    const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
+    wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
+  }
+  if (!helper) {
+    f32x4 acc[T][RT];
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    proj_core_xw<RT, T, XS, KC, RT, true>(wp, 512, 0, 1, u1 - u0, xring, acc);
+    bal_epilogue<RT, XS, EPI, RT>(p, tile, s, 0, 1, acc);
+  } else {
+    const int h = wave - kMainWaves;
+    f32x4 acc[T][2];
+#pragma unroll
+    for (int j = 0; j < T; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    proj_core_xw<RT, T, XS, KC, 2, false>(wp, 512, h, 2, u1 - u0, xring, acc);
+    bal_epilogue<RT, XS, EPI, 2>(p, tile, s, h, 2, acc);
   }
 }
 
@@ -380,12 +426,11 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
   }
 }
 
-// Workgroups per split of the balanced launch (at most 256 per launch, at most one
-// unit per compute wave); the split count is the host's, a function of the shape.
+// Workgroups per split of the balanced launch (at most 256 per launch, at most
+// kMaxUnits units each); the split count is the host's, a function of the shape.
 static int bal_cols(int units, int S) {
-  constexpr int NWC = 8 - kXWaves;   // compute waves per workgroup
   int cols = std::min(kCUs / S, units);
-  if ((units + cols - 1) / cols > NWC) cols = (units + NWC - 1) / NWC;
+  if ((units + cols - 1) / cols > kMaxUnits) cols = (units + kMaxUnits - 1) / kMaxUnits;
   return std::max(cols, 1);
 }
 

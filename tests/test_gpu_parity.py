@@ -190,6 +190,20 @@ def test_attention_chunks_and_own_columns_cross_boundaries(context):
     pair.close()
 
 
+def test_attention_four_query_tiles_and_idle_waves():
+    """G = 8 query heads per kv head: a lane of 8 columns has 64 query rows (all four
+    query tiles of the attention workgroup busy), a lane of 3 columns 24 (two tiles,
+    the other waves only copy); chunks of 256 positions with the columns straddling one."""
+    cfg = small_dense(hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128, ffn=512, vocab=1024, context=300,
+                      n_layers=1, layer_kinds=("attn",))
+    pair = Pair(cfg, lanes=2, context=300, max_blocks=(300 + 40) // 16 + 1, attn_chunk=256)
+    toks = [[1, 2, 3, 4, 5, 6, 7, 8], [9, 10, 11]]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
+    log(f"four query tiles: logit err {lerr:.2e}")
+    assert not mism
+    pair.close()
+
+
 def test_small_hybrid_bf16_round_and_commit():
     cfg = small_hybrid(hidden=256, head_dim=128, ffn=512, vocab=1024, gdn_heads=2, gdn_dim=128, context=40)
     pair = Pair(cfg, lanes=2, context=40, max_blocks=8)

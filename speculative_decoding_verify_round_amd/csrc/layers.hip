@@ -117,13 +117,49 @@ __device__ __forceinline__ void sum_splits4(const float* P, size_t split_stride,
   }
 }
 
-// x[r] += float(sum_s P[s][r]) (s in order), then h[r] = round(rmsnorm(x[r]) * gain)
+// The first kSplitBatch split partials of four consecutive floats, loaded (clamped to a
+// valid split) and then summed in split order in float64: callers issue every load of a
+// thread before the first sum.
+__device__ __forceinline__ void load_splits4(const float* P, size_t split_stride, int S, f32x4 (&pv)[kSplitBatch]) {
+#pragma unroll
+  for (int i = 0; i < kSplitBatch; ++i) pv[i] = *reinterpret_cast<const f32x4*>(P + (size_t)min(i, S - 1) * split_stride);
+}
+__device__ __forceinline__ void sum_loaded4(const f32x4 (&pv)[kSplitBatch], const float* P, size_t split_stride, int S,
+                                            double (&t)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = (double)pv[0][e];
+#pragma unroll
+  for (int i = 1; i < kSplitBatch; ++i) {
+    if (i >= S) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] += (double)pv[i][e];
+  }
+  if (S > kSplitBatch) {   // more splits than one batch (the split rule allows at most 8)
+    double u[4];
+    sum_splits4(P + kSplitBatch * split_stride, split_stride, S - kSplitBatch, u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] += u[e];
+  }
+}
+
+// x[r] += float(sum_s P[s][r]) (s in order), then h[r] = round(rmsnorm(x[r]) * gain).
+// Every load of the row (residual, the S partials, the gains of both float4 groups) is
+// issued before the first is used, so the kernel pays one memory round trip.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int S, int R, float* x, int H,
                                                              const float* gain, float eps, T* h) {
   __shared__ double red[32];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * H;
+  const size_t sstride = (size_t)R * H;
+  f32x4 xo[kRowGroups], gn[kRowGroups], pv[kRowGroups][kSplitBatch];
+#pragma unroll
+  for (int gi = 0; gi < kRowGroups; ++gi) {
+    const int g = min(threadIdx.x + gi * kRowThreads, H / 4 - 1);   // a valid address for every lane
+    xo[gi] = *reinterpret_cast<const f32x4*>(xr + 4 * g);
+    gn[gi] = *reinterpret_cast<const f32x4*>(gain + 4 * g);
+    load_splits4(P + (size_t)r * H + 4 * g, sstride, S, pv[gi]);
+  }
   f32x4 xn[kRowGroups];
   double ss = 0.0;
 #pragma unroll
@@ -131,16 +167,26 @@ __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int 
     const int g = threadIdx.x + gi * kRowThreads;
     xn[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (4 * g >= H) continue;
-    const f32x4 xo = *reinterpret_cast<const f32x4*>(xr + 4 * g);
     double t[4];
-    sum_splits4(P + (size_t)r * H + 4 * g, (size_t)R * H, S, t);
+    sum_loaded4(pv[gi], P + (size_t)r * H + 4 * g, sstride, S, t);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) xn[gi][e] = (float)((double)xo[e] + (double)(float)t[e]);   // x + float(projection)
+    for (int e = 0; e < 4; ++e) xn[gi][e] = (float)((double)xo[gi][e] + (double)(float)t[e]);   // x + float(projection)
     *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ss += (double)xn[gi][q] * (double)xn[gi][q];
   }
-  norm_store(xn, r, H, gain, eps, h, act_plane(R, H), ss, red);
+  const double tot = block_sum_f64(ss, red);
+  const double scale = 1.0 / sqrt(tot / (double)H + (double)eps);
+  const size_t plane = act_plane(R, H);
+#pragma unroll
+  for (int gi = 0; gi < kRowGroups; ++gi) {
+    const int g = threadIdx.x + gi * kRowThreads;
+    if (4 * g >= H) break;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (float)((double)xn[gi][e] * scale * (double)gn[gi][e]);
+    st_out4(h, plane, r, 4 * g, H, v);
+  }
 }
 
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,

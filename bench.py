@@ -84,11 +84,15 @@ def gpu_weights(cfg, seed: int):
 
 
 def gateup_source_hash() -> str:
-    import hashlib
+    """Hash of the code (comments and whitespace removed) the gate/up kernel is built from."""
+    import hashlib, re
     h = hashlib.sha256()
     for f in GATEUP_SOURCES:
-        with open(os.path.join(ROOT, "speculative_decoding_verify_round_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "speculative_decoding_verify_round_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)     # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                   # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

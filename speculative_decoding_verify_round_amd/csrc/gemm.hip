@@ -6,15 +6,18 @@
 // decoding", gpillon.github.io/ignis).  Both operands are stored as 1 KB MFMA
 // fragments (frag_off), so every wave load is one contiguous 1 KB.
 //
-// Workgroup = 4 waves on T consecutive 16-feature tiles each, all on the same
-// K split.  The activation rows (B operand, up to four 16-row tiles, one or
-// two bf16 planes) are staged chunk by chunk into a double-buffered LDS ring
-// that the four waves share; the weights (A operand) stream through an
-// eight-step register ring with non-temporal loads.  The X chunk for the next
-// step range is fetched at the start of a chunk and written to LDS at its end,
-// so every global load -- weights and activations alike -- has a whole chunk
-// of MFMA steps to arrive (the in-order vmcnt counter never makes a step wait
-// for a younger load).
+// Three cores share the fragment layout and the weight ring (an eight-step register
+// ring per wave, non-temporal loads):
+//  * R <= 16 (k_proj_direct): one wave per workgroup on two tiles, the activation
+//    fragments read straight from memory into a ring beside the weights';
+//  * R > 16 (k_proj_bal, proj_core_xw): eight waves with split roles -- main waves
+//    own a unit (tile pair) each, two helpers share a fifth, two loaders copy the
+//    activation chunks into an LDS ring by DMA;
+//  * the LM head and the race (proj_core): four waves on T tiles each share a
+//    double-buffered LDS ring of activation chunks; the X chunk for the next step
+//    range is fetched at the start of a chunk and written to LDS at its end, so every
+//    global load has a whole chunk of MFMA steps to arrive (the in-order vmcnt
+//    counter never makes a step wait for a younger load).
 //
 // Numerics: each output element is one fp32 MFMA accumulation chain over its
 // split in a fixed K order (per step the lo plane, then the hi plane); K

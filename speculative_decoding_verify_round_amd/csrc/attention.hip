@@ -11,13 +11,15 @@
 // of a lane/kv-head pair are processed together, so every K/V byte of the lane
 // is read once per layer.  The round's own columns are staged in cache-layout
 // blocks aligned to absolute positions, so a 16-position block is either a
-// committed block of the paged cache or a staged block, and the online softmax
-// visits positions in order.  A row's result is therefore independent of how
-// many columns the round carries and of whether a key is still staged or
-// already committed.
+// committed block of the paged cache or a staged block, and which positions an
+// online softmax visits, in which order, is fixed by absolute position.  A row's
+// result is therefore independent of how many columns the round carries and of
+// whether a key is still staged or already committed.
 //
-// bf16 path (head_dim 128): wave w owns query tile w (16 of the lane's
-// (k+1) x G query rows).  Per 32 positions:
+// bf16 path (head_dim 128): two waves per query tile (16 of the lane's (k+1) x G
+// query rows), one per 32-position half of every 64-position stage, each with an
+// online softmax of its own that is merged with the other's at the chunk end.  Per
+// 32 positions:
 //   S^T[pos][query] = K . Q^T with v_mfma_f32_16x16x32_bf16 (K rows = A; the
 //   float32 queries = B, as bf16 hi + lo planes);
 //   P = exp2(S * log2(e)/sqrt(d) - m) in fp32, split into bf16 hi + lo;

@@ -246,6 +246,12 @@ struct ProjParams {
   float* P;             // [S][R][N] float32 partial sums
   bf16_t* Y;            // SwiGLU output planes, packed with width N
   size_t yplane;
+  // balanced SwiGLU launch (rem > 0): base whole units per CU, the rem units past
+  // base * kCUs cut into pq K pieces; piece sums in Q [rem][pq][2][R][16], one
+  // arrival counter per cut unit in cnt (zero between launches)
+  int base, rem, pq;
+  float* Q;
+  int* cnt;
 };
 
 struct GemmF32Params {

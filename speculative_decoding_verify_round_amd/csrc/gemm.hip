@@ -143,6 +143,111 @@ constexpr int kMainWaves = 4;
 constexpr int kHelpers = 2;
 constexpr int kMaxUnits = kMainWaves + 1;   // units per workgroup
 
+// ------------------------------------------------------------------------------- cut units
+// A gate/up launch whose unit count is not a multiple of the CU count would leave some
+// CUs one whole unit more to stream than the others (1088 units: 64 CUs with five, 192
+// with four), and the launch lasts as long as its busiest CU.  The balanced launch gives
+// every CU `base` whole units plus one K piece (whole 256-wide steps) of one of the `rem`
+// units left over, each of those cut into `pq` pieces, so every CU streams the same
+// weight bytes to within a piece.  A piece's gate and up sums go to Q with
+// agent-coherent stores (sc1: they reach the point of coherence of all CUs before the
+// wave's store counter drops); once they are complete, the wave (or workgroup) counts
+// itself in with an atomic add, and the one that completes the unit's count reads the
+// pieces back with sc1 loads, adds them in piece order in float64, applies the SwiGLU
+// epilogue and zeroes the counter for the next launch.  Pieces and their order follow
+// from the shape alone, so a row's result never depends on how many rows the round has.
+constexpr int kMaxPieces = 8;
+
+// float(silu(g) * u) evaluated in float64 from the fp32 projections
+__device__ __forceinline__ float swiglu(float g32, float u32) {
+  const double g = (double)g32, u = (double)u32;
+  return (float)(g / (1.0 + exp(-g)) * u);
+}
+
+struct SwigluPlan {
+  int base, rem, pq;
+};
+
+__host__ __device__ inline SwigluPlan swiglu_plan(int units, int K) {
+  SwigluPlan s{units / kCUs, units % kCUs, 0};
+  const int U = K >> 8;
+  if (s.base < 1 || s.base > kMainWaves || s.rem == 0) return SwigluPlan{s.base, 0, 0};
+  s.pq = kCUs / s.rem;
+  s.pq = s.pq < U ? s.pq : U;
+  s.pq = s.pq < kMaxPieces ? s.pq : kMaxPieces;
+  if (s.pq < 2) return SwigluPlan{s.base, 0, 0};   // nothing to even out
+  return s;
+}
+
+int swiglu_pieces(int N, int K, int* rem, int* pq) {
+  const SwigluPlan s = swiglu_plan((N + 15) / 16, K);
+  *rem = s.rem;
+  *pq = s.pq;
+  return s.rem * s.pq;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t piece_rsrc(const ProjParams& p) {
+  const int bytes = p.rem * p.pq * 2 * p.R * 16 * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(p.Q, 0, bytes, 0x00020000);
+}
+
+// Byte offset of Q[r][part][j][row][f].
+__device__ __forceinline__ uint32_t piece_off(const ProjParams& p, int r, int part, int j, int row, int f) {
+  return (uint32_t)((((((size_t)r * p.pq + part) * 2 + j) * p.R + row) * 16 + f) * 4);
+}
+
+// Row tile t of tile j (gate 0, up 1) of a piece: lane holds features 4 kq .. + 3 of row
+// 16 t + r16.
+__device__ __forceinline__ void piece_store(const ProjParams& p, __amdgpu_buffer_rsrc_t rs, int r, int part, int t,
+                                            int j, f32x4 v) {
+  const int lane = threadIdx.x & 63, row = 16 * t + (lane & 15);
+  if (row >= p.R) return;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, piece_off(p, r, part, j, row, 4 * (lane >> 4)),
+                                         0, 16);
+}
+
+// Counts one arrival at cut unit r once the caller's piece stores are complete; true for
+// the arrival that completes `arrivals`.
+__device__ __forceinline__ bool piece_arrive(const ProjParams& p, int r, int arrivals) {
+  return __hip_atomic_fetch_add(p.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrivals - 1;
+}
+
+// Thread t of nt: (row, four features) items t, t + nt, ... of cut unit r.
+__device__ void piece_combine(const ProjParams& p, __amdgpu_buffer_rsrc_t rs, int r, int t, int nt) {
+  const int unit = p.base * kCUs + r;
+  for (int it = t; it < p.R * 4; it += nt) {
+    const int row = it >> 2, f4 = it & 3;
+    u32x4 gv[kMaxPieces], uv[kMaxPieces];
+#pragma unroll
+    for (int q = 0; q < kMaxPieces; ++q) {
+      const int qc = min(q, p.pq - 1);
+      gv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 0, row, 4 * f4), 0, 16);
+      uv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 1, row, 4 * f4), 0, 16);
+    }
+    double gs[4], us[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gs[e] = (double)__uint_as_float(gv[0][e]);
+      us[e] = (double)__uint_as_float(uv[0][e]);
+    }
+#pragma unroll
+    for (int q = 1; q < kMaxPieces; ++q) {
+      if (q >= p.pq) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gs[e] += (double)__uint_as_float(gv[q][e]);
+        us[e] += (double)__uint_as_float(uv[q][e]);
+      }
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = swiglu((float)gs[e], (float)us[e]);
+    const int nf = unit * 16 + 4 * f4;
+    if (nf + 4 <= p.N) st_out4(p.Y, p.yplane, row, nf, p.N, v);
+  }
+  if (t == 0) __hip_atomic_store(p.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Loader waves: X chunk g of the unit range into ring slot g % kXSlots, then the
 // chunk's barrier once it has landed.
 template <int RT, int XS, int KC>
@@ -181,9 +286,11 @@ __device__ __forceinline__ void x_loader(const bf16_t* __restrict__ X, size_t xp
 // r0 = h, RS = 2, NR = 2, a row tile past RT reads a valid slot and is discarded).
 // NT: non-temporal weight loads (data read once); helpers share a unit and load it
 // cacheable so that the second one finds it in L2.
+// g0: chunks of the launch before the range (a K piece): the range's first weights are
+// requested before the wave passes those chunks' barriers.
 template <int RT, int T, int XS, int KC, int NR, bool NT>
 __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, int r0, int RS, int nu,
-                                             const char* xring, f32x4 (&acc)[T][NR]) {
+                                             const char* xring, f32x4 (&acc)[T][NR], int g0 = 0) {
   constexpr int NB = KC * RT * XS;
   constexpr int NC = kUnit / KC;
   constexpr int CHUNK = NB * 1024;
@@ -206,7 +313,7 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
     constexpr bool MORE = decltype(more_tag)::value;
     auto chunk = [&](auto h_tag) {
       constexpr int h = decltype(h_tag)::value;
-      const int g = u * NC + h;
+      const int g = g0 + u * NC + h;
       wg_barrier();                                        // chunk g is in LDS
       const char* slot = xring + (g % kXSlots) * CHUNK + lane * 16;
 #pragma unroll
@@ -234,6 +341,7 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
   };
 #pragma unroll
   for (int k = 0; k < kUnit; ++k) load(k, k);
+  for (int g = 0; g < g0; ++g) wg_barrier();
   for (int u = 0; u + 1 < nu; ++u) run_unit(std::true_type{}, u);
   run_unit(std::false_type{}, nu - 1);
 }
@@ -282,11 +390,6 @@ __device__ __forceinline__ void proj_core_direct(const bf16_t* const (&wp)[T], s
 template <int RT>
 constexpr int chunk_steps() { return RT <= 2 ? 8 : 4; }
 
-// float(silu(g) * u) evaluated in float64 from the fp32 projections
-__device__ __forceinline__ float swiglu(float g32, float u32) {
-  const double g = (double)g32, u = (double)u32;
-  return (float)(g / (1.0 + exp(-g)) * u);
-}
 
 // ------------------------------------------------------------------------------- projection
 // R > 16: at most 256 workgroups of eight waves per launch.  Units are tile
@@ -336,10 +439,75 @@ __device__ __forceinline__ void bal_epilogue(const ProjParams& p, const int (&ti
   }
 }
 
+// Balanced SwiGLU launch, one workgroup per CU (S = 1): main wave i < base streams whole
+// unit base w + i; the helpers compute piece w (if any) over its K range from the same
+// X chunks, and then every wave takes part in the arrival (every wave, loaders and idle
+// waves included, passes the same barriers).
+template <int RT, int XS>
+__device__ __forceinline__ void bal_cut(const ProjParams& p, char* xring) {
+  constexpr int KC = chunk_steps<RT>(), T = 2, NC = kUnit / KC;
+  __shared__ int last;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int w = blockIdx.x;
+  const int KS = p.K >> 5, U = p.K >> 8, G = U * NC;
+  const int npieces = p.rem * p.pq;
+  const int r = w / p.pq, part = w - r * p.pq;
+  if (wave >= kMainWaves + kHelpers) {
+    x_loader<RT, XS, KC>(p.X, p.xplane, KS, 0, U, xring, wave - kMainWaves - kHelpers);
+  } else if (wave < kMainWaves) {
+    if (wave < p.base) {
+      const int unit = w * p.base + wave;
+      int tile[T] = {unit, unit};
+      const bf16_t* wp[T] = {p.W0 + (size_t)unit * KS * 512 + lane * 8, p.W1 + (size_t)unit * KS * 512 + lane * 8};
+      f32x4 acc[T][RT];
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      proj_core_xw<RT, T, XS, KC, RT, true>(wp, 512, 0, 1, U, xring, acc);
+      bal_epilogue<RT, XS, 1, RT>(p, tile, 0, 0, 1, acc);
+    } else {
+      for (int g = 0; g < G; ++g) wg_barrier();
+    }
+  } else if (w < npieces) {
+    const int h = wave - kMainWaves;
+    const int unit = p.base * kCUs + r;
+    const int k0 = part * U / p.pq, k1 = (part + 1) * U / p.pq;
+    const size_t off = ((size_t)unit * KS + (size_t)k0 * kUnit) * 512 + lane * 8;
+    const bf16_t* wp[T] = {p.W0 + off, p.W1 + off};
+    f32x4 acc[T][2];
+#pragma unroll
+    for (int j = 0; j < T; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    proj_core_xw<RT, T, XS, KC, 2, false>(wp, 512, h, 2, k1 - k0, xring, acc, k0 * NC);
+    const auto rs = piece_rsrc(p);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = h + 2 * i;
+      if (t < RT)
+#pragma unroll
+        for (int j = 0; j < T; ++j) piece_store(p, rs, r, part, t, j, acc[j][i]);
+    }
+    for (int g = k1 * NC; g < G; ++g) wg_barrier();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the piece is stored
+  } else {
+    for (int g = 0; g < G; ++g) wg_barrier();
+  }
+  wg_barrier();                                          // both helpers' pieces are stored
+  if (threadIdx.x == 0) last = w < npieces && piece_arrive(p, r, p.pq);
+  wg_barrier();
+  if (last) piece_combine(p, piece_rsrc(p), r, threadIdx.x, blockDim.x);
+}
+
 template <int RT, int XS, int EPI>
 __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   constexpr int KC = chunk_steps<RT>(), T = 2;
   __shared__ __attribute__((aligned(1024))) char xring[kXSlots * KC * RT * XS * 1024];
+  if constexpr (EPI == 1) {
+    if (p.rem > 0) {
+      bal_cut<RT, XS>(p, xring);
+      return;
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
   const int ub = (int)((long long)w * p.units / p.cols), ue = (int)((long long)(w + 1) * p.units / p.cols);
@@ -382,9 +550,37 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   }
 }
 
-// R <= 16: one wave per workgroup (T tiles, one split), epilogues as k_proj.
+// A piece of a cut unit, one wave: the unit's gate and up tiles over the piece's K range.
+template <int XS>
+__device__ __forceinline__ void direct_piece(const ProjParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int pi = blockIdx.x - p.base * kCUs, r = pi / p.pq, part = pi - r * p.pq;
+  const int unit = p.base * kCUs + r;
+  const int KS = p.K >> 5, U = p.K >> 8;
+  const int k0 = part * U / p.pq, k1 = (part + 1) * U / p.pq;
+  const size_t off = ((size_t)unit * KS + (size_t)k0 * kUnit) * 512 + lane * 8;
+  const bf16_t* wp[2] = {p.W0 + off, p.W1 + off};
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  proj_core_direct<2, XS>(wp, 512, p.X, p.xplane, k0 * kUnit, k1 - k0, p.R, acc);
+  const auto rs = piece_rsrc(p);
+  piece_store(p, rs, r, part, 0, 0, acc[0]);
+  piece_store(p, rs, r, part, 0, 1, acc[1]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the piece is stored
+  int last = 0;
+  if (lane == 0) last = piece_arrive(p, r, p.pq);
+  if (__builtin_amdgcn_readfirstlane(last)) piece_combine(p, rs, r, lane, 64);
+}
+
+// R <= 16: one wave per workgroup (T tiles, one split), epilogues as k_proj.  A
+// balanced SwiGLU launch appends the piece workgroups after the whole units.
 template <int T, int XS, int EPI>
 __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
+  if constexpr (EPI == 1) {
+    if (p.rem > 0 && (int)blockIdx.x >= p.base * kCUs) {
+      direct_piece<XS>(p);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int col = blockIdx.x % p.cols, s = blockIdx.x / p.cols;
   const int KS = p.K >> 5, U = p.K >> 8;
@@ -440,10 +636,15 @@ static int bal_cols(int units, int S) {
 int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
   ProjParams p = p0;
   const int RT = (p.R + 15) / 16;
+  p.rem = 0;
+  if (swiglu && p.S == 1 && p.Q && p.cnt) {
+    const SwigluPlan sp = swiglu_plan(p.tiles, p.K);
+    p.base = sp.base; p.rem = sp.rem; p.pq = sp.pq;
+  }
   if (RT == 1) {   // one wave per workgroup, two tiles per wave
     constexpr int T = 2;
     p.cols = swiglu ? p.tiles : (p.tiles + T - 1) / T;
-    dim3 grid(p.cols * p.S), block(64);
+    dim3 grid(p.rem ? p.base * kCUs + p.rem * p.pq : p.cols * p.S), block(64);
     if (swiglu) hipLaunchKernelGGL((k_proj_direct<2, 2, 1>), grid, block, 0, st, p);
     else if (xs == 2) hipLaunchKernelGGL((k_proj_direct<2, 2, 0>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_proj_direct<2, 1, 0>), grid, block, 0, st, p);
@@ -451,7 +652,7 @@ int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
   }
   p.units = swiglu ? p.tiles : (p.tiles + 1) / 2;
   p.cols = bal_cols(p.units, p.S);
-  dim3 grid(p.cols * p.S), block(512);
+  dim3 grid(p.rem ? kCUs : p.cols * p.S), block(512);
 #define SV_P(RT_, XS_, E_) hipLaunchKernelGGL((k_proj_bal<RT_, XS_, E_>), grid, block, 0, st, p)
 #define SV_P_RT(XS_, E_)             \
   switch (RT) {                      \

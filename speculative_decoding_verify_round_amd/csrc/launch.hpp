@@ -7,6 +7,9 @@ namespace sv {
 
 // projections
 int launch_proj(const ProjParams& p, bool swiglu, int xs, hipStream_t st);
+// cut units of a balanced gate/up launch of N features over K (rem units of pq pieces
+// each); returns rem * pq, 0 when the launch needs no cut
+int swiglu_pieces(int N, int K, int* rem, int* pq);
 int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st);
 
 // LM head statistics and the residual race
@@ -28,7 +31,7 @@ int launch_attn_combine(const AttnParams& p, void* o, bool bf16, hipStream_t st)
 int launch_rope_table(const int32_t* kv_len, const RowInfo& ri, int d, float theta, double* table,
                       hipStream_t st);
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
-                      float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st);
+                      float* x, void* h, const RowInfo& ri, bool bf16, int* zero, int nzero, hipStream_t st);
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
                       const RowInfo& ri, bool bf16, hipStream_t st);
 int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int nq, int nkv, int d,

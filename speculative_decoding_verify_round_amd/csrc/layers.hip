@@ -66,11 +66,16 @@ __device__ __forceinline__ f32x4 ld_act4(const bf16_t* p) {
                __uint_as_float(w[1] & 0xffff0000u)};
 }
 
+// Also zeroes the nzero arrival counters of the round's balanced gate/up launches
+// (each launch leaves them zero again; this covers a workspace that held anything else).
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_embed_norm(const int32_t* tokens, const T* embed, int V, int H,
-                                                             const float* gain, float eps, float* x, T* h, int R) {
+                                                             const float* gain, float eps, float* x, T* h, int R,
+                                                             int* zero, int nzero) {
   __shared__ double red[32];
   const int r = blockIdx.x;
+  if (r == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   int tok = tokens[r];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
   float* xr = x + (size_t)r * H;
@@ -91,13 +96,15 @@ __global__ __launch_bounds__(kRowThreads) void k_embed_norm(const int32_t* token
 }
 
 int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, const float* gain, float eps,
-                      float* x, void* h, const RowInfo& ri, bool bf16, hipStream_t st) {
+                      float* x, void* h, const RowInfo& ri, bool bf16, int* zero, int nzero, hipStream_t st) {
   if (bf16)
     hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, tokens,
-                       reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h), ri.R);
+                       reinterpret_cast<const bf16_t*>(embed), V, H, gain, eps, x, reinterpret_cast<bf16_t*>(h), ri.R,
+                       zero, nzero);
   else
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(ri.R), dim3(kRowThreads), 0, st, tokens,
-                       reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h), ri.R);
+                       reinterpret_cast<const float*>(embed), V, H, gain, eps, x, reinterpret_cast<float*>(h), ri.R,
+                       zero, nzero);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -75,7 +75,8 @@ int split_for(const spec_model* m, int N, int K, bool fused_pair) {
 }
 
 struct WsLayout {
-  size_t x, h, P, q, o, a, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, total;
+  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, total;
+  int n_cnt;                    // arrival counters of the gate/up cut units
   size_t stage_layer_elems;     // elements per attention layer in stk/stv
   size_t gst_layer_floats;      // floats per gdn layer in gst
   int n_chunks;
@@ -112,6 +113,11 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.q = take((size_t)R * qdim * 4);
   w.o = take(R16 * std::max(qdim, gdim) * 4);
   w.a = take(R16 * d.ffn * 4);
+  int rem = 0, pq = 0;
+  if (m->bf16 && d.n_layers) sv::swiglu_pieces(d.ffn, (int)H, &rem, &pq);
+  w.n_cnt = rem;
+  w.pieces = take((size_t)rem * pq * 2 * R * 16 * 4);
+  w.pcnt = take((size_t)rem * 4);
   w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 8);
   w.stage_layer_elems = (size_t)L * sv::kStageBlocks * SPEC_KV_BLOCK * d.n_kv_heads * d.head_dim;
   w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
@@ -235,8 +241,9 @@ struct ProfScope {
 // X: an fp32 model's float activations [R][K]; for a bf16 model the packed
 // activation planes (hi, then lo when two_planes; one exact bf16 plane otherwise).
 // W: packed fragments (bf16) or row-major [N][K] float.
+// Q / cnt: the cut-unit pieces and counters of a balanced gate/up launch (null elsewhere).
 int project(const spec_model* m, int cls, const void* X, bool two_planes, const void* W0, const void* W1, int R,
-            int N, int K, int S, float* P, void* Y, hipStream_t st) {
+            int N, int K, int S, float* P, void* Y, hipStream_t st, float* Q = nullptr, int* cnt = nullptr) {
   ProfScope ps(m, cls, st);
   if (m->bf16) {
     sv::ProjParams p{};
@@ -248,6 +255,8 @@ int project(const spec_model* m, int cls, const void* X, bool two_planes, const 
     p.P = P;
     p.Y = reinterpret_cast<sv::bf16_t*>(Y);
     p.yplane = sv::act_plane(R, N);
+    p.Q = Q;
+    p.cnt = cnt;
     return sv::launch_proj(p, W1 != nullptr, two_planes ? 2 : 1, st);
   }
   sv::GemmF32Params p{};
@@ -273,7 +282,8 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
   const bool rope = d.rope_theta != 0.f && m->n_attn > 0;
   if (rope) SV_CHECK(sv::launch_rope_table(r->kv_len, ri, d.head_dim, d.rope_theta, at<double>(ws, w.rope), st));
   const float* g0 = d.n_layers ? m->layers[0].w.norm1 : d.final_norm;
-  SV_CHECK(sv::launch_embed_norm(r->tokens, d.embed, d.vocab, H, g0, d.rms_eps, x, h, ri, bf, st));
+  SV_CHECK(sv::launch_embed_norm(r->tokens, d.embed, d.vocab, H, g0, d.rms_eps, x, h, ri, bf, at<int>(ws, w.pcnt),
+                                 w.n_cnt, st));
   const size_t apool = (size_t)r->n_blocks * d.n_kv_heads * SPEC_KV_BLOCK * d.head_dim * ab;
   for (int i = 0; i < d.n_layers; ++i) {
     const Layer& L = m->layers[i];
@@ -326,7 +336,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
     SV_CHECK(project(m, SPEC_K_PROJ_O, at<void>(ws, w.o), true, L.w.w_o, nullptr, R, H, Ko, S_o, P, nullptr, st));
     SV_CHECK(sv::launch_resid_norm(P, S_o, x, H, L.w.norm2, d.rms_eps, h, ri, bf, st));
     SV_CHECK(project(m, SPEC_K_GATE_UP, h, true, L.w.w_gate, L.w.w_up, R, d.ffn, H, 1, nullptr, at<void>(ws, w.a),
-                     st));
+                     st, at<float>(ws, w.pieces), at<int>(ws, w.pcnt)));
     SV_CHECK(project(m, SPEC_K_DOWN, at<void>(ws, w.a), true, L.w.w_down, nullptr, R, H, d.ffn, m->s_down.S, P,
                      nullptr, st));
     SV_CHECK(sv::launch_resid_norm(P, m->s_down.S, x, H, gnext, d.rms_eps, h, ri, bf, st));

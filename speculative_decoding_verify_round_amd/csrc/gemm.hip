@@ -156,7 +156,7 @@ constexpr int kMaxUnits = kMainWaves + 1;   // units per workgroup
 // pieces back with sc1 loads, adds them in piece order in float64, applies the SwiGLU
 // epilogue and zeroes the counter for the next launch.  Pieces and their order follow
 // from the shape alone, so a row's result never depends on how many rows the round has.
-constexpr int kMaxPieces = 8;
+constexpr int kMaxPieces = 4;
 
 // float(silu(g) * u) evaluated in float64 from the fp32 projections
 __device__ __forceinline__ float swiglu(float g32, float u32) {
@@ -206,53 +206,56 @@ __device__ __forceinline__ void piece_store(const ProjParams& p, __amdgpu_buffer
                                          0, 16);
 }
 
-// Counts one arrival at cut unit r once the caller's piece stores are complete; true for
-// the arrival that completes `arrivals`.
-__device__ __forceinline__ bool piece_arrive(const ProjParams& p, int r, int arrivals) {
-  return __hip_atomic_fetch_add(p.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrivals - 1;
+// The pieces of one (row, four features) item of cut unit r: gate and up, pq of each
+// (slots past pq repeat the last piece and are not added).
+struct PieceLoads {
+  u32x4 g[kMaxPieces], u[kMaxPieces];
+};
+
+__device__ __forceinline__ PieceLoads piece_load(const ProjParams& p, __amdgpu_buffer_rsrc_t rs, int r, int item) {
+  const int row = item >> 2, f = 4 * (item & 3);
+  PieceLoads ld;
+#pragma unroll
+  for (int q = 0; q < kMaxPieces; ++q) {
+    const int qc = min(q, p.pq - 1);
+    ld.g[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 0, row, f), 0, 16);
+    ld.u[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 1, row, f), 0, 16);
+  }
+  return ld;
 }
 
-// Thread t of nt: (row, four features) items t, t + nt, ... of cut unit r.
-__device__ void piece_combine(const ProjParams& p, __amdgpu_buffer_rsrc_t rs, int r, int t, int nt) {
-  const int unit = p.base * kCUs + r;
-  for (int it = t; it < p.R * 4; it += nt) {
-    const int row = it >> 2, f4 = it & 3;
-    u32x4 gv[kMaxPieces], uv[kMaxPieces];
+// Adds the pieces in piece order in float64 and stores the item's SwiGLU output.
+__device__ __forceinline__ void piece_finish(const ProjParams& p, int unit, int item, const PieceLoads& ld) {
+  const int row = item >> 2, f = 4 * (item & 3);
+  double gs[4], us[4];
 #pragma unroll
-    for (int q = 0; q < kMaxPieces; ++q) {
-      const int qc = min(q, p.pq - 1);
-      gv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 0, row, 4 * f4), 0, 16);
-      uv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, piece_off(p, r, qc, 1, row, 4 * f4), 0, 16);
-    }
-    double gs[4], us[4];
+  for (int e = 0; e < 4; ++e) {
+    gs[e] = (double)__uint_as_float(ld.g[0][e]);
+    us[e] = (double)__uint_as_float(ld.u[0][e]);
+  }
+#pragma unroll
+  for (int q = 1; q < kMaxPieces; ++q) {
+    if (q >= p.pq) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      gs[e] = (double)__uint_as_float(gv[0][e]);
-      us[e] = (double)__uint_as_float(uv[0][e]);
+      gs[e] += (double)__uint_as_float(ld.g[q][e]);
+      us[e] += (double)__uint_as_float(ld.u[q][e]);
     }
-#pragma unroll
-    for (int q = 1; q < kMaxPieces; ++q) {
-      if (q >= p.pq) break;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gs[e] += (double)__uint_as_float(gv[q][e]);
-        us[e] += (double)__uint_as_float(uv[q][e]);
-      }
-    }
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = swiglu((float)gs[e], (float)us[e]);
-    const int nf = unit * 16 + 4 * f4;
-    if (nf + 4 <= p.N) st_out4(p.Y, p.yplane, row, nf, p.N, v);
   }
-  if (t == 0) __hip_atomic_store(p.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = swiglu((float)gs[e], (float)us[e]);
+  const int nf = unit * 16 + f;
+  if (nf + 4 <= p.N) st_out4(p.Y, p.yplane, row, nf, p.N, v);
 }
 
 // Loader waves: X chunk g of the unit range into ring slot g % kXSlots, then the
 // chunk's barrier once it has landed.
 template <int RT, int XS, int KC>
+// rs, SK: the chunks start at step rs of a range of SK steps and wrap around (rs = 0: in
+// order).
 __device__ __forceinline__ void x_loader(const bf16_t* __restrict__ X, size_t xplane, int KS, int step0, int nu,
-                                         char* xring, int lw) {
+                                         char* xring, int lw, int rs = 0, int SK = 1 << 30) {
   constexpr int NB = KC * RT * XS;           // 1 KB X fragments per chunk: b = (plane * RT + tile) * KC + step
   constexpr int NC = kUnit / KC;             // chunks per unit
   constexpr int CHUNK = NB * 1024;
@@ -262,11 +265,13 @@ __device__ __forceinline__ void x_loader(const bf16_t* __restrict__ X, size_t xp
   const int G = nu * NC;
   auto issue = [&](int g) {
     char* slot = xring + (g % kXSlots) * CHUNK;
+    int gk = g * KC + rs;
+    gk = gk < SK ? gk : gk - SK;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int b = lw + kXWaves * i;
       const int pl = b / (RT * KC), t = (b / KC) % RT, st = b % KC;
-      const bf16_t* src = X + pl * xplane + ((size_t)t * KS + step0 + g * KC + st) * 512;
+      const bf16_t* src = X + pl * xplane + ((size_t)t * KS + step0 + gk + st) * 512;
       dma16<false>(src, lane * 16, slot + b * 1024);
     }
   };
@@ -286,11 +291,13 @@ __device__ __forceinline__ void x_loader(const bf16_t* __restrict__ X, size_t xp
 // r0 = h, RS = 2, NR = 2, a row tile past RT reads a valid slot and is discarded).
 // NT: non-temporal weight loads (data read once); helpers share a unit and load it
 // cacheable so that the second one finds it in L2.
-// g0: chunks of the launch before the range (a K piece): the range's first weights are
-// requested before the wave passes those chunks' barriers.
+// g0: chunks of the launch before the range: the range's first weights are requested
+// before the wave passes those chunks' barriers.  rs, SK: the steps start at step rs of
+// SK and wrap around, as the X chunks do (rs = 0: in order).
 template <int RT, int T, int XS, int KC, int NR, bool NT>
 __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_t wstep, int r0, int RS, int nu,
-                                             const char* xring, f32x4 (&acc)[T][NR], int g0 = 0) {
+                                             const char* xring, f32x4 (&acc)[T][NR], int g0 = 0, int rs = 0,
+                                             int SK = 1 << 30) {
   constexpr int NB = KC * RT * XS;
   constexpr int NC = kUnit / KC;
   constexpr int CHUNK = NB * 1024;
@@ -303,6 +310,8 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
   // loads sit on straight-line paths, so the compiler's waits are exact.
   u32x4 wr[kUnit][T];
   auto load = [&](int slot, int step) {
+    step += rs;
+    step = step < SK ? step : step - SK;
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       const u32x4* src = reinterpret_cast<const u32x4*>(wp[j] + (size_t)step * wstep);
@@ -353,7 +362,7 @@ __device__ __forceinline__ void proj_core_xw(const bf16_t* const (&wp)[T], size_
 template <int T, int XS>
 __device__ __forceinline__ void proj_core_direct(const bf16_t* const (&wp)[T], size_t wstep,
                                                  const bf16_t* __restrict__ X, size_t xplane, int step0, int nu,
-                                                 int rows, f32x4 (&acc)[T]) {
+                                                 int rows, f32x4 (&acc)[T], int rs = 0, int SK = 1 << 30) {
   const int lane = threadIdx.x & 63;
   const bf16_t* xp = X + (size_t)step0 * 512 + lane * 8;   // row tile 0: fragment s at s * 512
   // lane i carries row i % 16 of an X fragment: lanes of the tile's padding rows
@@ -361,6 +370,8 @@ __device__ __forceinline__ void proj_core_direct(const bf16_t* const (&wp)[T], s
   const bool xrow = (lane & 15) < rows;
   u32x4 wr[kUnit][T], xr[kUnit][XS];
   auto load = [&](int slot, int st) {
+    st += rs;
+    st = st < SK ? st : st - SK;
 #pragma unroll
     for (int pl = 0; pl < XS; ++pl) {
       xr[slot][pl] = u32x4{0u, 0u, 0u, 0u};
@@ -439,22 +450,36 @@ __device__ __forceinline__ void bal_epilogue(const ProjParams& p, const int (&ti
   }
 }
 
-// Balanced SwiGLU launch, one workgroup per CU (S = 1): main wave i < base streams whole
-// unit base w + i; the helpers compute piece w (if any) over its K range from the same
-// X chunks, and then every wave takes part in the arrival (every wave, loaders and idle
-// waves included, passes the same barriers).
+// K rotation of whole unit `unit` in a balanced SwiGLU launch: every workgroup (and
+// every wave-sized workgroup of the same unit in the one-row-tile launch) takes the K
+// steps from the start of its piece on, wrapping around, so the pieces are done first.
+__device__ __forceinline__ int cut_rotation(const ProjParams& p, int unit) {
+  const int w = unit / p.base, U = p.K >> 8;
+  if (w >= p.rem * p.pq) return 0;
+  return (w % p.pq) * U / p.pq;
+}
+
+// Balanced SwiGLU launch, one workgroup per CU (S = 1), K order rotated to start at the
+// workgroup's piece: main wave i < base streams whole unit base w + i; helper 0
+// computes piece w (if any) over all row tiles from the same X chunks, stores it, and
+// over the next chunk barriers lets the stores complete, counts itself in, and -- if it
+// completes the unit -- adds the pieces and writes the unit's SwiGLU output, so none of
+// this lands on the launch's tail.  Every wave passes the same barriers.
 template <int RT, int XS>
 __device__ __forceinline__ void bal_cut(const ProjParams& p, char* xring) {
   constexpr int KC = chunk_steps<RT>(), T = 2, NC = kUnit / KC;
-  __shared__ int last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int w = blockIdx.x;
-  const int KS = p.K >> 5, U = p.K >> 8, G = U * NC;
-  const int npieces = p.rem * p.pq;
+  const int KS = p.K >> 5, U = p.K >> 8, G = U * NC, SK = U * kUnit;
+  const bool cut = w < p.rem * p.pq;
   const int r = w / p.pq, part = w - r * p.pq;
+  const int k0 = cut ? part * U / p.pq : 0, k1 = cut ? (part + 1) * U / p.pq : 0;
+  const int rs = k0 * kUnit;
   if (wave >= kMainWaves + kHelpers) {
-    x_loader<RT, XS, KC>(p.X, p.xplane, KS, 0, U, xring, wave - kMainWaves - kHelpers);
-  } else if (wave < kMainWaves) {
+    x_loader<RT, XS, KC>(p.X, p.xplane, KS, 0, U, xring, wave - kMainWaves - kHelpers, rs, SK);
+    return;
+  }
+  if (wave < kMainWaves) {
     if (wave < p.base) {
       const int unit = w * p.base + wave;
       int tile[T] = {unit, unit};
@@ -464,38 +489,56 @@ __device__ __forceinline__ void bal_cut(const ProjParams& p, char* xring) {
       for (int j = 0; j < T; ++j)
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      proj_core_xw<RT, T, XS, KC, RT, true>(wp, 512, 0, 1, U, xring, acc);
+      proj_core_xw<RT, T, XS, KC, RT, true>(wp, 512, 0, 1, U, xring, acc, 0, rs, SK);
       bal_epilogue<RT, XS, 1, RT>(p, tile, 0, 0, 1, acc);
     } else {
       for (int g = 0; g < G; ++g) wg_barrier();
     }
-  } else if (w < npieces) {
-    const int h = wave - kMainWaves;
-    const int unit = p.base * kCUs + r;
-    const int k0 = part * U / p.pq, k1 = (part + 1) * U / p.pq;
-    const size_t off = ((size_t)unit * KS + (size_t)k0 * kUnit) * 512 + lane * 8;
-    const bf16_t* wp[T] = {p.W0 + off, p.W1 + off};
-    f32x4 acc[T][2];
-#pragma unroll
-    for (int j = 0; j < T; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    proj_core_xw<RT, T, XS, KC, 2, false>(wp, 512, h, 2, k1 - k0, xring, acc, k0 * NC);
-    const auto rs = piece_rsrc(p);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = h + 2 * i;
-      if (t < RT)
-#pragma unroll
-        for (int j = 0; j < T; ++j) piece_store(p, rs, r, part, t, j, acc[j][i]);
-    }
-    for (int g = k1 * NC; g < G; ++g) wg_barrier();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the piece is stored
-  } else {
-    for (int g = 0; g < G; ++g) wg_barrier();
+    return;
   }
-  wg_barrier();                                          // both helpers' pieces are stored
-  if (threadIdx.x == 0) last = w < npieces && piece_arrive(p, r, p.pq);
-  wg_barrier();
-  if (last) piece_combine(p, piece_rsrc(p), r, threadIdx.x, blockDim.x);
+  if (wave != kMainWaves || !cut) {
+    for (int g = 0; g < G; ++g) wg_barrier();
+    return;
+  }
+  // helper 0: the piece, chunks 0 .. (k1 - k0) NC - 1 of the rotated order
+  const int unit = p.base * kCUs + r;
+  const size_t off = ((size_t)unit * KS + (size_t)k0 * kUnit) * 512 + lane * 8;
+  const bf16_t* wp[T] = {p.W0 + off, p.W1 + off};
+  f32x4 acc[T][RT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  proj_core_xw<RT, T, XS, KC, RT, true>(wp, 512, 0, 1, k1 - k0, xring, acc);
+  const auto rsrc = piece_rsrc(p);
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int j = 0; j < T; ++j) piece_store(p, rsrc, r, part, t, j, acc[j][t]);
+  int g = (k1 - k0) * NC;
+  auto pass = [&](int n) {   // n chunk barriers, or as many as are left
+    for (int i = 0; i < n && g < G; ++i, ++g) wg_barrier();
+  };
+  pass(2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the piece is stored
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  pass(2);
+  if (__builtin_amdgcn_readfirstlane(old) == p.pq - 1) {
+    // this piece completed the unit: two (row, four features) items per lane at a time,
+    // loads issued one chunk barrier before their use
+    for (int it0 = 0; it0 < p.R * 4; it0 += 128) {
+      PieceLoads ld[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ld[i] = piece_load(p, rsrc, r, min(it0 + 64 * i + lane, p.R * 4 - 1));
+      pass(1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (it0 + 64 * i + lane < p.R * 4) piece_finish(p, unit, it0 + 64 * i + lane, ld[i]);
+    }
+    if (lane == 0) __hip_atomic_store(p.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  pass(G);
 }
 
 template <int RT, int XS, int EPI>
@@ -566,9 +609,14 @@ __device__ __forceinline__ void direct_piece(const ProjParams& p) {
   piece_store(p, rs, r, part, 0, 0, acc[0]);
   piece_store(p, rs, r, part, 0, 1, acc[1]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the piece is stored
-  int last = 0;
-  if (lane == 0) last = piece_arrive(p, r, p.pq);
-  if (__builtin_amdgcn_readfirstlane(last)) piece_combine(p, rs, r, lane, 64);
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__builtin_amdgcn_readfirstlane(old) == p.pq - 1) {   // this piece completed the unit
+    const int item = min(lane, p.R * 4 - 1);                 // R <= 16: one item per lane
+    const PieceLoads ld = piece_load(p, rs, r, item);
+    if (lane < p.R * 4) piece_finish(p, unit, lane, ld);
+    if (lane == 0) __hip_atomic_store(p.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // R <= 16: one wave per workgroup (T tiles, one split), epilogues as k_proj.  A
@@ -597,7 +645,10 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
   f32x4 acc[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  proj_core_direct<T, XS>(wp, 512, p.X, p.xplane, u0 * kUnit, u1 - u0, p.R, acc);
+  int rs = 0;
+  if constexpr (EPI == 1)
+    if (p.rem > 0) rs = cut_rotation(p, col) * kUnit;   // the K order of the unit's balanced workgroup
+  proj_core_direct<T, XS>(wp, 512, p.X, p.xplane, u0 * kUnit, u1 - u0, p.R, acc, rs, U * kUnit);
   const int r = lane & 15, kq = lane >> 4;
   if (r >= p.R) return;
   if constexpr (EPI == 0) {

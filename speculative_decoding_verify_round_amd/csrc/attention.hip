@@ -63,6 +63,52 @@ __device__ __forceinline__ float col_sum(float v) {
   return a + b;
 }
 
+// ---------------------------------------------------------------- QKV post-processing
+// A bf16 model's attention kernel takes the QKV projection's split partials directly:
+// each value is the sum of the S partials in split order in float64, rounded once to
+// float; q and k are then rotated (rotate-half RoPE, "per-token side inputs such as
+// positions" of the FreeToken issue's "Flow") in float64 and rounded to float, k and v to
+// bf16 for the cache.
+
+// NG groups of four consecutive floats, every split loaded (four splits at a time)
+// before the first addition.
+template <int NG>
+__device__ __forceinline__ void proj_sum(const float* const (&src)[NG], size_t ss, int S, float (&out)[NG][4]) {
+  constexpr int B = 4;
+  double acc[NG][4];
+  for (int s0 = 0; s0 < S; s0 += B) {
+    f32x4 v[B][NG];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int n = 0; n < NG; ++n) v[b][n] = *reinterpret_cast<const f32x4*>(src[n] + (size_t)min(s0 + b, S - 1) * ss);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (s0 + b >= S) break;
+#pragma unroll
+      for (int n = 0; n < NG; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[n][e] = (s0 + b == 0) ? (double)v[b][n][e] : acc[n][e] + (double)v[b][n][e];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NG; ++n)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[n][e] = (float)acc[n][e];
+}
+
+// Two bf16 values in one word, a at the lower address.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// (a, b) = elements i and i + d/2 of one head: rotated by the angle of (cos c, sin sn).
+__device__ __forceinline__ void rotate_half(float& a, float& b, double c, double sn) {
+  const double av = (double)a, bv = (double)b;
+  a = (float)(av * c - bv * sn);
+  b = (float)(bv * c + av * sn);
+}
+
 // bf16 verify attention, one workgroup per (chunk range, kv head, lane).  The
 // workgroup streams its range of chunks as 64-position stages through a
 // kAttnStages-deep LDS ring filled by DMA (three stages in flight while one is
@@ -121,24 +167,19 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
   const float scale = p.scale_log2;
   const char* Kp = reinterpret_cast<const char*>(p.kpool);
   const char* Vp = reinterpret_cast<const char*>(p.vpool);
-  const char* SK = reinterpret_cast<const char*>(p.sk);
-  const char* SV = reinterpret_cast<const char*>(p.sv);
   constexpr int BLOCK_BYTES = kBlock * D * 2;
-
-  // byte offset of absolute block b (head g) in its pool or in the staged blocks; a
-  // block wholly past the lane's end reads staged block 0 (finite, masked)
-  auto block_off = [&](int b, int id) -> size_t {
-    const int sid = kStageBlocks * l + (16 * b < end ? b - b0 : 0);
-    return ((size_t)(b >= b0 ? sid : id) * nkv + g) * BLOCK_BYTES;
-  };
+  // Blocks below b0 are committed cache blocks.  Block b0 and every block after it are
+  // fetched from the lane's boundary cache block (its committed prefix, slots below
+  // kv_len % 16, is exact); the round's own columns are then written into the LDS stage
+  // over it, and V is zeroed at positions past the lane's end (K there is masked).
+  const int blk0 = clamp_blk(bt[min(b0, p.max_blocks - 1)], p.n_blocks);
   // per-lane DMA offsets, fixed for the kernel.  K waves: segment i holds positions
   // 4 i .. 4 i + 3 of block w (stage position p = 16 w + 4 i + lane / 16; LDS chunk
   // lane % 16 receives chunk (lane % 16) ^ f(p)).  V waves: segment i holds rows
   // 32 i .. 32 i + 31 of block w - 4 (lane t: row t / 2, LDS half t & 1 receives half
   // (t & 1) ^ (row / 4 & 1)).
   const int bw = wave & 3;                    // the block this wave copies
-  const char* pool = h ? Vp : Kp;             // its committed pool and its staged blocks
-  const char* stg = h ? SV : SK;
+  const char* pool = h ? Vp : Kp;             // its pool
   uint32_t off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -151,14 +192,16 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
   auto issue = [&](int t) {
     char* dst = ring + (t % NS) * SBYTES + h * KBYTES + 4096 * bw;
     const int b = fb + 4 * t + bw;
-    const int id = __builtin_amdgcn_readfirstlane(b < b0 ? sblk[b - fb] : 0);
-    const char* src = (b >= b0 ? stg : pool) + block_off(b, id);
+    const int id = __builtin_amdgcn_readfirstlane(b < b0 ? sblk[b - fb] : blk0);
+    const char* src = pool + ((size_t)id * nkv + g) * BLOCK_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16<true>(src, off[i], dst + 1024 * i);
   };
 
-  // block ids of the range and the wave's queries (bf16 hi + lo planes, the B operands):
-  // every load is issued unconditionally from a valid address before any is used
+  // ---- prologue, one round trip before the first DMA (the compiler's waits for these
+  // loads do not count the DMAs, so every load is consumed before the first DMA): the
+  // block ids of the range; for workgroups whose range reaches position kv_len, the
+  // round's own columns; the wave's queries
   constexpr int IPT = kAttnWgBlocks / 512;
   const int ncommit = min(4 * T, b0 - fb);
   int idv[IPT];
@@ -167,21 +210,133 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
     const int i = min(tid + 512 * k, max(ncommit - 1, 0));   // fb + i < max_blocks
     idv[k] = bt[fb + i];
   }
-  const int m = 16 * qtile + r16;              // the lane's query row
-  f32x4 qraw[8];
-  {
-    const int mc = min(m, Mq - 1);
-    const int j = mc / p.G, hh = mc - j * p.G;
-    const float* ptr = p.q + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D + kq * 8;
+  const int N = (p.nq + 2 * nkv) * D;
+  const size_t ss = (size_t)p.ri.R * N;
+  // own columns: item k of this thread (k = 0, 1) is (column j, rotation pairs i0 .. i0 + 3
+  // of K) for items below cols 16, then (column j, elements i0 .. i0 + 3 of V); the split
+  // partials of up to four splits are requested here, summed after the queries
+  const bool own = min(c1 * p.chunk, end) > kvl;
+  const int nownk = cols * 16, nown = cols * 48;
+  constexpr int OB = 4;                        // splits requested up front
+  f32x4 ownraw[2][2][OB];
+  auto own_item = [&](int it, bool& isk, int& j, int& i0) {
+    isk = it < nownk;
+    const int jt = isk ? it : it - nownk, per = isk ? 16 : 32;
+    j = jt / per;
+    i0 = 4 * (jt - j * per);
+  };
+  auto own_src = [&](int it, int half) -> const float* {
+    bool isk;
+    int j, i0;
+    own_item(it, isk, j, i0);
+    const float* row = p.P + (size_t)(rs + j) * N;
+    return isk ? row + (size_t)(p.nq + g) * D + i0 + half * (D / 2) : row + (size_t)(p.nq + nkv + g) * D + i0;
+  };
+  if (own) {
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      qraw[2 * ds] = *reinterpret_cast<const f32x4*>(ptr + ds * 32);
-      qraw[2 * ds + 1] = *reinterpret_cast<const f32x4*>(ptr + ds * 32 + 4);
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && nown <= 512) break;        // one item per thread
+      const int it = min(tid + 512 * k, nown - 1);
+      const int nh = it < nownk ? 2 : 1;       // K items read both halves of the head
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+          if (hf < nh) ownraw[k][hf][b] = *reinterpret_cast<const f32x4*>(own_src(it, hf) + (size_t)min(b, p.S - 1) * ss);
+    }
+  }
+  // queries, each element once per workgroup: item it (two per thread) = (query row mr,
+  // rotation pairs i0 .. i0 + 3); the float32 queries go to ring slot NS - 1 (untouched
+  // until the loop's first barrier), float4 group c of row mr at c ^ (mr & 31)
+  float* qs = reinterpret_cast<float*>(ring + (NS - 1) * SBYTES);   // [64][128] floats
+  float qv[2][2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int it = min(tid + 512 * k, Mq * 16 - 1);
+    const int mr = it >> 4, i0 = 4 * (it & 15);
+    const int jr = mr / p.G, hr = mr - jr * p.G;
+    const float* row = p.P + (size_t)(rs + jr) * N + (size_t)(g * p.G + hr) * D + i0;
+    const float* src[2] = {row, row + D / 2};
+    proj_sum<2>(src, ss, p.S, qv[k]);
+    if (p.rope) {
+      const double* rt = p.rope + ((size_t)(rs + jr) * (D / 2) + i0) * 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rotate_half(qv[k][0][e], qv[k][1][e], rt[2 * e], rt[2 * e + 1]);
+    }
+  }
+  // own columns: sums in split order in float64 (splits past OB requested now), rotation,
+  // bf16; held in registers until the column's stage is in LDS
+  u32x4 ownv[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  if (own) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && nown <= 512) break;
+      const int it = tid + 512 * k;
+      bool isk;
+      int j, i0;
+      own_item(min(it, nown - 1), isk, j, i0);
+      float v[2][4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if (hf == 1 && !isk) break;
+        double a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (double)ownraw[k][hf][0][e];
+#pragma unroll
+        for (int b = 1; b < OB; ++b)
+          if (b < p.S)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] += (double)ownraw[k][hf][b][e];
+        for (int b = OB; b < p.S; ++b) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(own_src(min(it, nown - 1), hf) + (size_t)b * ss);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] += (double)w[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[hf][e] = (float)a[e];
+      }
+      if (isk && p.rope) {
+        const double* rt = p.rope + ((size_t)(rs + j) * (D / 2) + i0) * 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rotate_half(v[0][e], v[1][e], rt[2 * e], rt[2 * e + 1]);
+      }
+      ownv[k] = isk ? u32x4{pack_bf16(v[0][0], v[0][1]), pack_bf16(v[0][2], v[0][3]), pack_bf16(v[1][0], v[1][1]),
+                            pack_bf16(v[1][2], v[1][3])}
+                    : u32x4{pack_bf16(v[0][0], v[0][1]), pack_bf16(v[0][2], v[0][3]), 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int it = tid + 512 * k;
+    if (it < Mq * 16) {
+      const int mr = it >> 4, c = it & 15;   // float4 groups c (pairs 4c ..) and c + 16 (their partners)
+      *reinterpret_cast<f32x4*>(qs + mr * D + 4 * (c ^ (mr & 31))) =
+          f32x4{qv[k][0][0], qv[k][0][1], qv[k][0][2], qv[k][0][3]};
+      *reinterpret_cast<f32x4*>(qs + mr * D + 4 * ((c + 16) ^ (mr & 31))) =
+          f32x4{qv[k][1][0], qv[k][1][1], qv[k][1][2], qv[k][1][3]};
     }
   }
 #pragma unroll
   for (int k = 0; k < IPT; ++k)
     if (tid + 512 * k < ncommit) sblk[tid + 512 * k] = clamp_blk(idv[k], p.n_blocks);
+  if (own) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) asm volatile("" ::"v"(ownv[k]));
+  }
+  wg_barrier();   // block ids and queries staged
+  for (int t = 0; t < NS - 1 && t < T; ++t) issue(t);
+  // the wave's queries: elements kq 8 + 32 ds + e of row m (float4 groups 2 kq + 8 ds and
+  // + 1), read back before the loop's first barrier frees slot NS - 1 for the DMAs
+  const int m = 16 * qtile + r16;              // the lane's query row
+  f32x4 qraw[8];
+  {
+    const int mc = min(m, Mq - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = 2 * kq + 8 * (i >> 1) + (i & 1);
+      qraw[i] = *reinterpret_cast<const f32x4*>(qs + mc * D + 4 * (c ^ (mc & 31)));
+    }
+  }
   const bool valid = m < Mq;
   const int lim = valid ? kvl + m / p.G : -1;  // last position the row attends to
   u32x4 qh[4], ql[4];
@@ -197,12 +352,53 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
       ql[ds][i] = valid ? lw : 0u;
     }
   }
-  // the compiler's waits for the loads above must precede the first DMA (its counts
-  // do not include the DMAs): consume every query register here
+
+  // Writes the own columns of stage t (positions s0 .. s0 + 63) into its ring slot and
+  // zeroes V past the lane's end; the caller's barrier publishes them.
+  auto patch = [&](int t) {
+    const int s0 = first + STEP * t;
+    char* sK = ring + (t % NS) * SBYTES;
+    char* sV = sK + KBYTES;
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) asm volatile("" ::"v"(qh[ds]), "v"(ql[ds]));
-  wg_barrier();   // block ids staged
-  for (int t = 0; t < NS - 1 && t < T; ++t) issue(t);
+    for (int k = 0; k < 2; ++k) {
+      const int it = tid + 512 * k;
+      if (it >= nown) continue;
+      const bool isk = it < nownk;
+      const int jt = isk ? it : it - nownk, per = isk ? 16 : 32;
+      const int j = jt / per, i0 = 4 * (jt - j * per);
+      const int ps = kvl + j - s0;
+      if (ps < 0 || ps >= STEP) continue;
+      if (isk) {
+        const int f = (ps & 3) | (((ps >> 3) & 3) << 2), c = i0 >> 3, o = (i0 & 7) * 2;
+        *reinterpret_cast<u32x2*>(sK + ps * 256 + ((c ^ f) << 4) + o) = u32x2{ownv[k][0], ownv[k][1]};
+        *reinterpret_cast<u32x2*>(sK + ps * 256 + (((8 + c) ^ f) << 4) + o) = u32x2{ownv[k][2], ownv[k][3]};
+      } else {
+        const int bb = ps >> 4, sl = ps & 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = i0 + e;
+          const uint32_t w = ownv[k][e >> 1];
+          *reinterpret_cast<bf16_t*>(sV + bb * 4096 + d * 32 + (((sl >> 3) ^ ((d >> 2) & 1)) << 4) + (sl & 7) * 2) =
+              (bf16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        }
+      }
+    }
+    // V rows past the end: thread = (block bb of the stage, row d)
+    {
+      const int bb = tid >> 7, d = tid & 127;
+      const int sz = min(max(end - (s0 + 16 * bb), 0), 16);   // first slot to zero
+      char* vrow = sV + bb * 4096 + d * 32;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        char* half = vrow + ((hs ^ ((d >> 2) & 1)) << 4);
+        if (8 * hs >= sz) {
+          *reinterpret_cast<u32x4*>(half) = u32x4{0u, 0u, 0u, 0u};
+        } else if (8 * hs + 8 > sz) {
+          for (int e = sz - 8 * hs; e < 8; ++e) *reinterpret_cast<bf16_t*>(half + 2 * e) = (bf16_t)0;
+        }
+      }
+    }
+  };
 
   // running max (raw score units), this lane's part of the row sum, O^T[16 dt + 4 kq + e][m]
   float mrun = -INFINITY, lrun = 0.f;
@@ -297,6 +493,10 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
     }
     wg_barrier();                            // stage t is in LDS; stage t - 1 is consumed
     if (t + NS - 1 < T) issue(t + NS - 1);   // into the slot stage t - 1 used
+    if (own && first + STEP * t + STEP > kvl) {
+      patch(t);
+      wg_barrier();                          // the own columns are in the stage
+    }
     if (active) compute(t);
     if (t % cs == cs - 1 || t == T - 1) {
       // chunk end: half 1 hands its (O, max, sum) to half 0 through the slot of stage t
@@ -338,6 +538,34 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
       lrun = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // the own columns' K and V for the commit: staged block (kv_len % 16 + j) / 16, slot
+  // (kv_len % 16 + j) % 16, in the cache's block layout
+  if (own) {
+    bf16_t* SKg = reinterpret_cast<bf16_t*>(const_cast<void*>(p.sk));
+    bf16_t* SVg = reinterpret_cast<bf16_t*>(const_cast<void*>(p.sv));
+    const int pre = kvl & 15;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = tid + 512 * k;
+      if (it >= nown) continue;
+      const bool isk = it < nownk;
+      const int jt = isk ? it : it - nownk, per = isk ? 16 : 32;
+      const int j = jt / per, i0 = 4 * (jt - j * per);
+      const int slot = pre + j, sl = slot & 15;
+      const size_t sb = (size_t)kStageBlocks * l + (slot >> 4);
+      if (isk) {
+        bf16_t* dst = SKg + ((sb * nkv + g) * kBlock + sl) * D + i0;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{ownv[k][0], ownv[k][1]};
+        *reinterpret_cast<u32x2*>(dst + D / 2) = u32x2{ownv[k][2], ownv[k][3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = ownv[k][e >> 1];
+          SVg[((sb * nkv + g) * D + i0 + e) * kBlock + sl] = (bf16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        }
+      }
     }
   }
 }

@@ -361,6 +361,11 @@ struct AttnParams {
   float scale_log2;       // log2(e) / sqrt(d)
   float* part;            // [L][nkv][n_chunks] slots of 64 rows x (d + kAttnPartPad) floats, part_index order
   RowInfo ri;
+  // bf16 model: the attention kernel forms the queries and the staged columns itself from
+  // the QKV projection's split partials (null: q, sk and sv are already written)
+  const float* P;         // [S][R][(nq + 2 nkv) d]
+  int S;
+  const double* rope;     // [R][d / 2] (cos, sin) in float64, or null (no positional encoding)
 };
 
 }  // namespace sv

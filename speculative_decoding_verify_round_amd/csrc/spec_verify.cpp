@@ -302,9 +302,16 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       ap.q = q; ap.sk = sk; ap.sv = svp;
       ap.kpool = reinterpret_cast<const char*>(r->k_pool) + (size_t)L.attn_index * apool;
       ap.vpool = reinterpret_cast<const char*>(r->v_pool) + (size_t)L.attn_index * apool;
-      const sv::KvStage ks{r->kv_len, r->block_table, r->max_blocks, r->n_blocks, ap.kpool, ap.vpool};
-      SV_CHECK(sv::launch_qkv_post(P, S_in, at<double>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ks, ri, bf,
-                                   st));
+      if (bf) {
+        // the attention kernel sums the QKV partials, rotates and stages the columns itself
+        ap.P = P;
+        ap.S = S_in;
+        ap.rope = rope ? at<double>(ws, w.rope) : nullptr;
+      } else {
+        const sv::KvStage ks{r->kv_len, r->block_table, r->max_blocks, r->n_blocks, ap.kpool, ap.vpool};
+        SV_CHECK(sv::launch_qkv_post(P, S_in, at<double>(ws, w.rope), rope ? 1 : 0, nq, nkv, hd, q, sk, svp, ks, ri,
+                                     bf, st));
+      }
       ap.block_table = r->block_table; ap.max_blocks = r->max_blocks; ap.n_blocks = r->n_blocks;
       ap.kv_len = r->kv_len;
       ap.nq = nq; ap.nkv = nkv; ap.G = nq / nkv; ap.d = hd;

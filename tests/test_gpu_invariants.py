@@ -14,7 +14,7 @@ import torch
 
 import synth
 from gpu_helpers import log
-from helpers import small_hybrid
+from helpers import small_dense, small_hybrid
 from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel
 
 pytestmark = pytest.mark.gpu
@@ -132,3 +132,17 @@ def test_rejected_columns_leave_no_trace(dev):
     Kb = before_k[0][[int(dev.bt[0][(dev.context + 2 + j) // 16]) for j in range(4)], :,
                      [(dev.context + 2 + j) % 16 for j in range(4)], :].float().cpu().numpy()
     assert np.array_equal(K, Kb)
+
+
+def test_rows_bitwise_across_projection_kernels():
+    # FFN 5120 over K 1024: 320 gate/up units = 256 whole ones + 64 cut into 4 K pieces
+    cfg = small_dense(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=5120, vocab=2048, context=300)
+    d = Dev(cfg, lanes=4, context=300, max_blocks=24)
+    try:
+        toks = [[1 + 9 * l + j for j in range(6)] for l in range(4)]
+        many = _logits(d.dc, toks)                       # 24 rows: eight-wave kernels
+        one = _logits(d.fresh(lane_ids=[2]), [toks[2]])  # 6 rows: one-wave kernels
+        assert np.array_equal(many[12:18], one)
+        log("lane 2: 24-row and 6-row rounds give the same bits")
+    finally:
+        d.dm.close()

@@ -250,6 +250,35 @@ int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float
 int64_t spec_packed_weight_bytes(int N, int K);
 int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream);
 
+/* Copy-from-the-conversation drafter (n-gram prompt lookup): "Speculative decoding",
+ * mashbox docs, "Where it runs" (--speculation ngram: the drafter looks up the last few
+ * tokens earlier in the request and proposes the tokens that followed them there).
+ * history: device int32 [lanes][max_len], lane l's tokens so far in history[l][0 ..
+ * hist_len[l]), the last one being the lane's anchor (the token at position kv_len).
+ * For n = n_max down to n_min the suffix of length n is looked up; the most recent
+ * earlier occurrence (largest p with p + n < len) of the longest suffix that recurs is
+ * copied: draft i is the token at p + n + i of the history extended by the drafts (a
+ * copy that reaches the end goes on over what it has just proposed).  Output, device:
+ * tokens [lanes][k + 1] = the anchor, then k drafts (the anchor repeated when no suffix
+ * recurs, so every lane keeps k + 1 columns), lane-major as spec_round.tokens expects;
+ * n_match [lanes] = the matched n, 0 for none.  A lane with hist_len < 1 gets token 0
+ * columns.  1 <= lanes <= SPEC_MAX_LANES, 0 <= k < SPEC_MAX_COLS,
+ * 1 <= n_min <= n_max <= SPEC_MAX_NGRAM, max_len >= 1, else SPEC_E_INVAL.  All buffers
+ * are the caller's; the call only enqueues work on the stream. */
+#define SPEC_MAX_NGRAM 8
+int spec_ngram_draft(const int32_t* history, const int32_t* hist_len, int lanes, int max_len, int k,
+                     int n_max, int n_min, int32_t* tokens, int32_t* n_match, void* stream);
+
+/* The history update of a multi-round loop (the round's committed run, "One round, step
+ * by step", ignis, step 5): after spec_accept and spec_commit, lane l's out_tokens[l][0
+ * .. committed[l]) (device, row stride out_stride) are appended to history[l] and
+ * hist_len[l] grows by committed[l], both capped at max_len.  Device buffers, the
+ * caller's; lanes in [1, SPEC_MAX_LANES], out_stride >= 1, else SPEC_E_INVAL.  With
+ * spec_ngram_draft this makes a loop of rounds that never waits for the host. */
+int spec_history_append(int32_t* history, int32_t* hist_len, int lanes, int max_len,
+                        const int32_t* committed, const int32_t* out_tokens, int out_stride,
+                        void* stream);
+
 /* Measurement: record HIP events around launches 0, every, 2 every, ... of one
  * kernel class, counted from this call (SPEC_K_NONE stops recording; every >= 1,
  * else SPEC_E_INVAL), and read back the summed duration and the number of the

@@ -14,7 +14,9 @@ computes, written from the pages' description of the method:
     (Leviathan, Kalman & Matias 2022, Definition 3.7 / Theorem 3.8);
   * the FreeToken tracking issue, "Per-request state": verify reads the live
     recurrent state and stages scratch, commit rolls the state to the accepted
-    count.
+    count;
+  * "Speculative decoding" (mashbox docs, "Where it runs"): the copy-from-the-
+    conversation drafter (n-gram prompt lookup).
 
 Every dot product and reduction is accumulated in float64 and rounded once to
 float32; values are rounded to bf16 exactly where a bf16 model stores them.
@@ -29,3 +31,4 @@ from .model import OracleModel, KVCache, RoundResult  # noqa: F401
 from .accept import (  # noqa: F401
     row_stats, accept_greedy, accept_sampled, rule_outcomes, one_position_output,
 )
+from .ngram import ngram_draft, round_tokens, speculative_greedy_ngram  # noqa: F401

@@ -27,8 +27,9 @@ HEADER_SYMBOLS = (
     "spec_status_string", "spec_plan_drafts", "spec_model_create", "spec_model_destroy",
     "spec_workspace_bytes", "spec_verify_round", "spec_verify_head", "spec_accept", "spec_commit",
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
-    "spec_profile_enable", "spec_profile_collect",
+    "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
 )
+SPEC_MAX_NGRAM = 8
 
 
 class SpecError(RuntimeError):
@@ -107,6 +108,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_profile_enable.argtypes = [C.c_void_p, C.c_int, C.c_int]
         lib.spec_profile_collect.restype = C.c_int
         lib.spec_profile_collect.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int)]
+        lib.spec_ngram_draft.restype = C.c_int
+        lib.spec_ngram_draft.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                         C.c_void_p, C.c_void_p, C.c_void_p]
+        lib.spec_history_append.restype = C.c_int
+        lib.spec_history_append.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int,
+                                            C.c_void_p]
         _lib = lib
     return _lib
 
@@ -190,3 +197,17 @@ def spec_profile_collect(model):
     n = C.c_int()
     _check(load_library().spec_profile_collect(model, C.byref(t), C.byref(n)), "spec_profile_collect")
     return t.value, n.value
+
+
+def spec_ngram_draft(history_ptr: int, hist_len_ptr: int, lanes: int, max_len: int, k: int, n_max: int, n_min: int,
+                     tokens_ptr: int, n_match_ptr: int, stream: int) -> None:
+    _check(load_library().spec_ngram_draft(C.c_void_p(history_ptr), C.c_void_p(hist_len_ptr), lanes, max_len, k,
+                                           n_max, n_min, C.c_void_p(tokens_ptr), C.c_void_p(n_match_ptr),
+                                           C.c_void_p(stream)), "spec_ngram_draft")
+
+
+def spec_history_append(history_ptr: int, hist_len_ptr: int, lanes: int, max_len: int, committed_ptr: int,
+                        out_tokens_ptr: int, out_stride: int, stream: int) -> None:
+    _check(load_library().spec_history_append(C.c_void_p(history_ptr), C.c_void_p(hist_len_ptr), lanes, max_len,
+                                              C.c_void_p(committed_ptr), C.c_void_p(out_tokens_ptr), out_stride,
+                                              C.c_void_p(stream)), "spec_history_append")

@@ -12,6 +12,7 @@ constexpr int kBlock = 16;       // tokens per paged-KV block
 constexpr int kWave = 64;
 constexpr int kMaxChunk = 4096;     // largest split-KV attention chunk (positions)
 constexpr int kAttnPartPad = 4;     // a chunk partial row: O[d], then m and l, then 2 pad floats
+constexpr int kMaxNgram = 8;          // longest suffix the n-gram drafter looks up (SPEC_MAX_NGRAM)
 constexpr int kCUs = 256;           // compute units of an MI355X (workgroup slots of one-per-CU launches)
 // The round's own K/V columns are staged per lane in kStageBlocks cache-layout blocks
 // aligned to absolute positions: staged block v of lane l covers positions

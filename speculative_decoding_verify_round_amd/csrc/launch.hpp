@@ -47,6 +47,12 @@ int launch_kvlen_update(const int32_t* committed, int32_t* kv_len, const RowInfo
 int launch_sum_partials(const float* P, int S, size_t n, float* Y, hipStream_t st);
 int launch_copy_rows(const void* src, void* dst, size_t bytes, hipStream_t st);
 
+// n-gram drafter and the history of a multi-round loop
+int launch_ngram_draft(const int32_t* hist, const int32_t* hist_len, int lanes, int max_len, int k, int n_max,
+                       int n_min, int32_t* tokens, int32_t* n_match, hipStream_t st);
+int launch_history_append(int32_t* hist, int32_t* hist_len, int lanes, int max_len, const int32_t* committed,
+                          const int32_t* out_tokens, int out_stride, hipStream_t st);
+
 // acceptance
 int launch_row_reduce(const LmPartial* part, int groups, int R, float inv_t, RowStat* rs, void* user_stats,
                       hipStream_t st);

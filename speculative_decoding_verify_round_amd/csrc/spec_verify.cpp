@@ -611,6 +611,29 @@ int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream) {
   return sv::launch_pack_weight(src, dst, N, K, reinterpret_cast<hipStream_t>(stream)) ? SPEC_E_HIP : SPEC_OK;
 }
 
+static_assert(SPEC_MAX_NGRAM == sv::kMaxNgram, "n-gram bound of the header and the kernels");
+
+int spec_ngram_draft(const int32_t* history, const int32_t* hist_len, int lanes, int max_len, int k, int n_max,
+                     int n_min, int32_t* tokens, int32_t* n_match, void* stream) {
+  if (!history || !hist_len || !tokens || !n_match) return SPEC_E_INVAL;
+  if (lanes < 1 || lanes > SPEC_MAX_LANES || max_len < 1 || k < 0 || k >= SPEC_MAX_COLS) return SPEC_E_INVAL;
+  if (n_min < 1 || n_max < n_min || n_max > SPEC_MAX_NGRAM) return SPEC_E_INVAL;
+  return sv::launch_ngram_draft(history, hist_len, lanes, max_len, k, n_max, n_min, tokens, n_match,
+                                reinterpret_cast<hipStream_t>(stream))
+             ? SPEC_E_HIP
+             : SPEC_OK;
+}
+
+int spec_history_append(int32_t* history, int32_t* hist_len, int lanes, int max_len, const int32_t* committed,
+                        const int32_t* out_tokens, int out_stride, void* stream) {
+  if (!history || !hist_len || !committed || !out_tokens) return SPEC_E_INVAL;
+  if (lanes < 1 || lanes > SPEC_MAX_LANES || max_len < 1 || out_stride < 1) return SPEC_E_INVAL;
+  return sv::launch_history_append(history, hist_len, lanes, max_len, committed, out_tokens, out_stride,
+                                   reinterpret_cast<hipStream_t>(stream))
+             ? SPEC_E_HIP
+             : SPEC_OK;
+}
+
 int spec_profile_enable(spec_model* m, int kernel_class, int every) {
   if (!m || kernel_class < SPEC_K_NONE || kernel_class >= SPEC_K_COUNT || every < 1) return SPEC_E_INVAL;
   m->prof_class = kernel_class;

@@ -195,3 +195,27 @@ def test_pack_weight_sizes_and_validation():
     assert lib.spec_pack_weight(None, FAKE, 16, 256, None) == B.SPEC_E_INVAL
     assert lib.spec_pack_weight(FAKE, FAKE, 16, 256, None) == B.SPEC_E_INVAL      # in place
     assert lib.spec_pack_weight(FAKE, FAKE + 64, 16, 100, None) == B.SPEC_E_INVAL
+
+
+def test_ngram_calls_validate():
+    """The drafter and history calls refuse bad sizes and null buffers before any HIP call."""
+    lib = B.load_library()
+    bad = [
+        (None, FAKE, 2, 64, 3, 3, 1, FAKE, FAKE, None),
+        (FAKE, FAKE, 0, 64, 3, 3, 1, FAKE, FAKE, None),              # lanes
+        (FAKE, FAKE, B.SPEC_MAX_LANES + 1, 64, 3, 3, 1, FAKE, FAKE, None),
+        (FAKE, FAKE, 2, 0, 3, 3, 1, FAKE, FAKE, None),               # max_len
+        (FAKE, FAKE, 2, 64, -1, 3, 1, FAKE, FAKE, None),             # k
+        (FAKE, FAKE, 2, 64, B.SPEC_MAX_COLS, 3, 1, FAKE, FAKE, None),
+        (FAKE, FAKE, 2, 64, 3, 3, 0, FAKE, FAKE, None),              # n_min
+        (FAKE, FAKE, 2, 64, 3, 2, 3, FAKE, FAKE, None),              # n_max < n_min
+        (FAKE, FAKE, 2, 64, 3, B.SPEC_MAX_NGRAM + 1, 1, FAKE, FAKE, None),
+        (FAKE, FAKE, 2, 64, 3, 3, 1, None, FAKE, None),
+    ]
+    for args in bad:
+        assert lib.spec_ngram_draft(*args) == B.SPEC_E_INVAL, args
+    assert lib.spec_history_append(None, FAKE, 2, 64, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_history_append(FAKE, FAKE, 0, 64, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_history_append(FAKE, FAKE, 2, 0, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_history_append(FAKE, FAKE, 2, 64, FAKE, FAKE, 0, None) == B.SPEC_E_INVAL
+    assert lib.spec_history_append(FAKE, FAKE, 2, 64, None, FAKE, 16, None) == B.SPEC_E_INVAL

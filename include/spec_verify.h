@@ -279,6 +279,35 @@ int spec_history_append(int32_t* history, int32_t* hist_len, int lanes, int max_
                         const int32_t* committed, const int32_t* out_tokens, int out_stride,
                         void* stream);
 
+/* Per-request miss back-off of a drafter, host side ("Speculative decoding", mashbox
+ * docs, "What it does for you": a request whose guesses keep missing stops guessing for
+ * a while).  The engine runs several passes (verify rounds) per device call and decides
+ * once per call who guesses:
+ *  - spec_backoff_call at the start of a call: a request may guess unless it is waiting;
+ *    the call speculates (returns 1, else 0) when some request may guess and the row
+ *    budget (spec_plan_drafts(k, row_budget, n), n counting every active request)
+ *    leaves it a draft; drafts[i] = that plan for a request that may guess in a call that
+ *    speculates, 0 otherwise;
+ *  - spec_backoff_pass after each pass of the call, kept[i] = the request's drafts the
+ *    model kept (committed - 1).  In a call that speculates, every pass counts for each
+ *    request that may guess: 4 passes in a row that keep nothing start a wait of 16
+ *    passes (the count starts again), each further such 4 double it up to 256, and a pass
+ *    that keeps a guess clears the count and sets the wait back to 16 -- unless the
+ *    request is waiting: the rest of the call in which a wait began still guesses and
+ *    its passes count toward the wait.  Every other pass only shortens a running wait.
+ * States are caller-owned host memory, n in [1, SPEC_MAX_LANES]; spec_backoff_init sets
+ * them to "not waiting, next wait 16".  Pure host functions (no device work); bad
+ * arguments return SPEC_E_INVAL and change nothing. */
+typedef struct {
+  int32_t miss_run;    /* counted passes in a row that kept nothing, since the last wait began */
+  int32_t wait_len;    /* length of the next wait, 16 .. 256 */
+  int32_t wait_left;   /* passes of the current wait still to go, 0 when not waiting */
+  int32_t may_guess;   /* 1 if the request may guess in the current call */
+} spec_backoff;
+int spec_backoff_init(spec_backoff* states, int n);
+int spec_backoff_call(spec_backoff* states, int n, int k, int row_budget, int32_t* drafts);
+int spec_backoff_pass(spec_backoff* states, int n, const int32_t* kept, int speculates);
+
 /* Measurement: record HIP events around launches 0, every, 2 every, ... of one
  * kernel class, counted from this call (SPEC_K_NONE stops recording; every >= 1,
  * else SPEC_E_INVAL), and read back the summed duration and the number of the

@@ -28,8 +28,14 @@ HEADER_SYMBOLS = (
     "spec_workspace_bytes", "spec_verify_round", "spec_verify_head", "spec_accept", "spec_commit",
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
     "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
+    "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass",
 )
 SPEC_MAX_NGRAM = 8
+
+
+class SpecBackoff(C.Structure):
+    """Mirror of spec_backoff (one request's miss back-off state)."""
+    _fields_ = [("miss_run", C.c_int32), ("wait_len", C.c_int32), ("wait_left", C.c_int32), ("may_guess", C.c_int32)]
 
 
 class SpecError(RuntimeError):
@@ -111,6 +117,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_ngram_draft.restype = C.c_int
         lib.spec_ngram_draft.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                          C.c_void_p, C.c_void_p, C.c_void_p]
+        lib.spec_backoff_init.restype = C.c_int
+        lib.spec_backoff_init.argtypes = [C.c_void_p, C.c_int]
+        lib.spec_backoff_call.restype = C.c_int
+        lib.spec_backoff_call.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
+        lib.spec_backoff_pass.restype = C.c_int
+        lib.spec_backoff_pass.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int]
         lib.spec_history_append.restype = C.c_int
         lib.spec_history_append.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int,
                                             C.c_void_p]
@@ -211,3 +223,15 @@ def spec_history_append(history_ptr: int, hist_len_ptr: int, lanes: int, max_len
     _check(load_library().spec_history_append(C.c_void_p(history_ptr), C.c_void_p(hist_len_ptr), lanes, max_len,
                                               C.c_void_p(committed_ptr), C.c_void_p(out_tokens_ptr), out_stride,
                                               C.c_void_p(stream)), "spec_history_append")
+
+
+def spec_backoff_init(states, n: int) -> None:
+    _check(load_library().spec_backoff_init(states, n), "spec_backoff_init")
+
+
+def spec_backoff_call(states, n: int, k: int, row_budget: int, drafts) -> bool:
+    return bool(_check(load_library().spec_backoff_call(states, n, k, row_budget, drafts), "spec_backoff_call"))
+
+
+def spec_backoff_pass(states, n: int, kept, speculates: bool) -> None:
+    _check(load_library().spec_backoff_pass(states, n, kept, int(speculates)), "spec_backoff_pass")

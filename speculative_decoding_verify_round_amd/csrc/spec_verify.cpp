@@ -611,6 +611,49 @@ int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream) {
   return sv::launch_pack_weight(src, dst, N, K, reinterpret_cast<hipStream_t>(stream)) ? SPEC_E_HIP : SPEC_OK;
 }
 
+// ---------------------------------------------------------------- miss back-off (host)
+constexpr int kMissPasses = 4, kFirstWait = 16, kMaxWait = 256;
+
+int spec_backoff_init(spec_backoff* st, int n) {
+  if (!st || n < 1 || n > SPEC_MAX_LANES) return SPEC_E_INVAL;
+  for (int i = 0; i < n; ++i) st[i] = spec_backoff{0, kFirstWait, 0, 1};
+  return SPEC_OK;
+}
+
+int spec_backoff_call(spec_backoff* st, int n, int k, int row_budget, int32_t* drafts) {
+  if (!st || !drafts || n < 1 || n > SPEC_MAX_LANES) return SPEC_E_INVAL;
+  const int plan = spec_plan_drafts(k, row_budget, n);
+  if (plan < 0) return plan;
+  bool any = false;
+  for (int i = 0; i < n; ++i) {
+    st[i].may_guess = st[i].wait_left == 0;
+    any = any || st[i].may_guess;
+  }
+  const bool speculates = any && plan > 0;
+  for (int i = 0; i < n; ++i) drafts[i] = speculates && st[i].may_guess ? plan : 0;
+  return speculates ? 1 : 0;
+}
+
+int spec_backoff_pass(spec_backoff* st, int n, const int32_t* kept, int speculates) {
+  if (!st || !kept || n < 1 || n > SPEC_MAX_LANES) return SPEC_E_INVAL;
+  for (int i = 0; i < n; ++i) {
+    spec_backoff& s = st[i];
+    if (speculates && s.may_guess && s.wait_left == 0) {
+      if (kept[i] > 0) {          // a kept guess: the count clears, the next wait is 16 again
+        s.miss_run = 0;
+        s.wait_len = kFirstWait;
+      } else if (++s.miss_run == kMissPasses) {
+        s.miss_run = 0;
+        s.wait_left = s.wait_len;
+        s.wait_len = std::min(2 * s.wait_len, kMaxWait);
+      }
+    } else if (s.wait_left > 0) {  // waiting: the pass counts toward the wait, kept or not
+      --s.wait_left;
+    }
+  }
+  return SPEC_OK;
+}
+
 static_assert(SPEC_MAX_NGRAM == sv::kMaxNgram, "n-gram bound of the header and the kernels");
 
 int spec_ngram_draft(const int32_t* history, const int32_t* hist_len, int lanes, int max_len, int k, int n_max,

@@ -157,6 +157,17 @@ typedef struct {
   uint64_t seed;               /* Philox4x32-10 key */
   void* workspace;             /* device, >= spec_workspace_bytes; 256-byte aligned */
   size_t workspace_bytes;
+  /* Per-row presence and frequency penalties (the FreeToken issue, "Design": per-row
+   * penalties in target-side verify).  counts: device int32 [lanes][vocab], each lane's
+   * token counts up to and including its anchor, or NULL for no penalties.  Row j of a
+   * lane conditions on those tokens and on its drafts d_1 .. d_j, so a token seen c times
+   * there loses presence * [c > 0] + frequency * c from its logit before every statistic
+   * and decision (argmax, softmax at T, the textbook rule, the residual and bonus draws).
+   * With counts, both penalties must be finite, else SPEC_E_INVAL.  spec_counts_add
+   * keeps counts current after each commit. */
+  const int32_t* counts;
+  float presence_penalty;
+  float frequency_penalty;
 } spec_round;
 
 /* Per-row statistics of the LM head (T = 1 in greedy mode). */
@@ -249,6 +260,14 @@ int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float
  * the stream. */
 int64_t spec_packed_weight_bytes(int N, int K);
 int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream);
+
+/* counts[l][t] += 1 for every token t of lane l's committed run, out_tokens[l][0 ..
+ * committed[l]) (device, row stride out_stride), after spec_accept: the counts that
+ * spec_round.counts expects for the next round (tokens up to the new anchor).  Tokens
+ * outside [0, vocab) are skipped.  Device buffers, the caller's; lanes in [1,
+ * SPEC_MAX_LANES], vocab >= 1, out_stride >= 1, else SPEC_E_INVAL. */
+int spec_counts_add(int32_t* counts, int vocab, int lanes, const int32_t* committed,
+                    const int32_t* out_tokens, int out_stride, void* stream);
 
 /* Copy-from-the-conversation drafter (n-gram prompt lookup): "Speculative decoding",
  * mashbox docs, "Where it runs" (--speculation ngram: the drafter looks up the last few

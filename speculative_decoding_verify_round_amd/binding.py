@@ -28,7 +28,7 @@ HEADER_SYMBOLS = (
     "spec_workspace_bytes", "spec_verify_round", "spec_verify_head", "spec_accept", "spec_commit",
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
     "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
-    "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass",
+    "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass", "spec_counts_add",
 )
 SPEC_MAX_NGRAM = 8
 
@@ -64,7 +64,8 @@ class SpecRound(C.Structure):
                 ("max_blocks", C.c_int), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("n_blocks", C.c_int),
                 ("gdn_state", C.c_void_p), ("mode", C.c_int), ("temperature", C.c_float),
                 ("q_probs", C.c_void_p), ("seed", C.c_uint64), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t)]
+                ("workspace_bytes", C.c_size_t), ("counts", C.c_void_p), ("presence_penalty", C.c_float),
+                ("frequency_penalty", C.c_float)]
 
 
 class SpecRowStat(C.Structure):
@@ -123,6 +124,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_backoff_call.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
         lib.spec_backoff_pass.restype = C.c_int
         lib.spec_backoff_pass.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int]
+        lib.spec_counts_add.restype = C.c_int
+        lib.spec_counts_add.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]
         lib.spec_history_append.restype = C.c_int
         lib.spec_history_append.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int,
                                             C.c_void_p]
@@ -235,3 +238,10 @@ def spec_backoff_call(states, n: int, k: int, row_budget: int, drafts) -> bool:
 
 def spec_backoff_pass(states, n: int, kept, speculates: bool) -> None:
     _check(load_library().spec_backoff_pass(states, n, kept, int(speculates)), "spec_backoff_pass")
+
+
+def spec_counts_add(counts_ptr: int, vocab: int, lanes: int, committed_ptr: int, out_tokens_ptr: int,
+                    out_stride: int, stream: int) -> None:
+    _check(load_library().spec_counts_add(C.c_void_p(counts_ptr), vocab, lanes, C.c_void_p(committed_ptr),
+                                          C.c_void_p(out_tokens_ptr), out_stride, C.c_void_p(stream)),
+           "spec_counts_add")

@@ -295,6 +295,8 @@ struct LmParams {
   uint32_t key0, key1;     // Philox key
   LmPartial* part;         // [R][groups]
   RowInfo ri;
+  const int32_t* counts;   // [L][V] token counts of each lane up to its anchor, or null (no penalties)
+  float presence, frequency;
 };
 
 // Row statistics after reducing the LM-head partials (internal workspace form).
@@ -328,7 +330,38 @@ struct RaceParams {
   const LaneDecision* dec; // [L]
   float* part;             // [L][groups][4]: residual key, index, fallback key, index
   RowInfo ri;
+  const int32_t* tokens;   // [R] round tokens (the drafts before the rejected row)
+  const int32_t* counts;   // [L][V] or null, as LmParams
+  float presence, frequency;
 };
+
+// Presence / frequency penalty of one row: row j of a lane conditions on the lane's
+// tokens up to its anchor (cnt) and on the round's drafts d_1 .. d_j (lane_tokens[1 .. j]),
+// so a token seen c times there loses presence * [c > 0] + frequency * c.
+struct RowPenalty {
+  const int32_t* cnt;           // the lane's counts row, null: no penalty
+  const int32_t* lane_tokens;   // the lane's round tokens (anchor first)
+  int j;
+  float presence, frequency;
+};
+
+__device__ __forceinline__ RowPenalty row_penalty(const int32_t* counts, int V, const int32_t* tokens,
+                                                  const RowInfo& ri, int r, float presence, float frequency) {
+  RowPenalty rp;
+  const int l = ri.row_lane[r];
+  rp.cnt = counts ? counts + (size_t)l * V : nullptr;
+  rp.lane_tokens = tokens + ri.lane_start[l];
+  rp.j = ri.row_col[r];
+  rp.presence = presence;
+  rp.frequency = frequency;
+  return rp;
+}
+
+__device__ __forceinline__ float penalized(float z, int v, const RowPenalty& rp) {
+  int c = rp.cnt[v];
+  for (int i = 1; i <= rp.j; ++i) c += rp.lane_tokens[i] == v;
+  return z - ((c > 0 ? rp.presence : 0.f) + rp.frequency * (float)c);
+}
 
 // Where the QKV epilogue stages a round's own K/V columns from: the lanes' cache
 // lengths and the committed prefix of each lane's first staged block (layer slices).

@@ -1,5 +1,5 @@
-// Copy-from-the-conversation drafter (n-gram prompt lookup) and the history update of a
-// multi-round loop (gfx950).
+// Copy-from-the-conversation drafter (n-gram prompt lookup), the history update of a
+// multi-round loop, and the token counts the per-row penalties use (gfx950).
 //
 // "Speculative decoding" (mashbox docs, "Where it runs", --speculation ngram): the
 // drafter looks up the last few tokens earlier in the request and proposes the tokens
@@ -83,6 +83,26 @@ __global__ void k_history_append(int32_t* __restrict__ hist, int32_t* __restrict
     if (len + i < max_len) hist[(size_t)l * max_len + len + i] = out_tokens[(size_t)l * out_stride + i];
   __syncthreads();
   if (threadIdx.x == 0) hist_len[l] = min(len + c, max_len);
+}
+
+// counts[l][t] += 1 for each token of lane l's committed run: one thread per lane, so a
+// token that occurs twice in a run is counted twice without atomics.
+__global__ void k_counts_add(int32_t* __restrict__ counts, int vocab, int lanes, const int32_t* __restrict__ committed,
+                             const int32_t* __restrict__ out_tokens, int out_stride) {
+  const int l = blockIdx.x * blockDim.x + threadIdx.x;
+  if (l >= lanes) return;
+  const int c = min(max(committed[l], 0), out_stride);
+  for (int i = 0; i < c; ++i) {
+    const int t = out_tokens[(size_t)l * out_stride + i];
+    if (t >= 0 && t < vocab) counts[(size_t)l * vocab + t] += 1;
+  }
+}
+
+int launch_counts_add(int32_t* counts, int vocab, int lanes, const int32_t* committed, const int32_t* out_tokens,
+                      int out_stride, hipStream_t st) {
+  hipLaunchKernelGGL(k_counts_add, dim3((lanes + 63) / 64), dim3(64), 0, st, counts, vocab, lanes, committed,
+                     out_tokens, out_stride);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_ngram_draft(const int32_t* hist, const int32_t* hist_len, int lanes, int max_len, int k, int n_max,

@@ -803,6 +803,7 @@ struct RowMeta {
   int bonus;        // 1 if the row is its lane's last row (bonus draw row)
   uint32_t pos;     // bonus position kv_len + col + 1
   uint32_t lane;
+  RowPenalty pen;   // pen.cnt null: no penalties
 };
 
 __device__ __forceinline__ RowMeta row_meta(const LmParams& p, int r) {
@@ -813,6 +814,7 @@ __device__ __forceinline__ RowMeta row_meta(const LmParams& p, int r) {
   m.bonus = last;
   m.pos = (uint32_t)(p.kv_len[l] + j + 1);
   m.lane = (uint32_t)l;
+  m.pen = row_penalty(p.counts, p.V, p.tokens, p.ri, r, p.presence, p.frequency);
   return m;
 }
 
@@ -841,8 +843,13 @@ __device__ __forceinline__ Stat stat_merge(Stat a, Stat b, float inv_t) {
 
 // Statistics of four logits z[e] at tokens v0 + e held by one lane, merged across the
 // four lane groups (xor 16, 32) so every lane of a 16-lane column ends with the tile's stats.
-__device__ __forceinline__ Stat tile_stats(const float z[4], int v0, const RowMeta& rm, const LmParams& p) {
+__device__ __forceinline__ Stat tile_stats(const float (&zr)[4], int v0, const RowMeta& rm, const LmParams& p) {
   Stat s;
+  float z[4] = {zr[0], zr[1], zr[2], zr[3]};
+  if (rm.pen.cnt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = penalized(z[e], v0 + e, rm.pen);
+  }
   float m = z[0]; int a = v0;
 #pragma unroll
   for (int e = 1; e < 4; ++e) if (z[e] > m) { m = z[e]; a = v0 + e; }
@@ -913,7 +920,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
   for (int t = 0; t < RT; ++t) {
     const int r = t * 16 + r16;
     RowMeta rm;
-    rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0;
+    rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0; rm.pen.cnt = nullptr;
     if (r < p.R) rm = row_meta(p, r);
     Stat s = stat_identity();
 #pragma unroll
@@ -947,7 +954,8 @@ __global__ void k_lmhead_f32(LmParams p) {
     const float* w = reinterpret_cast<const float*>(p.W) + (size_t)v * p.H;
     double zz = 0.0;
     for (int k = 0; k < p.H; ++k) zz += (double)X[k] * (double)w[k];
-    const float z = (float)zz;
+    float z = (float)zz;
+    if (rm.pen.cnt) z = penalized(z, v, rm.pen);
     s.m = z; s.arg = v; s.se = 1.f;
     s.zn = (rm.next_tok == v) ? z : NAN;
     if (p.sampled && rm.bonus) {
@@ -1008,8 +1016,14 @@ __device__ __forceinline__ bool less_key(float k, int i, float bk, int bi) {
   return k < bk || (k == bk && i < bi);
 }
 
-__device__ __forceinline__ void race_lane(const float z[4], int v0, const RaceParams& p, int l, RaceKey& rk) {
+__device__ __forceinline__ void race_lane(const float (&zr)[4], int v0, const RaceParams& p, int l, RaceKey& rk) {
   const LaneDecision d = p.dec[l];
+  float z[4] = {zr[0], zr[1], zr[2], zr[3]};
+  if (p.counts) {   // the rejected row's penalty, as its statistics had it
+    const RowPenalty rp = row_penalty(p.counts, p.V, p.tokens, p.ri, d.resid_row, p.presence, p.frequency);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = penalized(z[e], v0 + e, rp);
+  }
   const int qrow = d.resid_row + 1;
   const uint32_t pos = (uint32_t)(p.kv_len[l] + d.resid_col);
   uint32_t c[4] = {pos, (uint32_t)l, kPurposeRace, (uint32_t)(v0 >> 2)};
@@ -1106,7 +1120,8 @@ __global__ void k_race_f32(RaceParams p) {
     const float* w = reinterpret_cast<const float*>(p.W) + (size_t)v * p.H;
     double zz = 0.0;
     for (int k = 0; k < p.H; ++k) zz += (double)X[k] * (double)w[k];
-    const float z = (float)zz;
+    float z = (float)zz;
+    if (p.counts) z = penalized(z, v, row_penalty(p.counts, p.V, p.tokens, p.ri, d.resid_row, p.presence, p.frequency));
     const uint32_t pos = (uint32_t)(p.kv_len[l] + d.resid_col);
     uint32_t c[4] = {pos, (uint32_t)l, kPurposeRace, (uint32_t)(v >> 2)};
     philox4x32_10(c, p.key0, p.key1);

@@ -50,6 +50,8 @@ int launch_copy_rows(const void* src, void* dst, size_t bytes, hipStream_t st);
 // n-gram drafter and the history of a multi-round loop
 int launch_ngram_draft(const int32_t* hist, const int32_t* hist_len, int lanes, int max_len, int k, int n_max,
                        int n_min, int32_t* tokens, int32_t* n_match, hipStream_t st);
+int launch_counts_add(int32_t* counts, int vocab, int lanes, const int32_t* committed, const int32_t* out_tokens,
+                      int out_stride, hipStream_t st);
 int launch_history_append(int32_t* hist, int32_t* hist_len, int lanes, int max_len, const int32_t* committed,
                           const int32_t* out_tokens, int out_stride, hipStream_t st);
 

@@ -180,6 +180,7 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
   if (r->mode == SPEC_SAMPLED) {
     if (!r->q_probs || !(r->temperature > 0.f) || !std::isfinite(r->temperature)) return SPEC_E_INVAL;
   }
+  if (r->counts && (!std::isfinite(r->presence_penalty) || !std::isfinite(r->frequency_penalty))) return SPEC_E_INVAL;
   const int mb = head_only ? 1 : r->max_blocks;
   if (!head_only) {
     if (m->d.n_layers == 0) return SPEC_E_INVAL;
@@ -367,6 +368,9 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   p.key1 = (uint32_t)(r->seed >> 32);
   p.part = at<sv::LmPartial>(r->workspace, w.lmp);
   p.ri = ri;
+  p.counts = r->counts;
+  p.presence = r->presence_penalty;
+  p.frequency = r->frequency_penalty;
   ProfScope ps(m, SPEC_K_LM_HEAD, st);
   return sv::launch_lmhead(p, m->bf16, st) ? SPEC_E_HIP : SPEC_OK;
 }
@@ -537,6 +541,10 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
     p.dec = at<sv::LaneDecision>(ws, w.dec);
     p.part = at<float>(ws, w.racep);
     p.ri = ri;
+    p.tokens = r->tokens;
+    p.counts = r->counts;
+    p.presence = r->presence_penalty;
+    p.frequency = r->frequency_penalty;
     SV_CHECK(sv::launch_race(p, m->bf16, s));
     SV_CHECK(sv::launch_race_finish(at<float>(ws, w.racep), m->lm_groups, at<sv::LaneDecision>(ws, w.dec),
                                     out_tokens, ri, s));
@@ -663,6 +671,16 @@ int spec_ngram_draft(const int32_t* history, const int32_t* hist_len, int lanes,
   if (n_min < 1 || n_max < n_min || n_max > SPEC_MAX_NGRAM) return SPEC_E_INVAL;
   return sv::launch_ngram_draft(history, hist_len, lanes, max_len, k, n_max, n_min, tokens, n_match,
                                 reinterpret_cast<hipStream_t>(stream))
+             ? SPEC_E_HIP
+             : SPEC_OK;
+}
+
+int spec_counts_add(int32_t* counts, int vocab, int lanes, const int32_t* committed, const int32_t* out_tokens,
+                    int out_stride, void* stream) {
+  if (!counts || !committed || !out_tokens) return SPEC_E_INVAL;
+  if (lanes < 1 || lanes > SPEC_MAX_LANES || vocab < 1 || out_stride < 1) return SPEC_E_INVAL;
+  return sv::launch_counts_add(counts, vocab, lanes, committed, out_tokens, out_stride,
+                               reinterpret_cast<hipStream_t>(stream))
              ? SPEC_E_HIP
              : SPEC_OK;
 }

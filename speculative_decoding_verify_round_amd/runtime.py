@@ -109,7 +109,8 @@ class RoundCall:
 
     def __init__(self, cache: "DeviceCache", lane_tokens: Sequence[Sequence[int]], mode: str = "greedy",
                  temperature: float = 1.0, q_probs: Optional[torch.Tensor] = None, seed: int = 0,
-                 kv_len_host: Optional[Sequence[int]] = None, tokens_dev: Optional[torch.Tensor] = None):
+                 kv_len_host: Optional[Sequence[int]] = None, tokens_dev: Optional[torch.Tensor] = None,
+                 counts: Optional[torch.Tensor] = None, presence: float = 0.0, frequency: float = 0.0):
         self.cache = cache
         self.L = len(lane_tokens)
         self.cols = [len(t) for t in lane_tokens]
@@ -141,6 +142,10 @@ class RoundCall:
         r.seed = int(seed)
         r.workspace = cache.workspace.data_ptr()
         r.workspace_bytes = cache.workspace.numel()
+        self.counts = counts            # device int32 [lanes][vocab] or None: per-row penalties
+        r.counts = counts.data_ptr() if counts is not None else None
+        r.presence_penalty = float(presence)
+        r.frequency_penalty = float(frequency)
         self.r = r
 
 

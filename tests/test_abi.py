@@ -219,3 +219,17 @@ def test_ngram_calls_validate():
     assert lib.spec_history_append(FAKE, FAKE, 2, 0, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
     assert lib.spec_history_append(FAKE, FAKE, 2, 64, FAKE, FAKE, 0, None) == B.SPEC_E_INVAL
     assert lib.spec_history_append(FAKE, FAKE, 2, 64, None, FAKE, 16, None) == B.SPEC_E_INVAL
+
+
+def test_penalty_fields_validate(model):
+    """Non-finite penalties with a counts buffer are refused; counts_add refuses bad sizes."""
+    lib = B.load_library()
+    for pres, freq in ((float("nan"), 0.1), (0.1, float("inf"))):
+        r = make_round(model)
+        r.counts, r.presence_penalty, r.frequency_penalty = FAKE, pres, freq
+        assert lib.spec_verify_round(model, C.byref(r), None) == B.SPEC_E_INVAL
+        assert lib.spec_accept(model, C.byref(r), FAKE, FAKE, None, None) == B.SPEC_E_INVAL
+    assert lib.spec_counts_add(None, 100, 2, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_counts_add(FAKE, 0, 2, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_counts_add(FAKE, 100, 0, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
+    assert lib.spec_counts_add(FAKE, 100, 2, FAKE, FAKE, 0, None) == B.SPEC_E_INVAL

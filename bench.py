@@ -269,6 +269,9 @@ def main():
     ap.add_argument("--plain-steps", type=int, default=10, help="plain one-row rounds timed for comparison")
     ap.add_argument("--drafter", choices=("planted", "ngram"), default="planted",
                     help="planted drafts (default) or the n-gram drafter on each lane's own history")
+    ap.add_argument("--penalties", default=None, metavar="PRESENCE,FREQUENCY",
+                    help="per-row presence and frequency penalties on every round (plain ones too), with "
+                         "each lane's counts kept on the device; the lanes' histories are 8K seeded tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (the reference for HBM counters)")
     args = ap.parse_args()
@@ -309,6 +312,23 @@ def main():
         dc.gdn.normal_(0.0, 1.0 / np.sqrt(128.0))
     torch.cuda.synchronize()
     anchors = [int(t) for t in synth.uniform_tokens(cfg.input_seed, 5, L, cfg.vocab)]
+    pen, counts0 = {}, None
+    if args.penalties:
+        if args.drafter != "planted":
+            print("--penalties runs with the planted drafts", file=sys.stderr)
+            sys.exit(2)
+        pres, freq = (float(x) for x in args.penalties.split(","))
+        # each lane's counts: a seeded history as long as the context, then its anchor
+        hist = np.stack([np.append(synth.uniform_tokens(cfg.input_seed, 300 + l, ctx, cfg.vocab), anchors[l])
+                         for l in range(L)])
+        counts0 = torch.from_numpy(np.stack([np.bincount(h, minlength=cfg.vocab) for h in hist]).astype(np.int32))
+        counts0 = counts0.cuda()
+        pen = {"counts": counts0.clone(), "presence": pres, "frequency": freq}
+
+    def add_counts():
+        if pen:
+            B.spec_counts_add(pen["counts"].data_ptr(), cfg.vocab, L, dc.committed.data_ptr(),
+                              dc.out_tokens.data_ptr(), dc.out_tokens.shape[1], torch.cuda.current_stream().cuda_stream)
 
     # reference plain-greedy continuation (one row per lane per round); also the plain-round timing
     log(f"reference continuation: {ref_len} plain rounds")
@@ -317,11 +337,12 @@ def main():
     cur = torch.tensor(anchors, dtype=torch.int32, device="cuda")
     plain_times = []
     for s in range(ref_len):
-        rc = dc.round([[0]] * L, tokens_dev=cur)
+        rc = dc.round([[0]] * L, tokens_dev=cur, **pen)
         t0 = time.perf_counter()
         dc.verify(rc)
         dc.accept(rc, stats=False)
         dc.commit(rc)
+        add_counts()
         nxt = dc.out_tokens[:, 0].clone()
         torch.cuda.synchronize()
         plain_times.append(time.perf_counter() - t0)
@@ -329,6 +350,8 @@ def main():
         cur = nxt
     plain_ms = float(np.median(plain_times[2:2 + max(1, args.plain_steps)]) * 1e3)
     dc.set_kv_len([ctx] * L)
+    if pen:
+        pen["counts"].copy_(counts0)
 
     if args.drafter == "ngram":
         result = run_ngram(args, cfg, dm, dc, anchors, plain_ms)
@@ -363,10 +386,11 @@ def main():
             flat += [int(ref[l, pos[l]])] + drafts_for(l)
         tok_host.copy_(torch.tensor(flat, dtype=torch.int32))
         tok_dev.copy_(tok_host, non_blocking=True)
-        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev)
+        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev, **pen)
         dc.verify(rc)
         dc.accept(rc, stats=False)
         dc.commit(rc)
+        add_counts()
         c = dc.committed.cpu().numpy()          # the per-round device -> host crossing
         for l in range(L):
             pos[l] += int(c[l])
@@ -413,7 +437,9 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer dense bf16 decoder H{cfg.hidden}, "
                                f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, FFN {cfg.ffn}, "
                                f"vocab {cfg.vocab}; {L} lanes x (k={k} + 1) = {R} rows, context {ctx}, greedy, "
-                               f"drafts planted at slot acceptance 0.9..0.35",
+                               f"drafts planted at slot acceptance 0.9..0.35"
+                               + (f", presence/frequency penalties {pen['presence']}/{pen['frequency']} per row"
+                                  if pen else ""),
                    "lanes": L, "k": k, "rows": R, "context": ctx, "mode": "greedy"},
         "verify_rows_per_s": round(rows_s, 1),
         "tokens_per_round": round(tpr, 3),

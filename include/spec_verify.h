@@ -163,7 +163,8 @@ typedef struct {
    * lane conditions on those tokens and on its drafts d_1 .. d_j, so a token seen c times
    * there loses presence * [c > 0] + frequency * c from its logit before every statistic
    * and decision (argmax, softmax at T, the textbook rule, the residual and bonus draws).
-   * With counts, both penalties must be finite, else SPEC_E_INVAL.  spec_counts_add
+   * With counts, both penalties must be finite and counts 16-byte aligned, else
+   * SPEC_E_INVAL.  spec_counts_add
    * keeps counts current after each commit. */
   const int32_t* counts;
   float presence_penalty;

@@ -357,10 +357,40 @@ __device__ __forceinline__ RowPenalty row_penalty(const int32_t* counts, int V, 
   return rp;
 }
 
+__device__ __forceinline__ float penalty_of(int c, const RowPenalty& rp) {
+  return (c > 0 ? rp.presence : 0.f) + rp.frequency * (float)c;
+}
+
 __device__ __forceinline__ float penalized(float z, int v, const RowPenalty& rp) {
   int c = rp.cnt[v];
   for (int i = 1; i <= rp.j; ++i) c += rp.lane_tokens[i] == v;
-  return z - ((c > 0 ? rp.presence : 0.f) + rp.frequency * (float)c);
+  return z - penalty_of(c, rp);
+}
+
+// Penalties of the tokens v0[t] .. v0[t] + 3 of T groups of four (each v0 a multiple of
+// 4 and at most V - 4; a lane's count row is 16-byte aligned): one 16-byte count load per
+// group and one pass over the row's drafts, whose loads do not depend on each other.
+template <int T>
+__device__ __forceinline__ void penalties4(const RowPenalty& rp, const int (&v0)[T], float (&pz)[T][4]) {
+  int c[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int4 cv = *reinterpret_cast<const int4*>(rp.cnt + v0[t]);
+    c[t][0] = cv.x; c[t][1] = cv.y; c[t][2] = cv.z; c[t][3] = cv.w;
+  }
+#pragma unroll
+  for (int i = 1; i < kMaxCols; ++i) {
+    const int d = rp.lane_tokens[min(i, rp.j)];   // index within the lane's columns
+    const bool on = i <= rp.j;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[t][e] += (on && d == v0[t] + e) ? 1 : 0;
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pz[t][e] = penalty_of(c[t][e], rp);
 }
 
 // Where the QKV epilogue stages a round's own K/V columns from: the lanes' cache

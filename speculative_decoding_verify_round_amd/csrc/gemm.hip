@@ -841,15 +841,11 @@ __device__ __forceinline__ Stat stat_merge(Stat a, Stat b, float inv_t) {
   return o;
 }
 
-// Statistics of four logits z[e] at tokens v0 + e held by one lane, merged across the
-// four lane groups (xor 16, 32) so every lane of a 16-lane column ends with the tile's stats.
-__device__ __forceinline__ Stat tile_stats(const float (&zr)[4], int v0, const RowMeta& rm, const LmParams& p) {
+// Statistics of four logits z[e] at tokens v0 + e held by one lane (penalties already
+// applied), merged across the four lane groups (xor 16, 32) so every lane of a 16-lane
+// column ends with the tile's stats.
+__device__ __forceinline__ Stat tile_stats(const float (&z)[4], int v0, const RowMeta& rm, const LmParams& p) {
   Stat s;
-  float z[4] = {zr[0], zr[1], zr[2], zr[3]};
-  if (rm.pen.cnt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = penalized(z[e], v0 + e, rm.pen);
-  }
   float m = z[0]; int a = v0;
 #pragma unroll
   for (int e = 1; e < 4; ++e) if (z[e] > m) { m = z[e]; a = v0 + e; }
@@ -922,11 +918,20 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
     RowMeta rm;
     rm.next_tok = -1; rm.bonus = 0; rm.pos = 0; rm.lane = 0; rm.pen.cnt = nullptr;
     if (r < p.R) rm = row_meta(p, r);
+    float pz[T][4] = {};
+    if (rm.pen.cnt) {
+      int v0[T];
+#pragma unroll
+      for (int j = 0; j < T; ++j) v0[j] = min(tile[j], tiles - 1) * 16 + 4 * kq;
+      penalties4<T>(rm.pen, v0, pz);
+    }
     Stat s = stat_identity();
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       if (tile[j] < tiles) {   // wave-uniform; every lane joins tile_stats' cross-lane shuffles
-        const float z[4] = {acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]};
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = acc[j][t][e] - pz[j][e];
         s = stat_merge(s, tile_stats(z, tile[j] * 16 + 4 * kq, rm, p), p.inv_t);
       }
     }
@@ -1021,8 +1026,11 @@ __device__ __forceinline__ void race_lane(const float (&zr)[4], int v0, const Ra
   float z[4] = {zr[0], zr[1], zr[2], zr[3]};
   if (p.counts) {   // the rejected row's penalty, as its statistics had it
     const RowPenalty rp = row_penalty(p.counts, p.V, p.tokens, p.ri, d.resid_row, p.presence, p.frequency);
+    const int vv[1] = {v0};
+    float pz[1][4];
+    penalties4<1>(rp, vv, pz);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = penalized(z[e], v0 + e, rp);
+    for (int e = 0; e < 4; ++e) z[e] -= pz[0][e];
   }
   const int qrow = d.resid_row + 1;
   const uint32_t pos = (uint32_t)(p.kv_len[l] + d.resid_col);

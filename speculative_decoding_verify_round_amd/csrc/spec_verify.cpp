@@ -180,7 +180,9 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
   if (r->mode == SPEC_SAMPLED) {
     if (!r->q_probs || !(r->temperature > 0.f) || !std::isfinite(r->temperature)) return SPEC_E_INVAL;
   }
-  if (r->counts && (!std::isfinite(r->presence_penalty) || !std::isfinite(r->frequency_penalty))) return SPEC_E_INVAL;
+  if (r->counts && (!std::isfinite(r->presence_penalty) || !std::isfinite(r->frequency_penalty) ||
+                    (reinterpret_cast<uintptr_t>(r->counts) & 15) != 0))
+    return SPEC_E_INVAL;
   const int mb = head_only ? 1 : r->max_blocks;
   if (!head_only) {
     if (m->d.n_layers == 0) return SPEC_E_INVAL;

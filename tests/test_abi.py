@@ -222,13 +222,16 @@ def test_ngram_calls_validate():
 
 
 def test_penalty_fields_validate(model):
-    """Non-finite penalties with a counts buffer are refused; counts_add refuses bad sizes."""
+    """Non-finite penalties or a misaligned counts buffer are refused; counts_add refuses bad sizes."""
     lib = B.load_library()
     for pres, freq in ((float("nan"), 0.1), (0.1, float("inf"))):
         r = make_round(model)
         r.counts, r.presence_penalty, r.frequency_penalty = FAKE, pres, freq
         assert lib.spec_verify_round(model, C.byref(r), None) == B.SPEC_E_INVAL
         assert lib.spec_accept(model, C.byref(r), FAKE, FAKE, None, None) == B.SPEC_E_INVAL
+    r = make_round(model)
+    r.counts, r.presence_penalty, r.frequency_penalty = FAKE + 4, 0.1, 0.1     # not 16-byte aligned
+    assert lib.spec_verify_round(model, C.byref(r), None) == B.SPEC_E_INVAL
     assert lib.spec_counts_add(None, 100, 2, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
     assert lib.spec_counts_add(FAKE, 0, 2, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
     assert lib.spec_counts_add(FAKE, 100, 0, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL

@@ -35,13 +35,18 @@ from .numerics import bf16, f32, store, rmsnorm, rope, sigmoid, silu
 L2_EPS = 1e-6
 
 
-def attend(q, keys, vals, n_ctx: int) -> np.ndarray:
+def attend(q, keys, vals, n_ctx: int, window: int = 0) -> np.ndarray:
     """Grouped-query attention of one lane's columns (float64, exact two-pass softmax).
 
     q: [c, n_q, d] queries of columns 0..c-1; keys, vals: [n_ctx + c, n_kv, d]
     (committed context, then the lane's own columns).  Column j sees positions
     0 .. n_ctx + j (causal among its own columns); query head h reads kv head
     h // (n_q / n_kv); scores are scaled by 1/sqrt(d).
+
+    Sliding-window targets (FreeToken issue, "Design": sliding-window targets; the
+    Gemma 4 assistant thread): with window W > 0 column j sees only its last W
+    positions, n_ctx + j - W + 1 .. n_ctx + j (itself included) -- the reading of a
+    window of W positions that ends at the query.
     """
     c, nq, d = q.shape
     G = nq // keys.shape[1]
@@ -51,13 +56,14 @@ def attend(q, keys, vals, n_ctx: int) -> np.ndarray:
     scale = 1.0 / np.sqrt(d)
     for j in range(c):
         n_vis = n_ctx + j + 1
+        lo = max(0, n_vis - window) if window > 0 else 0
         for hq in range(nq):
             g = hq // G
-            s = kk[:n_vis, g, :] @ np.asarray(q[j, hq], np.float64) * scale
+            s = kk[lo:n_vis, g, :] @ np.asarray(q[j, hq], np.float64) * scale
             s -= s.max()
             p = np.exp(s)
             p /= p.sum()
-            out[j, hq] = p @ vv[:n_vis, g, :]
+            out[j, hq] = p @ vv[lo:n_vis, g, :]
     return out
 
 
@@ -221,7 +227,7 @@ class OracleModel:
             ck, cv = cache.gather(li, l, n_ctx)
             keys = np.concatenate([ck, k[rows.start:rows.stop]], axis=0)
             vals = np.concatenate([cv, v[rows.start:rows.stop]], axis=0)
-            o[rows.start:rows.stop] = attend(q[rows.start:rows.stop], keys, vals, n_ctx)
+            o[rows.start:rows.stop] = attend(q[rows.start:rows.stop], keys, vals, n_ctx, cfg.layer_window(li))
         return self._act(o).reshape(R, nq * d), k, v
 
     def _gdn_inputs(self, h, lw):

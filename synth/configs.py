@@ -26,6 +26,8 @@ class ModelConfig:
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0     # 0.0 = no positional encoding
     kv_block: int = 16
+    sliding_window: int = 0         # 0 = full attention; W > 0: a row sees its last W positions
+    window_global_every: int = 0    # g > 0: attention layers g-1, 2g-1, ... keep full attention
     # round workload
     lanes: int = 1
     k: int = 3
@@ -41,6 +43,13 @@ class ModelConfig:
     @property
     def n_attn(self) -> int:
         return sum(1 for s in self.layer_kinds if s == "attn")
+
+    def layer_window(self, attn_index: int) -> int:
+        """Window of the attention layer with this index among attention layers (0 = full)."""
+        g = self.window_global_every
+        if self.sliding_window <= 0 or (g > 0 and attn_index % g == g - 1):
+            return 0
+        return self.sliding_window
 
     @property
     def n_gdn(self) -> int:

@@ -124,6 +124,14 @@ typedef struct {
   const void* lm_head;     /* [vocab][hidden]: row-major (f32) or packed (bf16) */
   const float* final_norm; /* [hidden]; may be NULL for a head-only model */
   const spec_layer_weights* layers;   /* host [n_layers] */
+  /* Sliding-window targets (FreeToken issue, "Design": sliding-window targets; the
+   * Gemma 4 assistant thread): sliding_window = 0 is full attention; W > 0 makes a row
+   * at position P of a windowed attention layer attend to positions P - W + 1 .. P
+   * only.  window_global_every = g > 0 keeps full attention in attention layers g - 1,
+   * 2g - 1, ... (counted among the attention layers); 0 windows every attention layer.
+   * Both >= 0, else SPEC_E_INVAL. */
+  int sliding_window;
+  int window_global_every;
 } spec_model_desc;
 
 typedef struct spec_model spec_model;
@@ -261,6 +269,18 @@ int spec_debug_gemm(const spec_model* model, const void* X, const void* W, float
  * the stream. */
 int64_t spec_packed_weight_bytes(int N, int K);
 int spec_pack_weight(const void* src, void* dst, int N, int K, void* stream);
+
+/* Out-of-window frees of a sliding-window target (FreeToken issue, "Design": each
+ * request frees the slots whose interval has slid out of the window).  Returns the
+ * first cache block (index into the lane's block_table row) that a verify round at
+ * committed length kv_len reads in an attention layer of window W > 0; the round never
+ * reads or dereferences the table entries below it, and since kv_len only grows they
+ * stay unread, so the caller may release and reuse those blocks -- when every attention
+ * layer of the model is windowed and shares that table.  Rejected columns never reach
+ * the cache (spec_commit writes only committed ones), so rejection frees nothing.
+ * window == 0: returns 0 (nothing may be freed).  kv_len < 0 or window < 0:
+ * SPEC_E_INVAL.  Host only. */
+int spec_window_live_block(int kv_len, int window);
 
 /* counts[l][t] += 1 for every token t of lane l's committed run, out_tokens[l][0 ..
  * committed[l]) (device, row stride out_stride), after spec_accept: the counts that

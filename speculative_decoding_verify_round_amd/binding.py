@@ -29,6 +29,7 @@ HEADER_SYMBOLS = (
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
     "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
     "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass", "spec_counts_add",
+    "spec_window_live_block",
 )
 SPEC_MAX_NGRAM = 8
 
@@ -55,7 +56,8 @@ class SpecModelDesc(C.Structure):
                 ("layer_kind", C.POINTER(C.c_int32)), ("gdn_heads", C.c_int), ("gdn_dim", C.c_int),
                 ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("kv_block", C.c_int),
                 ("attn_chunk", C.c_int), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
-                ("final_norm", C.c_void_p), ("layers", C.POINTER(SpecLayerWeights))]
+                ("final_norm", C.c_void_p), ("layers", C.POINTER(SpecLayerWeights)),
+                ("sliding_window", C.c_int), ("window_global_every", C.c_int)]
 
 
 class SpecRound(C.Structure):
@@ -124,6 +126,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_backoff_call.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
         lib.spec_backoff_pass.restype = C.c_int
         lib.spec_backoff_pass.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int]
+        lib.spec_window_live_block.restype = C.c_int
+        lib.spec_window_live_block.argtypes = [C.c_int, C.c_int]
         lib.spec_counts_add.restype = C.c_int
         lib.spec_counts_add.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p]
         lib.spec_history_append.restype = C.c_int
@@ -238,6 +242,13 @@ def spec_backoff_call(states, n: int, k: int, row_budget: int, drafts) -> bool:
 
 def spec_backoff_pass(states, n: int, kept, speculates: bool) -> None:
     _check(load_library().spec_backoff_pass(states, n, kept, int(speculates)), "spec_backoff_pass")
+
+
+def spec_window_live_block(kv_len: int, window: int) -> int:
+    r = load_library().spec_window_live_block(kv_len, window)
+    if r < 0:
+        _check(r, "spec_window_live_block")
+    return r
 
 
 def spec_counts_add(counts_ptr: int, vocab: int, lanes: int, committed_ptr: int, out_tokens_ptr: int,

@@ -153,9 +153,14 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
   const int nch = (end + p.chunk - 1) / p.chunk;
-  const int c0 = x * nch / (int)gridDim.x, c1 = (x + 1) * nch / (int)gridDim.x;
+  // sliding window: no row of the lane sees a position below lo, so the chunks below cl
+  // are skipped and the lane's first range starts at the stage holding lo
+  const int lo = p.window > 0 ? max(0, kvl - p.window + 1) : 0;
+  const int cl = lo / p.chunk, nw = nch - cl;
+  const int c0 = cl + x * nw / (int)gridDim.x, c1 = cl + (x + 1) * nw / (int)gridDim.x;
   if (c0 >= c1) return;
-  const int first = c0 * p.chunk;                                       // first position of the range
+  const int first = max(c0 * p.chunk, lo / STEP * STEP);                // first position of the range
+  const int tb = (first - c0 * p.chunk) / STEP;                         // stages of chunk c0 skipped
   const int T = (min(c1 * p.chunk, end) - first + STEP - 1) / STEP;     // stages of the range
   const int cs = p.chunk / STEP;                                        // stages per chunk
   const int fb = first >> 4, b0 = kvl >> 4;   // blocks >= b0 come from the staged columns
@@ -433,6 +438,15 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[y][e] = p0 + 4 * y + e <= lim ? sc[y][e] : -INFINITY;
     }
+    // positions below a query's window (W positions ending at its own column); the
+    // highest window start of the lane is end - W
+    if (p.window > 0 && first + STEP * t < end - p.window) {
+      const int lw = lim - p.window + 1;
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[y][e] = p0 + 4 * y + e >= lw ? sc[y][e] : -INFINITY;
+    }
     const float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                            fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     const float mnew = fmaxf(mrun, col_max(mx));
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
       wg_barrier();                          // the own columns are in the stage
     }
     if (active) compute(t);
-    if (t % cs == cs - 1 || t == T - 1) {
+    if ((tb + t) % cs == cs - 1 || t == T - 1) {
       // chunk end: half 1 hands its (O, max, sum) to half 0 through the slot of stage t
       // (free once every wave is past this barrier; the next issue into it follows the
       // next stage's barrier), half 0 merges and writes the tile's partial
@@ -520,7 +534,7 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
           f0 = __builtin_amdgcn_exp2f(fmaf(mrun, scale, -ms));
           f1 = __builtin_amdgcn_exp2f(fmaf(o1.x, scale, -ms));
         }
-        const int c = c0 + t / cs;
+        const int c = c0 + (tb + t) / cs;
         float* slot = p.part + (((size_t)l * nkv + g) * p.n_chunks + c) * 64 * PW;
         // rows past the lane's queries are skipped; row 16 q is always written (never
         // read when invalid) so that every store instruction has an active lane
@@ -582,6 +596,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
   const int end = kvl + cols;
   const int pos0 = c * p.chunk;
   if (pos0 >= end) return;
+  const int lo = p.window > 0 ? max(0, kvl - p.window + 1) : 0;   // no row sees a position below lo
+  if (pos0 + p.chunk <= lo) return;
   const int Mq = cols * p.G;
   const int wlen = p.chunk >> 2;
   const int wb = pos0 + wave * wlen, we = min(wb + wlen, end);
@@ -596,11 +612,12 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
     const int j = m / p.G, hh = m - j * p.G;
     const float* q = Qp + ((size_t)(rs + j) * p.nq + g * p.G + hh) * D;
     const int lim = kvl + j;
+    const int lw = p.window > 0 ? lim - p.window + 1 : 0;   // the row's window starts at lw
     float mr = -INFINITY;
     double lr = 0.0, o0 = 0.0, o1 = 0.0;
     for (int p0 = wb; p0 < we; p0 += 64) {
       const int pos = p0 + lane;
-      const bool valid = pos < we && pos <= lim;
+      const bool valid = pos < we && pos <= lim && pos >= lw;
       float s = -INFINITY;
       if (valid) {
         const float* kr;
@@ -624,6 +641,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
       for (int t = 0; t < nval; ++t) {
         const double pt = __shfl(pr, t);
         const int vp = p0 + t;
+        if (vp < lw) continue;   // below the window: weight 0, and its block may be released
         const float* vrow =
             vp < kvl ? Vp + ((size_t)clamp_blk(bt[vp >> 4], p.n_blocks) * nkv + g) * D * kBlock + (vp & 15)
                      : SV + ((size_t)(kStageBlocks * l + (vp >> 4) - (kvl >> 4)) * nkv + g) * D * kBlock + (vp & 15);
@@ -665,15 +683,19 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
 // a workgroup.  Ties go to fewer ranges.
 static int attn_ranges(const AttnParams& p) {
   const long pairs = (long)p.nkv * p.ri.L;
-  const long cap = (long)p.max_blocks * kBlock;
-  int best = p.n_chunks;
+  // chunks a lane's rows can see: all of them, or with a window of W the at most
+  // ceil((W + 15) / chunk) + 1 chunks that W - 1 + cols <= W + 15 positions touch
+  const int nc = p.window > 0 ? std::min(p.n_chunks, (p.window + kMaxCols - 1 + p.chunk - 1) / p.chunk + 1)
+                              : p.n_chunks;
+  const long cap = p.window > 0 ? (long)nc * p.chunk : (long)p.max_blocks * kBlock;
+  int best = nc;
   long best_cost = -1;
-  for (int gx = 1; gx <= p.n_chunks; ++gx) {
-    const long per = (p.n_chunks + gx - 1) / gx;
+  for (int gx = 1; gx <= nc; ++gx) {
+    const long per = (nc + gx - 1) / gx;
     if (per * (p.chunk / kBlock) > kAttnWgBlocks) continue;
     long longest = 0;
     for (int x = 0; x < gx; ++x) {
-      const long c0 = (long)x * p.n_chunks / gx, c1 = (long)(x + 1) * p.n_chunks / gx;
+      const long c0 = (long)x * nc / gx, c1 = (long)(x + 1) * nc / gx;
       const long pos = std::min(c1 * p.chunk, cap) - c0 * p.chunk;
       longest = std::max(longest, (pos + 63) / 64);
     }
@@ -716,13 +738,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o, int rp
   const int kvl = max(0, min(p.kv_len[l], cap - cols));
   const int end = kvl + cols;
   const int nch = min((end + p.chunk - 1) / p.chunk, p.n_chunks);
+  const int cl = p.window > 0 ? max(0, kvl - p.window + 1) / p.chunk : 0;   // first chunk in any window
   const float* base = p.part + ((size_t)l * p.nkv + g) * p.n_chunks * 64 * PW;
   const size_t cstride = (size_t)64 * PW;
   const size_t io = part_index(m, 4 * dq), im = part_index(m, D);
   // one pass in chunk order with a running max M: acc = sum_c O_c 2^(m_c - M), rescaled
   // (in float64) whenever M grows
   double M = -INFINITY, Oc[4] = {0.0, 0.0, 0.0, 0.0}, Lc = 0.0;
-  for (int c0 = 0; c0 < nch; c0 += kCombineBatch) {
+  for (int c0 = cl; c0 < nch; c0 += kCombineBatch) {
     f32x4 ov[kCombineBatch];
     float mv[kCombineBatch], lv[kCombineBatch];
 #pragma unroll

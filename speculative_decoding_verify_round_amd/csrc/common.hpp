@@ -430,6 +430,7 @@ struct AttnParams {
   const float* P;         // [S][R][(nq + 2 nkv) d]
   int S;
   const double* rope;     // [R][d / 2] (cos, sin) in float64, or null (no positional encoding)
+  int window;             // 0: full attention; W > 0: a row at position P sees P - W + 1 .. P
 };
 
 }  // namespace sv

@@ -171,6 +171,14 @@ int max_cols(const sv::RowInfo& ri) {
 }
 
 // Common validation of a round; fills ri and the workspace layout.
+// The window of the attention layer with this index among the attention layers: every
+// window_global_every-th one keeps full attention (0 = none does).
+int layer_window(const spec_model_desc& d, int attn_index) {
+  const int g = d.window_global_every;
+  if (d.sliding_window <= 0 || (g > 0 && attn_index % g == g - 1)) return 0;
+  return d.sliding_window;
+}
+
 int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri, WsLayout& w) {
   if (!m) return SPEC_E_INVAL;
   int st = build_rowinfo(r, ri);
@@ -322,6 +330,7 @@ int forward(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, con
       ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
       ap.part = at<float>(ws, w.apart);
       ap.ri = ri;
+      ap.window = layer_window(m->d, L.attn_index);
       {
         ProfScope ps(m, SPEC_K_ATTN, st);
         SV_CHECK(sv::launch_attention(ap, bf, st));
@@ -399,6 +408,13 @@ int spec_plan_drafts(int k, int row_budget, int lanes) {
   return std::max(0, std::min(k, rows / lanes - 1));
 }
 
+int spec_window_live_block(int kv_len, int window) {
+  if (kv_len < 0 || window < 0) return SPEC_E_INVAL;
+  if (window == 0) return 0;
+  // windowed layers read from the 64-position stage that holds the lowest window start
+  return std::max(0, kv_len - window + 1) / 64 * (64 / SPEC_KV_BLOCK);
+}
+
 int spec_model_create(const spec_model_desc* desc, spec_model** out) {
   if (!desc || !out) return SPEC_E_INVAL;
   *out = nullptr;
@@ -408,6 +424,7 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
   if (d.kv_block != SPEC_KV_BLOCK) return SPEC_E_UNSUPPORTED;
   if (!d.lm_head) return SPEC_E_INVAL;
   if (!(d.rms_eps >= 0.f) || !(d.rope_theta >= 0.f)) return SPEC_E_INVAL;
+  if (d.sliding_window < 0 || d.window_global_every < 0) return SPEC_E_INVAL;
   const bool bf = d.dtype == SPEC_BF16;
   if (bf && (d.hidden % 256) != 0) return SPEC_E_UNSUPPORTED;
   if ((d.hidden % 4) != 0 || d.hidden > 8192) return SPEC_E_UNSUPPORTED;

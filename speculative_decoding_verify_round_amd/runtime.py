@@ -85,6 +85,8 @@ class DeviceModel:
         desc.rms_eps, desc.rope_theta = cfg.rms_eps, cfg.rope_theta
         desc.kv_block = cfg.kv_block
         desc.attn_chunk = attn_chunk
+        desc.sliding_window = cfg.sliding_window
+        desc.window_global_every = cfg.window_global_every
         desc.embed = self.t["embed"].data_ptr() if "embed" in self.t else None
         desc.lm_head = self.t["lm_head"].data_ptr()
         desc.final_norm = self.t["final_norm"].data_ptr()

@@ -64,6 +64,7 @@ def make_desc(**kw):
     for i in range(d.n_layers):
         lw[i] = B.SpecLayerWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     d.layers = C.cast(lw, C.POINTER(B.SpecLayerWeights))
+    d.sliding_window, d.window_global_every = kw.get("sliding_window", 0), kw.get("window_global_every", 0)
     d._keep = (arr, lw)
     return d
 
@@ -236,3 +237,17 @@ def test_penalty_fields_validate(model):
     assert lib.spec_counts_add(FAKE, 0, 2, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
     assert lib.spec_counts_add(FAKE, 100, 0, FAKE, FAKE, 16, None) == B.SPEC_E_INVAL
     assert lib.spec_counts_add(FAKE, 100, 2, FAKE, FAKE, 0, None) == B.SPEC_E_INVAL
+
+
+def test_window_fields_and_live_block():
+    """Negative window settings are refused; the first block a windowed round reads is the
+    64-position stage holding the lowest window start, kv_len - W + 1."""
+    assert create_status(sliding_window=-1) == B.SPEC_E_INVAL
+    assert create_status(window_global_every=-2) == B.SPEC_E_INVAL
+    lib = B.load_library()
+    assert lib.spec_window_live_block(-1, 8) == B.SPEC_E_INVAL
+    assert lib.spec_window_live_block(10, -1) == B.SPEC_E_INVAL
+    assert lib.spec_window_live_block(5000, 0) == 0
+    for kv, W in ((0, 16), (100, 200), (300, 100), (700, 100), (8192, 1024), (64, 1), (63, 1)):
+        lo = max(0, kv - W + 1)
+        assert lib.spec_window_live_block(kv, W) == (lo // 64) * 4, (kv, W)

@@ -138,7 +138,10 @@ def round_bytes(cfg, lanes, k, context, committed_mean):
     per_layer = (cfg.qkv_rows * H + H * cfg.n_q_heads * cfg.head_dim + 3 * F * H) * ab
     weights = cfg.n_layers * per_layer + V * H * ab
     kv_row = 2 * cfg.n_kv_heads * cfg.head_dim * ab * cfg.n_attn
-    kv = lanes * context * kv_row
+    # a windowed layer reads only the positions some row of the lane can see
+    kv_layer = kv_row // max(cfg.n_attn, 1)
+    seen = [min(context, cfg.layer_window(i) + k) if cfg.layer_window(i) else context for i in range(cfg.n_attn)]
+    kv = lanes * kv_layer * sum(seen)
     staging = R * kv_row
     compaction = lanes * committed_mean * kv_row * 2
     embed = R * H * ab
@@ -272,6 +275,12 @@ def main():
     ap.add_argument("--penalties", default=None, metavar="PRESENCE,FREQUENCY",
                     help="per-row presence and frequency penalties on every round (plain ones too), with "
                          "each lane's counts kept on the device; the lanes' histories are 8K seeded tokens")
+    ap.add_argument("--attn-chunk", type=int, default=0,
+                    help="positions per split-KV chunk (default 1024; 512 with --window)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window target: attention layers see their last W positions")
+    ap.add_argument("--window-global-every", type=int, default=0,
+                    help="with --window, every g-th attention layer keeps full attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (the reference for HBM counters)")
     args = ap.parse_args()
@@ -284,6 +293,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.config)
+    if args.window:
+        cfg = cfg.with_(sliding_window=args.window, window_global_every=args.window_global_every)
     L, k, ctx = args.lanes, args.k, args.context
     R = L * (k + 1)
     steps, warm = args.steps, args.warmup
@@ -295,7 +306,11 @@ def main():
     # split-KV chunks of 1024 positions: at 8K context that halves the chunk partials the
     # combine merges (the chunk grid is a per-model setting; results depend on it only
     # through the fixed order of the merge)
-    dm = DeviceModel(cfg, w, prepacked=True, attn_chunk=1024)
+    # a window of W positions spans only about W / chunk + 1 chunks, and the chunk is the
+    # unit the ranges of one (lane, kv head) are cut from: smaller chunks keep more
+    # workgroups busy on a windowed layer
+    chunk = args.attn_chunk or (512 if args.window else 1024)
+    dm = DeviceModel(cfg, w, prepacked=True, attn_chunk=chunk)
     del w
     bt, nb = synth.block_table(cfg, L, max_blocks)
     dc = DeviceCache(dm, L, max_blocks, nb, block_table=bt, kv_len=[ctx] * L)
@@ -439,7 +454,11 @@ def main():
                                f"vocab {cfg.vocab}; {L} lanes x (k={k} + 1) = {R} rows, context {ctx}, greedy, "
                                f"drafts planted at slot acceptance 0.9..0.35"
                                + (f", presence/frequency penalties {pen['presence']}/{pen['frequency']} per row"
-                                  if pen else ""),
+                                  if pen else "")
+                               + (f", sliding window {cfg.sliding_window}"
+                                  + (f" (every {cfg.window_global_every}th attention layer global)"
+                                     if cfg.window_global_every else " on every attention layer")
+                                  if cfg.sliding_window else ""),
                    "lanes": L, "k": k, "rows": R, "context": ctx, "mode": "greedy"},
         "verify_rows_per_s": round(rows_s, 1),
         "tokens_per_round": round(tpr, 3),

@@ -159,3 +159,19 @@ def test_penalised_greedy_loop_tiny_fp32_equals_plain_penalised_greedy():
     assert np.array_equal(cd.cpu().numpy()[0], want)
     log(f"penalised tiny loop: {len(out)} tokens")
     pair.close()
+
+
+def test_penalised_sampled_rounds_tiny_fp32():
+    """The fp32 LM head and residual race with penalties, sampled at T = 0.8."""
+    cfg = synth.get_config("tiny-fp32").with_(context=37)
+    pair = Pair(cfg, lanes=4, context=37, max_blocks=8)
+    counts = _counts(cfg, 4, 12)
+    bad = []
+    for rnd in range(3):
+        q, d = synth.drafter_rows(cfg.input_seed, 70 + rnd, 4 * 5, cfg.vocab)
+        toks = [[100 + l] + [int(x) for x in d[l * 5 + 1:(l + 1) * 5]] for l in range(4)]
+        _, _, _, _, _, _, _, mism = _penalised_round(pair, toks, counts, "sampled", 0.8, q, seed=7 + rnd)
+        bad += mism
+    log(f"penalised sampled fp32: {bad}")
+    assert not bad
+    pair.close()

@@ -238,23 +238,30 @@ class DeviceCache:
         return out
 
     def ngram_rounds(self, history: torch.Tensor, hist_len: torch.Tensor, rounds: int, k: int, n_max: int,
-                     n_min: int = 1, stream: Optional[int] = None):
+                     n_min: int = 1, stream: Optional[int] = None, counts: Optional[torch.Tensor] = None,
+                     presence: float = 0.0, frequency: float = 0.0):
         """`rounds` greedy verify rounds on every lane, drafts from the lane's own history by the
         n-gram drafter, k + 1 columns per lane, each round's committed run appended to the
         history: device work only, no host round trip between rounds.  history: device int32
         [lanes][max_len] ending with each lane's anchor; hist_len: device int32 [lanes].
+        With counts (device int32 [lanes][vocab], each lane's tokens up to its anchor) every
+        round applies the per-row penalties and adds its committed runs to the counts.
         Returns the device tensors of the last round (tokens [lanes][k + 1], n_match [lanes])."""
         L, max_len = history.shape
         s = _stream(stream)
         tokens = torch.empty((L, k + 1), dtype=torch.int32, device=self.device)
         n_match = torch.empty(L, dtype=torch.int32, device=self.device)
-        rc = self.round([[0] * (k + 1)] * L, tokens_dev=tokens.view(-1))
+        rc = self.round([[0] * (k + 1)] * L, tokens_dev=tokens.view(-1), counts=counts, presence=presence,
+                        frequency=frequency)
         for _ in range(rounds):
             B.spec_ngram_draft(history.data_ptr(), hist_len.data_ptr(), L, max_len, k, n_max, n_min,
                                tokens.data_ptr(), n_match.data_ptr(), s)
             self.verify(rc, s)
             self.accept(rc, stats=False, stream=s)
             self.commit(rc, stream=s)
+            if counts is not None:
+                B.spec_counts_add(counts.data_ptr(), self.model.cfg.vocab, L, self.committed.data_ptr(),
+                                  self.out_tokens.data_ptr(), self.out_tokens.shape[1], s)
             B.spec_history_append(history.data_ptr(), hist_len.data_ptr(), L, max_len, self.committed.data_ptr(),
                                   self.out_tokens.data_ptr(), self.out_tokens.shape[1], s)
         return tokens, n_match

@@ -175,3 +175,53 @@ def test_penalised_sampled_rounds_tiny_fp32():
     log(f"penalised sampled fp32: {bad}")
     assert not bad
     pair.close()
+
+
+def test_penalised_ngram_device_loop_equals_plain_penalised_greedy():
+    """The n-gram drafter's device loop with penalties and device-kept counts (one lane's
+    prompt repeats itself) commits the oracle's plain penalised greedy tokens.  Mild
+    penalties, so that the repeating lane still keeps copied guesses."""
+    pres, freq = 0.05, 0.03
+    cfg = synth.get_config("tiny-fp32")
+    pair = Pair(cfg, lanes=2, context=0, max_blocks=24)
+    prompts = [[int(t) for t in synth.prompt_tokens(cfg)],
+               [int(t) for t in synth.uniform_tokens(cfg.input_seed, 91, 64, cfg.vocab)]]
+    prompts[1][32:] = prompts[1][:32]
+    pair.om.prefill(pair.oc, prompts, chunk=16)
+    for c0 in range(0, 63, 16):
+        c = min(16, 63 - c0)
+        rc = pair.dc.round([p[c0:c0 + c] for p in prompts])
+        pair.dc.verify(rc)
+        pair.dc.commit(rc, torch.full((2,), c, dtype=torch.int32, device="cuda"))
+    counts0 = np.stack([np.bincount(p, minlength=cfg.vocab) for p in prompts]).astype(np.int32)
+    rounds, k = 10, 7
+    refs = []
+    for l in range(2):
+        one = pair.oc.copy()
+        cnt, cur, ref = counts0[l].copy(), prompts[l][-1], []
+        for _ in range(rounds * (k + 1)):
+            res = pair.om.verify_round(one, [[cur] if i == l else [0] for i in range(2)])
+            row = res.logits[res.lane_rows[l].start]
+            nxt = argmax_lowest((row - penalty(cnt, pres, freq)).astype(np.float32))
+            pair.om.commit(one, res, [1, 1])
+            ref.append(nxt)
+            cnt[nxt] += 1
+            cur = nxt
+        refs.append(ref)
+    max_len = 64 + rounds * (k + 1)
+    hist = torch.zeros((2, max_len), dtype=torch.int32, device="cuda")
+    hist[:, :64] = torch.tensor(prompts, dtype=torch.int32).cuda()
+    hlen = torch.full((2,), 64, dtype=torch.int32, device="cuda")
+    cd = torch.from_numpy(counts0).cuda()
+    pair.dc.ngram_rounds(hist, hlen, rounds, k, 3, counts=cd, presence=pres, frequency=freq)
+    torch.cuda.synchronize()
+    hl, h = hlen.cpu().tolist(), hist.cpu().numpy()
+    for l in range(2):
+        got = [int(t) for t in h[l, 64:hl[l]]]
+        assert got == refs[l][:len(got)], l
+        want = counts0[l].copy()
+        add_counts(want, got)
+        assert np.array_equal(cd.cpu().numpy()[l], want), l
+    log(f"penalised n-gram loop: {[hl[l] - 64 for l in range(2)]} tokens in {rounds} rounds")
+    assert hl[1] - 64 > rounds            # the repeating lane kept guesses
+    pair.close()

@@ -42,6 +42,9 @@ CASES = [
     ("bf16 W100 mixed ctx700", "bf16", 100, 2, 700, 256),
     ("bf16 W300 ctx1000 chunk512", "bf16", 300, 0, 1000, 512),
     ("bf16 W3 inside own columns", "bf16", 3, 0, 37, 256),
+    ("bf16 window start on a chunk boundary", "bf16", 189, 0, 700, 256),
+    ("bf16 W2000 longer than the context", "bf16", 2000, 0, 700, 256),
+    ("bf16 W64 one stage", "bf16", 64, 0, 1000, 256),
     ("f32 W100 ctx700 chunk256", "f32", 100, 0, 700, 256),
     ("f32 W5 ctx37", "f32", 5, 0, 37, 256),
 ]

@@ -275,6 +275,9 @@ def main():
     ap.add_argument("--penalties", default=None, metavar="PRESENCE,FREQUENCY",
                     help="per-row presence and frequency penalties on every round (plain ones too), with "
                          "each lane's counts kept on the device; the lanes' histories are 8K seeded tokens")
+    ap.add_argument("--sampled", type=float, default=0.0, metavar="T",
+                    help="sampled verify at temperature T (textbook rule, residual race) against seeded "
+                         "drafter distributions, instead of greedy")
     ap.add_argument("--attn-chunk", type=int, default=0,
                     help="positions per split-KV chunk (default 1024; 512 with --window)")
     ap.add_argument("--window", type=int, default=0,
@@ -391,6 +394,17 @@ def main():
             d.append(t)
         return d
 
+    samp = {}
+    if args.sampled > 0:
+        if args.drafter != "planted":
+            print("--sampled runs with the planted drafts", file=sys.stderr)
+            sys.exit(2)
+        # the drafter's distributions: seeded softmax rows (the planted drafts stay the
+        # drafted tokens; q only enters the acceptance ratios and the residual)
+        gq = torch.Generator(device="cuda").manual_seed(cfg.input_seed + 5)
+        qd = torch.softmax(2.0 * torch.randn((R, cfg.vocab), generator=gq, device="cuda"), dim=-1)
+        samp = {"mode": "sampled", "temperature": args.sampled, "q_probs": qd}
+    n_step = [0]
     tok_host = torch.empty(R, dtype=torch.int32).pin_memory()
     tok_dev = torch.empty(R, dtype=torch.int32, device="cuda")
     committed_log = []
@@ -401,7 +415,10 @@ def main():
             flat += [int(ref[l, pos[l]])] + drafts_for(l)
         tok_host.copy_(torch.tensor(flat, dtype=torch.int32))
         tok_dev.copy_(tok_host, non_blocking=True)
-        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev, **pen)
+        n_step[0] += 1
+        if samp:
+            samp["seed"] = 1000 + n_step[0]
+        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev, **pen, **samp)
         dc.verify(rc)
         dc.accept(rc, stats=False)
         dc.commit(rc)
@@ -451,20 +468,22 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer dense bf16 decoder H{cfg.hidden}, "
                                f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, FFN {cfg.ffn}, "
-                               f"vocab {cfg.vocab}; {L} lanes x (k={k} + 1) = {R} rows, context {ctx}, greedy, "
-                               f"drafts planted at slot acceptance 0.9..0.35"
+                               f"vocab {cfg.vocab}; {L} lanes x (k={k} + 1) = {R} rows, context {ctx}, "
+                               + (f"sampled at T {args.sampled}, " if samp else "greedy, ")
+                               + f"drafts planted at slot acceptance 0.9..0.35"
                                + (f", presence/frequency penalties {pen['presence']}/{pen['frequency']} per row"
                                   if pen else "")
                                + (f", sliding window {cfg.sliding_window}"
                                   + (f" (every {cfg.window_global_every}th attention layer global)"
                                      if cfg.window_global_every else " on every attention layer")
                                   if cfg.sliding_window else ""),
-                   "lanes": L, "k": k, "rows": R, "context": ctx, "mode": "greedy"},
+                   "lanes": L, "k": k, "rows": R, "context": ctx, "mode": "sampled" if samp else "greedy"},
         "verify_rows_per_s": round(rows_s, 1),
         "tokens_per_round": round(tpr, 3),
         "textbook_tokens_per_round": round(textbook, 3),
         "drafter": f"planted α 0.9..0.35 · depth {k}, no gate · acceptance "
-                   f"{(committed - 1).sum()}/{committed.size * k} guesses · greedy · {L} streams",
+                   f"{(committed - 1).sum()}/{committed.size * k} guesses · "
+                   f"{'sampled' if samp else 'greedy'} · {L} streams",
         "plain_round_ms": round(plain_ms, 3),
         "verify_over_plain": round(ms_step / plain_ms, 3),
         "round_roofline_frac": round(rbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

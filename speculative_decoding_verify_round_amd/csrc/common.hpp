@@ -297,6 +297,7 @@ struct LmParams {
   RowInfo ri;
   const int32_t* counts;   // [L][V] token counts of each lane up to its anchor, or null (no penalties)
   float presence, frequency;
+  float* zs;               // bf16 sampled rounds: every row's logits [R][V] (before penalties), or null
 };
 
 // Row statistics after reducing the LM-head partials (internal workspace form).
@@ -333,6 +334,7 @@ struct RaceParams {
   const int32_t* tokens;   // [R] round tokens (the drafts before the rejected row)
   const int32_t* counts;   // [L][V] or null, as LmParams
   float presence, frequency;
+  const float* zs;         // the LM head's stored logits [R][V] (bf16 model)
 };
 
 // Presence / frequency penalty of one row: row j of a lane conditions on the lane's

@@ -929,6 +929,8 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       if (tile[j] < tiles) {   // wave-uniform; every lane joins tile_stats' cross-lane shuffles
+        if (p.zs && r < p.R)   // sampled: kept for the residual draw of a rejected row
+          *reinterpret_cast<f32x4*>(p.zs + (size_t)r * p.V + tile[j] * 16 + 4 * kq) = acc[j][t];
         float z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[e] = acc[j][t][e] - pz[j][e];
@@ -1149,6 +1151,35 @@ __global__ void k_race_f32(RaceParams p) {
     float* o = p.part + ((size_t)l * p.groups + blockIdx.x) * 4;
     o[0] = sh[0].k; o[1] = __int_as_float(sh[0].i); o[2] = sh[0].fk; o[3] = __int_as_float(sh[0].fi);
   }
+}
+
+// bf16 model: the rejected row's logits as the LM head stored them (the same values its
+// statistics saw), so the draw reads R x 4 bytes per token of that row instead of
+// streaming the head's weights again.  Workgroup g covers tokens 128 g .. 128 g + 127 (the
+// LM head's group), 32 threads per lane, 8 lanes at a time.
+__global__ __launch_bounds__(256) void k_race_stored(RaceParams p) {
+  const int tid = threadIdx.x, sub = tid & 31;
+  const int v0 = blockIdx.x * 128 + 4 * sub;
+  for (int l = tid >> 5; l < p.L; l += 8) {   // uniform per 32-thread group
+    RaceKey rk = race_identity();
+    const int rr = p.dec[l].resid_row;
+    if (rr >= 0 && v0 < p.V) {
+      const f32x4 zv = *reinterpret_cast<const f32x4*>(p.zs + (size_t)rr * p.V + v0);
+      const float z[4] = {zv[0], zv[1], zv[2], zv[3]};
+      race_lane(z, v0, p, l, rk);
+    }
+#pragma unroll
+    for (int x = 1; x <= 16; x <<= 1) rk = race_xor(rk, x);
+    if (sub == 0) {
+      float* o = p.part + ((size_t)l * p.groups + blockIdx.x) * 4;
+      o[0] = rk.k; o[1] = __int_as_float(rk.i); o[2] = rk.fk; o[3] = __int_as_float(rk.fi);
+    }
+  }
+}
+
+int launch_race_stored(const RaceParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_race_stored, dim3(p.groups), dim3(256), 0, st, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_race(const RaceParams& p, bool bf16, hipStream_t st) {

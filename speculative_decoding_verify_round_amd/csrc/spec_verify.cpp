@@ -75,7 +75,7 @@ int split_for(const spec_model* m, int N, int K, bool fused_pair) {
 }
 
 struct WsLayout {
-  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, total;
+  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, zs, total;
   int n_cnt;                    // arrival counters of the gate/up cut units
   size_t stage_layer_elems;     // elements per attention layer in stk/stv
   size_t gst_layer_floats;      // floats per gdn layer in gst
@@ -131,6 +131,7 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.dec = take((size_t)L * sizeof(sv::LaneDecision));
   w.racex = take(m->bf16 ? (size_t)sv::round16(L) * H * 4 : 0);
   w.racep = take((size_t)L * m->lm_groups * 16);
+  w.zs = take(m->bf16 ? (size_t)R * d.vocab * 4 : 0);
   w.total = off;
   return w;
 }
@@ -378,6 +379,7 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   p.key0 = (uint32_t)(r->seed & 0xffffffffu);
   p.key1 = (uint32_t)(r->seed >> 32);
   p.part = at<sv::LmPartial>(r->workspace, w.lmp);
+  p.zs = m->bf16 && r->mode == SPEC_SAMPLED ? at<float>(r->workspace, w.zs) : nullptr;
   p.ri = ri;
   p.counts = r->counts;
   p.presence = r->presence_penalty;
@@ -542,14 +544,8 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
   if (sampled) {
     sv::RaceParams p{};
     p.xs = m->d.n_layers == 0 ? 1 : 2;
-    if (m->bf16) {
-      p.X = at<void>(ws, w.racex);
-      p.xplane = sv::act_plane(ri.L, m->d.hidden);
-      SV_CHECK(sv::launch_gather_rows(at<void>(ws, w.h), sv::act_plane(ri.R, m->d.hidden), at<void>(ws, w.racex),
-                                      p.xplane, at<sv::LaneDecision>(ws, w.dec), ri.L, m->d.hidden, p.xs, s));
-    } else {
-      p.X = at<void>(ws, w.h);
-    }
+    p.X = at<void>(ws, w.h);   // fp32: the round's hidden rows (bf16 reads the stored logits)
+    p.zs = at<float>(ws, w.zs);
     p.W = m->d.lm_head;
     p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
     p.groups = m->lm_groups;
@@ -564,7 +560,7 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
     p.counts = r->counts;
     p.presence = r->presence_penalty;
     p.frequency = r->frequency_penalty;
-    SV_CHECK(sv::launch_race(p, m->bf16, s));
+    SV_CHECK(m->bf16 ? sv::launch_race_stored(p, s) : sv::launch_race(p, false, s));
     SV_CHECK(sv::launch_race_finish(at<float>(ws, w.racep), m->lm_groups, at<sv::LaneDecision>(ws, w.dec),
                                     out_tokens, ri, s));
   }

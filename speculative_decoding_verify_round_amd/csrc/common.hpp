@@ -317,11 +317,10 @@ struct LaneDecision {
 };
 
 struct RaceParams {
-  const void* X;           // bf16: the rejected rows gathered into packed planes (lane l = row l);
-                           // float: the round's hidden rows [R][H]
+  const void* X;           // fp32 model: the round's hidden rows [R][H]
   size_t xplane;
   int xs;
-  const void* W;           // packed [V][H] (bf16) or row-major [V][H] float
+  const void* W;           // fp32 model: row-major [V][H] float
   int R, V, H, L;
   int groups;
   const float* q;          // [R][V]

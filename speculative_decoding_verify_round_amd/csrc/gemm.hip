@@ -1009,8 +1009,9 @@ int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st) {
 int lmhead_groups(int V, bool bf16) { return bf16 ? ((V >> 4) + 7) / 8 : (V + 255) / 256; }
 
 // ------------------------------------------------------------------------------- residual race
-// Sampled mode, lanes whose draft i was rejected: recompute the logits of the
-// rejected row (row of column i - 1), form p_v = exp((z_v - m) / T) / se, and
+// Sampled mode, lanes whose draft i was rejected: take the logits of the rejected row
+// (row of column i - 1; stored by the bf16 LM head, recomputed in the fp32 path), form
+// p_v = exp((z_v - m) / T) / se, and
 // run the exponential race argmin_v E_v / max(0, p_v - q_v) with
 // E_v = -ln U(seed; position kv_len + i, lane, race, v).  A fallback race with
 // weights p_v is kept alongside for the case where every residual weight is 0.
@@ -1065,59 +1066,6 @@ __device__ __forceinline__ RaceKey race_xor(RaceKey r, int x) {
   RaceKey o;
   o.k = __shfl_xor(r.k, x); o.i = __shfl_xor(r.i, x); o.fk = __shfl_xor(r.fk, x); o.fi = __shfl_xor(r.fi, x);
   return race_merge(r, o);
-}
-
-template <int RT, int XS>
-__global__ __launch_bounds__(256, 2) void k_race_bf16(RaceParams p) {
-  constexpr int KC = chunk_steps<RT>(), T = 2;
-  using C = CoreShape<RT, T, XS, KC>;
-  static_assert(2 * C::NB * 64 * sizeof(u32x4) >= 4 * kMaxLanes * sizeof(RaceKey), "keys fit the X ring");
-  __shared__ u32x4 xl[2 * C::NB * 64];
-  // any lane with a rejection?  (uniform across the grid)
-  bool any = false;
-  for (int l = 0; l < p.L; ++l) any |= p.dec[l].resid_row >= 0;
-  if (!any) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int tiles = p.V >> 4, KS = p.H >> 5;
-  const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
-  int tile[T];
-  const bf16_t* wp[T];
-#pragma unroll
-  for (int j = 0; j < T; ++j) {
-    tile[j] = (blockIdx.x * 4 + wave) * T + j;
-    wp[j] = W + (size_t)min(tile[j], tiles - 1) * KS * 512 + lane * 8;
-  }
-  f32x4 acc[T][RT];
-#pragma unroll
-  for (int j = 0; j < T; ++j)
-#pragma unroll
-    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // X: the rejected rows gathered lane by lane (row tile t holds lanes 16 t ..)
-  proj_core<RT, T, XS, KC>(wp, 512, reinterpret_cast<const bf16_t*>(p.X), p.xplane, KS, 0, p.H >> 8, xl, acc);
-  RaceKey* sh = reinterpret_cast<RaceKey*>(xl);
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int l = t * 16 + r16;
-    RaceKey rk = race_identity();
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      if (tile[j] < tiles && l < p.L && p.dec[l].resid_row >= 0) {
-        const float z[4] = {acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]};
-        race_lane(z, tile[j] * 16 + 4 * kq, p, l, rk);
-      }
-    }
-    rk = race_xor(rk, 16);
-    rk = race_xor(rk, 32);
-    if (kq == 0 && l < p.L) sh[wave * kMaxLanes + l] = rk;
-  }
-  __syncthreads();
-  for (int l = threadIdx.x; l < p.L; l += blockDim.x) {
-    RaceKey r = sh[l];
-    for (int w = 1; w < 4; ++w) r = race_merge(r, sh[w * kMaxLanes + l]);
-    float* o = p.part + ((size_t)l * p.groups + blockIdx.x) * 4;
-    o[0] = r.k; o[1] = __int_as_float(r.i); o[2] = r.fk; o[3] = __int_as_float(r.fi);
-  }
 }
 
 __global__ void k_race_f32(RaceParams p) {
@@ -1182,47 +1130,11 @@ int launch_race_stored(const RaceParams& p, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_race(const RaceParams& p, bool bf16, hipStream_t st) {
-  if (bf16) {
-    const int RT = (p.L + 15) / 16;
-    dim3 grid(p.groups), block(256);
-#define SV_RACE(RT_, XS_) hipLaunchKernelGGL((k_race_bf16<RT_, XS_>), grid, block, 0, st, p)
-    if (p.xs == 1) {
-      switch (RT) { case 1: SV_RACE(1, 1); break; case 2: SV_RACE(2, 1); break; case 3: SV_RACE(3, 1); break; default: SV_RACE(4, 1); }
-    } else {
-      switch (RT) { case 1: SV_RACE(1, 2); break; case 2: SV_RACE(2, 2); break; case 3: SV_RACE(3, 2); break; default: SV_RACE(4, 2); }
-    }
-#undef SV_RACE
-  } else {
-    dim3 grid(p.groups, p.L), block(256);
-    hipLaunchKernelGGL(k_race_f32, grid, block, 0, st, p);
-  }
+int launch_race(const RaceParams& p, hipStream_t st) {
+  dim3 grid(p.groups, p.L), block(256);
+  hipLaunchKernelGGL(k_race_f32, grid, block, 0, st, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// Sampled residual: the rejected row of every lane, gathered into packed planes
-// (lane l -> row l); lanes without a rejection copy row 0 (their keys are discarded).
-__global__ void k_gather_rows(const bf16_t* __restrict__ src, size_t src_plane, bf16_t* __restrict__ dst,
-                              size_t dst_plane, const LaneDecision* dec, int L, int H, int xs) {
-  const int KS = H >> 5;
-  const size_t n = (size_t)L * H;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int l = (int)(i / H), k = (int)(i - (size_t)l * H);
-    const int row = max(dec[l].resid_row, 0);
-    const size_t so = frag_off(row, k, KS), d = frag_off(l, k, KS);
-    dst[d] = src[so];
-    if (xs == 2) dst[dst_plane + d] = src[src_plane + so];
-  }
-}
-
-int launch_gather_rows(const void* src, size_t src_plane, void* dst, size_t dst_plane, const LaneDecision* dec,
-                       int L, int H, int xs, hipStream_t st) {
-  const size_t n = (size_t)L * H;
-  const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
-  hipLaunchKernelGGL(k_gather_rows, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t*>(src), src_plane, reinterpret_cast<bf16_t*>(dst), dst_plane, dec,
-                     L, H, xs);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
 
 }  // namespace sv

@@ -15,10 +15,8 @@ int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st);
 // LM head statistics and the residual race
 int lmhead_groups(int V, bool bf16);
 int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st);
-int launch_race(const RaceParams& p, bool bf16, hipStream_t st);
+int launch_race(const RaceParams& p, hipStream_t st);
 int launch_race_stored(const RaceParams& p, hipStream_t st);
-int launch_gather_rows(const void* src, size_t src_plane, void* dst, size_t dst_plane, const LaneDecision* dec,
-                       int L, int H, int xs, hipStream_t st);
 
 // fragment packing
 int launch_pack_weight(const void* src, void* dst, int N, int K, hipStream_t st);

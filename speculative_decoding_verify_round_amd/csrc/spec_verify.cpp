@@ -75,7 +75,7 @@ int split_for(const spec_model* m, int N, int K, bool fused_pair) {
 }
 
 struct WsLayout {
-  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racex, racep, zs, total;
+  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racep, zs, total;
   int n_cnt;                    // arrival counters of the gate/up cut units
   size_t stage_layer_elems;     // elements per attention layer in stk/stv
   size_t gst_layer_floats;      // floats per gdn layer in gst
@@ -129,7 +129,6 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.lmp = take((size_t)R * m->lm_groups * sizeof(sv::LmPartial));
   w.rstat = take((size_t)R * sizeof(sv::RowStat));
   w.dec = take((size_t)L * sizeof(sv::LaneDecision));
-  w.racex = take(m->bf16 ? (size_t)sv::round16(L) * H * 4 : 0);
   w.racep = take((size_t)L * m->lm_groups * 16);
   w.zs = take(m->bf16 ? (size_t)R * d.vocab * 4 : 0);
   w.total = off;
@@ -560,7 +559,7 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
     p.counts = r->counts;
     p.presence = r->presence_penalty;
     p.frequency = r->frequency_penalty;
-    SV_CHECK(m->bf16 ? sv::launch_race_stored(p, s) : sv::launch_race(p, false, s));
+    SV_CHECK(m->bf16 ? sv::launch_race_stored(p, s) : sv::launch_race(p, s));
     SV_CHECK(sv::launch_race_finish(at<float>(ws, w.racep), m->lm_groups, at<sv::LaneDecision>(ws, w.dec),
                                     out_tokens, ri, s));
   }

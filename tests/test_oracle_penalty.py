@@ -94,3 +94,26 @@ def test_speculative_greedy_with_penalties_equals_plain_greedy():
         out += emitted
         anchor = emitted[-1]
     assert out == ref[:len(out)]
+
+
+def test_presence_and_frequency_terms_by_hand():
+    # Hand-computed: a token seen c times loses presence * [c > 0] + frequency * c.
+    # Counts 0, 1, 3 with presence 0.5 and frequency 0.25 lose 0, 0.75 and 1.25; with
+    # frequency 0 every seen token loses exactly the presence, whatever its count.  A
+    # swapped pair (0.25 * [c > 0] + 0.5 c) would give 0, 0.75, 1.75; a presence that
+    # scales with the count (0.5 c + 0.25 c) would give 0, 0.75, 2.25.
+    counts = np.array([0, 1, 3, 0], np.int64)
+    z = np.array([[1.0, 1.0, 1.0, -2.0]], np.float32)
+    got = penalized_rows(z, [0], counts, 0.5, 0.25)
+    assert np.array_equal(got[0], np.array([1.0, 0.25, -0.25, -2.0], np.float32))
+    got = penalized_rows(z, [0], counts, 0.5, 0.0)
+    assert np.array_equal(got[0], np.array([1.0, 0.5, 0.5, -2.0], np.float32))
+    got = penalized_rows(z, [0], counts, 0.0, 0.25)
+    assert np.array_equal(got[0], np.array([1.0, 0.75, 0.25, -2.0], np.float32))
+    # row 1 also counts its draft d_1 = token 0 (count 0 -> 1) and row 2 its d_2 = token 1
+    # (count 1 -> 2): row 1 token 0 loses 0.75; row 2 token 1 loses 0.5 + 0.5 = 1.0
+    z3 = np.zeros((3, 4), np.float32)
+    got = penalized_rows(z3, [2, 0, 1], counts, 0.5, 0.25)
+    assert np.array_equal(got[0], np.array([0.0, -0.75, -1.25, 0.0], np.float32))
+    assert np.array_equal(got[1], np.array([-0.75, -0.75, -1.25, 0.0], np.float32))
+    assert np.array_equal(got[2], np.array([-0.75, -1.0, -1.25, 0.0], np.float32))

@@ -30,8 +30,10 @@
  *     frees device memory; it owns only the host-side spec_model object.
  *   - Streams: `stream` is a hipStream_t passed as void*; NULL is the default
  *     stream.  Work is enqueued asynchronously, with no implicit
- *     synchronisation, no memset nodes and no host<->device copies, so a round
- *     can be captured into a HIP graph.
+ *     synchronisation, no memset nodes and no host<->device copies.  The LM
+ *     head of a sampled round of a bf16 model is one cooperative launch (one
+ *     workgroup per compute unit, all resident at once); every other launch is
+ *     an ordinary kernel launch.
  *   - Rows of a round are packed lane-major: lane l owns rows
  *     [row_start(l), row_start(l) + cols[l]) with row_start(l) = sum of cols of
  *     lanes before l; column 0 is the anchor, column j >= 1 is draft d_j.
@@ -208,11 +210,22 @@ int64_t spec_workspace_bytes(const spec_model* model, int max_lanes, int max_col
 /* The verify forward: every row through every layer once, then the fused LM
  * head's per-row statistics (logits are never written to memory).  Reads the
  * KV pools and recurrent state, writes neither; stages each column's K/V and
- * recurrent inputs in the workspace.  Errors: SPEC_E_INVAL (lanes, cols,
- * NULL buffers, sampled without q_probs or with T <= 0), SPEC_E_RANGE
- * (kv_len_host + cols exceeds 16 * max_blocks), SPEC_E_UNSUPPORTED (recurrent
- * layers with gdn_state == NULL; a lane whose cols x (n_q_heads / n_kv_heads)
- * query rows exceed 64), SPEC_E_WORKSPACE. */
+ * recurrent inputs in the workspace.
+ * Sampled rounds of a bf16 model: the textbook rule needs a row's whole
+ * normaliser before any residual weight is known ("Draft heads and speculative
+ * decoding", "Guess, then check").  The LM head is then one cooperative launch
+ * whose workgroups keep their vocabulary slices' logits on chip across two grid
+ * barriers: they reduce the row statistics, take every lane's accept/reject
+ * decision and run each lane's draw (the residual race on a rejected row, the
+ * bonus race when every draft is kept) on the logits they still hold; the
+ * workspace receives only per-workgroup partials.  This needs vocab / 16 <= 64
+ * per compute unit (vocab <= 262144 on 256 compute units) and vocab * hidden * 2
+ * <= 2^31, else SPEC_E_UNSUPPORTED.
+ * Errors: SPEC_E_INVAL (lanes, cols, NULL buffers, sampled without q_probs or
+ * with T <= 0), SPEC_E_RANGE (kv_len_host + cols exceeds 16 * max_blocks),
+ * SPEC_E_UNSUPPORTED (recurrent layers with gdn_state == NULL; a lane whose
+ * cols x (n_q_heads / n_kv_heads) query rows exceed 64; the sampled bf16 head
+ * limits above), SPEC_E_WORKSPACE. */
 int spec_verify_round(const spec_model* model, const spec_round* round, void* stream);
 
 /* The LM head and row statistics alone, on caller-given final hidden states
@@ -230,7 +243,12 @@ int spec_verify_head(const spec_model* model, const spec_round* round, const voi
  * Outputs (device): committed[lanes] in [1, cols]; out_tokens[lanes][SPEC_MAX_COLS]
  * holds the committed run (kept drafts, then the model's token); row_stats
  * [R] (may be NULL).  Must follow spec_verify_round / spec_verify_head of the
- * same round and workspace. */
+ * same round and workspace.  In a sampled round of a bf16 model the head has
+ * already decided (see spec_verify_round) and this call only gathers the
+ * outcome; committed[l] = 0 there marks a round whose head could not
+ * synchronise its workgroups (a bounded grid-barrier wait ran out, which a
+ * cooperative launch with every workgroup resident does not reach): the
+ * round's outputs are invalid and must be discarded. */
 int spec_accept(const spec_model* model, const spec_round* round, int32_t* committed,
                 int32_t* out_tokens, spec_row_stat* row_stats, void* stream);
 

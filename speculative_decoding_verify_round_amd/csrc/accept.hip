@@ -90,32 +90,11 @@ __global__ void k_lane_accept(const RowStat* rs, const int32_t* tokens, const in
     o[a] = rs[r0 + a].arg;
     d.committed = a + 1;
   } else {
-    const uint32_t kvl = (uint32_t)kv_len[l];
-    int i = 1;
-    for (; i <= k; ++i) {
-      const RowStat s = rs[r0 + i - 1];
-      const int di = tokens[r0 + i];
-      uint32_t c[4] = {kvl + (uint32_t)i, (uint32_t)l, kPurposeAccept, 0u};
-      philox4x32_10(c, key0, key1);
-      const float u = u01(c[0]);
-      const float pd = isnan(s.zn) ? 0.f : expf((s.zn - s.m) * inv_t) / s.se;
-      const float qd = (di >= 0 && di < V) ? q[(size_t)(r0 + i) * V + di] : 0.f;
-      if (u * qd < pd) {
-        o[i - 1] = di;
-        continue;
-      }
-      d.resid_row = r0 + i - 1;
-      d.resid_col = i;
-      d.m = s.m;
-      d.se = s.se;
-      break;
-    }
-    if (i > k) {
-      o[k] = rs[r0 + k].gi;     // bonus token from p_k
-      d.committed = k + 1;
-    } else {
-      d.committed = i;          // token i - 1 of out is written by the race finish
-    }
+    auto qd = [&](int r) {
+      const int t = tokens[r];
+      return (t >= 0 && t < V) ? q[(size_t)r * V + t] : 0.f;
+    };
+    d = decide_sampled(rs, tokens, kv_len, qd, inv_t, key0, key1, ri, l, o);
   }
   dec[l] = d;
   committed[l] = d.committed;
@@ -164,6 +143,72 @@ __global__ __launch_bounds__(256) void k_race_finish(const float* part, int grou
 int launch_race_finish(const float* part, int groups, const LaneDecision* dec, int32_t* out,
                        const RowInfo& ri, hipStream_t st) {
   hipLaunchKernelGGL(k_race_finish, dim3(ri.L), dim3(256), 0, st, part, groups, dec, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Sampled rounds of a bf16 model: the LM head's cooperative launch has already reduced
+// the row statistics, taken every lane's decision and run its draw (residual or bonus
+// race) over each workgroup's vocabulary slice (k_lmhead_coop).  Per lane: the user row
+// statistics, the race partials reduced in workgroup order (min key, lowest index), the
+// committed run.
+// bar[2] set means a grid barrier of the head ran out of time: committed = 0 flags the
+// round as failed.
+__global__ __launch_bounds__(256) void k_accept_coop(const RowStat* rs, const LaneDecision* dec, const float* part,
+                                                      const int* bar, const int32_t* tokens, float inv_t,
+                                                      int32_t* committed, int32_t* out, spec_row_stat_dev* user,
+                                                      RowInfo ri) {
+  __shared__ float sk[256], sf[256];
+  __shared__ int si[256], sfi[256];
+  const int l = blockIdx.x, t = threadIdx.x;
+  const int r0 = ri.lane_start[l], k = ri.lane_cols[l] - 1;
+  const LaneDecision d = dec[l];
+  const int groups = min(max(bar[3], 0), kCUs);
+  if (user && t <= k) {
+    const RowStat s = rs[r0 + t];
+    user[r0 + t].max_logit = s.m;
+    user[r0 + t].lse = s.m * inv_t + logf(s.se);
+    user[r0 + t].argmax = s.arg;
+    user[r0 + t].z_next = s.zn;
+  }
+  int x;
+  {   // the lane's draw: the residual race, or the bonus race when every draft was kept
+    float kk = INFINITY, f = INFINITY;
+    int ki = 0x7fffffff, fi = 0x7fffffff;
+    for (int g = t; g < groups; g += 256) {
+      const float* pp = part + ((size_t)l * groups + g) * 4;
+      const float bk = pp[0], bf = pp[2];
+      const int bi = __float_as_int(pp[1]), bfi = __float_as_int(pp[3]);
+      if (bk < kk || (bk == kk && bi < ki)) { kk = bk; ki = bi; }
+      if (bf < f || (bf == f && bfi < fi)) { f = bf; fi = bfi; }
+    }
+    sk[t] = kk; si[t] = ki; sf[t] = f; sfi[t] = fi;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (t < w) {
+        if (sk[t + w] < sk[t] || (sk[t + w] == sk[t] && si[t + w] < si[t])) { sk[t] = sk[t + w]; si[t] = si[t + w]; }
+        if (sf[t + w] < sf[t] || (sf[t + w] == sf[t] && sfi[t + w] < sfi[t])) { sf[t] = sf[t + w]; sfi[t] = sfi[t + w]; }
+      }
+      __syncthreads();
+    }
+    x = sk[0] < INFINITY ? si[0] : sfi[0];   // residual vanished: draw from p
+  }
+  if (t == 0) {
+    const bool failed = bar[2] != 0;
+    const int c = failed ? 0 : d.committed;
+    committed[l] = c;
+    if (!failed) {
+      int32_t* o = out + (size_t)l * kMaxCols;
+      for (int i = 0; i + 1 < c; ++i) o[i] = tokens[r0 + i + 1];
+      o[c - 1] = x;
+    }
+  }
+}
+
+int launch_accept_coop(const RowStat* rs, const LaneDecision* dec, const float* part, const int* bar,
+                       const int32_t* tokens, float inv_t, int32_t* committed, int32_t* out, void* user_stats,
+                       const RowInfo& ri, hipStream_t st) {
+  hipLaunchKernelGGL(k_accept_coop, dim3(ri.L), dim3(256), 0, st, rs, dec, part, bar, tokens, inv_t, committed, out,
+                     reinterpret_cast<spec_row_stat_dev*>(user_stats), ri);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -281,25 +281,6 @@ struct LmPartial {
   int pad0, pad1;
 };
 
-struct LmParams {
-  const void* X;           // final hidden: packed bf16 planes (bf16 model) or [R][H] float
-  size_t xplane;           // elements per plane
-  int xs;                  // bf16 planes in use (1: exact bf16 hidden states, 2: hi + lo)
-  const void* W;           // packed [V][H] (bf16) or row-major [V][H] float
-  int R, V, H;
-  int groups;              // number of partial groups per row
-  const int32_t* tokens;   // [R] round tokens (next-draft lookup)
-  const int32_t* kv_len;   // [L]
-  float inv_t;             // 1 / T (1 in greedy mode)
-  int sampled;
-  uint32_t key0, key1;     // Philox key
-  LmPartial* part;         // [R][groups]
-  RowInfo ri;
-  const int32_t* counts;   // [L][V] token counts of each lane up to its anchor, or null (no penalties)
-  float presence, frequency;
-  float* zs;               // bf16 sampled rounds: every row's logits [R][V] (before penalties), or null
-};
-
 // Row statistics after reducing the LM-head partials (internal workspace form).
 struct RowStat {
   float m, se, zn, gk;
@@ -316,11 +297,80 @@ struct LaneDecision {
   float pad2, pad3;
 };
 
+struct LmParams {
+  const void* X;           // final hidden: packed bf16 planes (bf16 model) or [R][H] float
+  size_t xplane;           // elements per plane
+  int xs;                  // bf16 planes in use (1: exact bf16 hidden states, 2: hi + lo)
+  const void* W;           // packed [V][H] (bf16) or row-major [V][H] float
+  int R, V, H;
+  int groups;              // number of partial groups per row (the grid of the sampled bf16 head)
+  const int32_t* tokens;   // [R] round tokens (next-draft lookup)
+  const int32_t* kv_len;   // [L]
+  float inv_t;             // 1 / T (1 in greedy mode)
+  int sampled;
+  uint32_t key0, key1;     // Philox key
+  LmPartial* part;         // [R][groups]
+  RowInfo ri;
+  const int32_t* counts;   // [L][V] token counts of each lane up to its anchor, or null (no penalties)
+  float presence, frequency;
+  // sampled bf16 head (one cooperative launch, logits kept on chip): the grid barrier's
+  // counters (kCoopCounters ints, zero at launch), the reduced row statistics, the lane
+  // decisions, the residual race partials [L][groups][4] and the drafter's q [R][V]
+  int* bar;
+  RowStat* rstat;
+  LaneDecision* dec;
+  float* racep;
+  const float* q;
+};
+
+// Counters of the sampled head's grid barriers in the workspace: arrivals at barrier 1
+// and 2, the error flag (a barrier wait that ran out), the grid size.
+constexpr int kCoopCounters = 4;
+
+// The textbook rule on one lane's rows (Leviathan et al., Def. 3.7): draft d_i is kept iff
+// u * q_i(d_i) < p_{i-1}(d_i), u the Philox uniform at (seed; position kv_len + i, lane,
+// accept), p = softmax(z / T) from the row statistics.  qd(r) is the drafter's q of row r
+// at its own draft token (0 for a token outside the vocabulary).  Returns the decision;
+// with o non-null the kept drafts and, when every draft is kept, the bonus token (the
+// race winner of the lane's last row) go to o.  rs may point to global memory or LDS.
+template <typename QD>
+__device__ __forceinline__ LaneDecision decide_sampled(const RowStat* rs, const int32_t* tokens, const int32_t* kv_len,
+                                                       QD qd, float inv_t, uint32_t key0, uint32_t key1,
+                                                       const RowInfo& ri, int l, int32_t* o) {
+  const int r0 = ri.lane_start[l], k = ri.lane_cols[l] - 1;
+  LaneDecision d;
+  d.resid_row = -1; d.resid_col = 0; d.pad = 0; d.m = 0.f; d.se = 1.f; d.pad2 = d.pad3 = 0.f;
+  const uint32_t kvl = (uint32_t)kv_len[l];
+  int i = 1;
+  for (; i <= k; ++i) {
+    const RowStat s = rs[r0 + i - 1];
+    const int di = tokens[r0 + i];
+    uint32_t c[4] = {kvl + (uint32_t)i, (uint32_t)l, kPurposeAccept, 0u};
+    philox4x32_10(c, key0, key1);
+    const float u = u01(c[0]);
+    const float pd = isnan(s.zn) ? 0.f : expf((s.zn - s.m) * inv_t) / s.se;
+    if (u * qd(r0 + i) < pd) {
+      if (o) o[i - 1] = di;
+      continue;
+    }
+    d.resid_row = r0 + i - 1;
+    d.resid_col = i;
+    d.m = s.m;
+    d.se = s.se;
+    break;
+  }
+  if (i > k) {
+    if (o) o[k] = rs[r0 + k].gi;   // bonus token from p_k
+    d.committed = k + 1;
+  } else {
+    d.committed = i;               // token i - 1 is the residual draw
+  }
+  return d;
+}
+// Residual race of an fp32 model (recomputes the rejected row's logits).
 struct RaceParams {
-  const void* X;           // fp32 model: the round's hidden rows [R][H]
-  size_t xplane;
-  int xs;
-  const void* W;           // fp32 model: row-major [V][H] float
+  const void* X;           // the round's hidden rows [R][H] float
+  const void* W;           // row-major [V][H] float
   int R, V, H, L;
   int groups;
   const float* q;          // [R][V]
@@ -333,7 +383,6 @@ struct RaceParams {
   const int32_t* tokens;   // [R] round tokens (the drafts before the rejected row)
   const int32_t* counts;   // [L][V] or null, as LmParams
   float presence, frequency;
-  const float* zs;         // the LM head's stored logits [R][V] (bf16 model)
 };
 
 // Presence / frequency penalty of one row: row j of a lane conditions on the lane's

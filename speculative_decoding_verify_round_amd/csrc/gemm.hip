@@ -772,8 +772,11 @@ int launch_pack_weight(const void* src, void* dst, int N, int K, hipStream_t st)
 }
 
 // Row-major bf16 rows [R][K] -> packed planes: hi = the rows, lo = 0 when xs == 2.
+// Also zeroes nzero counters (the sampled head's grid barrier of the same call).
 __global__ void k_pack_rows(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int R, int K, size_t plane,
-                            int xs) {
+                            int xs, int* zero, int nzero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   const size_t n = (size_t)R * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const int r = (int)(i / K), k = (int)(i - (size_t)r * K);
@@ -783,11 +786,13 @@ __global__ void k_pack_rows(const bf16_t* __restrict__ src, bf16_t* __restrict__
   }
 }
 
-int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, hipStream_t st) {
+int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, int* zero, int nzero,
+                     hipStream_t st) {
   const size_t n = (size_t)R * K;
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(k_pack_rows, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), R, K, plane, xs);
+                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), R, K, plane, xs, zero,
+                     nzero);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -929,8 +934,6 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_bf16(LmParams p) {
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       if (tile[j] < tiles) {   // wave-uniform; every lane joins tile_stats' cross-lane shuffles
-        if (p.zs && r < p.R)   // sampled: kept for the residual draw of a rejected row
-          *reinterpret_cast<f32x4*>(p.zs + (size_t)r * p.V + tile[j] * 16 + 4 * kq) = acc[j][t];
         float z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[e] = acc[j][t][e] - pz[j][e];
@@ -1009,12 +1012,13 @@ int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st) {
 int lmhead_groups(int V, bool bf16) { return bf16 ? ((V >> 4) + 7) / 8 : (V + 255) / 256; }
 
 // ------------------------------------------------------------------------------- residual race
-// Sampled mode, lanes whose draft i was rejected: take the logits of the rejected row
-// (row of column i - 1; stored by the bf16 LM head, recomputed in the fp32 path), form
-// p_v = exp((z_v - m) / T) / se, and
-// run the exponential race argmin_v E_v / max(0, p_v - q_v) with
-// E_v = -ln U(seed; position kv_len + i, lane, race, v).  A fallback race with
-// weights p_v is kept alongside for the case where every residual weight is 0.
+// Sampled mode, lanes whose draft i was rejected: the logits of the rejected row (row of
+// column i - 1) give p_v = exp((z_v - m) / T) / se, and the exponential race
+// argmin_v E_v / max(0, p_v - q_v), E_v = -ln U(seed; position kv_len + i, lane, race, v),
+// draws the residual token.  A fallback race with weights p_v is kept alongside for the
+// case where every residual weight is 0.  A bf16 model runs it inside the LM head's
+// cooperative launch on the logits the workgroups still hold (k_lmhead_coop); an fp32
+// model recomputes the row (k_race_f32).
 
 struct RaceKey {
   float k; int i; float fk; int fi;
@@ -1024,31 +1028,59 @@ __device__ __forceinline__ bool less_key(float k, int i, float bk, int bi) {
   return k < bk || (k == bk && i < bi);
 }
 
-__device__ __forceinline__ void race_lane(const float (&zr)[4], int v0, const RaceParams& p, int l, RaceKey& rk) {
-  const LaneDecision d = p.dec[l];
-  float z[4] = {zr[0], zr[1], zr[2], zr[3]};
-  if (p.counts) {   // the rejected row's penalty, as its statistics had it
-    const RowPenalty rp = row_penalty(p.counts, p.V, p.tokens, p.ri, d.resid_row, p.presence, p.frequency);
+// Penalised logits of the four tokens v0 .. v0 + 3 of row r (raw logits zr).
+__device__ __forceinline__ void penalise_row4(float (&z)[4], const float (&zr)[4], int v0, const LmParams& p, int r) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = zr[e];
+  if (p.counts) {   // the row's penalty, as its statistics had it
+    const RowPenalty rp = row_penalty(p.counts, p.V, p.tokens, p.ri, r, p.presence, p.frequency);
     const int vv[1] = {v0};
     float pz[1][4];
     penalties4<1>(rp, vv, pz);
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] -= pz[0][e];
   }
-  const int qrow = d.resid_row + 1;
+}
+
+// Residual race keys of the four tokens v0 .. v0 + 3 (raw logits zr, the drafter's q at
+// the rejected draft's row) for lane l's decision d.
+__device__ __forceinline__ void race_lane(const float (&zr)[4], const float (&q)[4], int v0, const LmParams& p, int l,
+                                          const LaneDecision& d, RaceKey& rk) {
+  float z[4];
+  penalise_row4(z, zr, v0, p, d.resid_row);
   const uint32_t pos = (uint32_t)(p.kv_len[l] + d.resid_col);
   uint32_t c[4] = {pos, (uint32_t)l, kPurposeRace, (uint32_t)(v0 >> 2)};
   philox4x32_10(c, p.key0, p.key1);
-  const float* q = p.q + (size_t)qrow * p.V + v0;
+  // the keys use the hardware exp, log and reciprocal: the winner's margin over the
+  // runner-up is of the order of the keys themselves, far above their rounding
+  const float rse = __frcp_rn(d.se);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float pv = expf((z[e] - d.m) * p.inv_t) / d.se;
+    const float pv = __expf((z[e] - d.m) * p.inv_t) * rse;
     const float w = fmaxf(0.f, pv - q[e]);
-    const float E = -logf(u01(c[e]));
-    const float key = w > 0.f ? E / w : INFINITY;
-    const float fkey = pv > 0.f ? E / pv : INFINITY;
+    const float E = -__logf(u01(c[e]));
+    const float key = w > 0.f ? __fdividef(E, w) : INFINITY;
+    const float fkey = pv > 0.f ? __fdividef(E, pv) : INFINITY;
     if (less_key(key, v0 + e, rk.k, rk.i)) { rk.k = key; rk.i = v0 + e; }
     if (less_key(fkey, v0 + e, rk.fk, rk.fi)) { rk.fk = fkey; rk.fi = v0 + e; }
+  }
+}
+
+// Bonus race keys of lane l (every draft kept) on its last row r: the winner of
+// argmax_v z_v / T - ln E_v, E_v = -ln U(seed; position kv_len + k + 1, lane, race, v), kept
+// as the minimum of ln E_v - z_v / T (the same values negated, so the same winner).
+__device__ __forceinline__ void bonus_lane(const float (&zr)[4], int v0, const LmParams& p, int l, int r,
+                                           RaceKey& rk) {
+  float z[4];
+  penalise_row4(z, zr, v0, p, r);
+  const uint32_t pos = (uint32_t)(p.kv_len[l] + p.ri.row_col[r] + 1);
+  uint32_t c[4] = {pos, (uint32_t)l, kPurposeRace, (uint32_t)(v0 >> 2)};
+  philox4x32_10(c, p.key0, p.key1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float E = -__logf(u01(c[e]));
+    const float key = __logf(E) - z[e] * p.inv_t;
+    if (less_key(key, v0 + e, rk.k, rk.i)) { rk.k = key; rk.i = v0 + e; }
   }
 }
 
@@ -1101,40 +1133,466 @@ __global__ void k_race_f32(RaceParams p) {
   }
 }
 
-// bf16 model: the rejected row's logits as the LM head stored them (the same values its
-// statistics saw), so the draw reads R x 4 bytes per token of that row instead of
-// streaming the head's weights again.  Workgroup g covers tokens 128 g .. 128 g + 127 (the
-// LM head's group), 32 threads per lane, 8 lanes at a time.
-__global__ __launch_bounds__(256) void k_race_stored(RaceParams p) {
-  const int tid = threadIdx.x, sub = tid & 31;
-  const int v0 = blockIdx.x * 128 + 4 * sub;
-  for (int l = tid >> 5; l < p.L; l += 8) {   // uniform per 32-thread group
-    RaceKey rk = race_identity();
-    const int rr = p.dec[l].resid_row;
-    if (rr >= 0 && v0 < p.V) {
-      const f32x4 zv = *reinterpret_cast<const f32x4*>(p.zs + (size_t)rr * p.V + v0);
-      const float z[4] = {zv[0], zv[1], zv[2], zv[3]};
-      race_lane(z, v0, p, l, rk);
-    }
-#pragma unroll
-    for (int x = 1; x <= 16; x <<= 1) rk = race_xor(rk, x);
-    if (sub == 0) {
-      float* o = p.part + ((size_t)l * p.groups + blockIdx.x) * 4;
-      o[0] = rk.k; o[1] = __int_as_float(rk.i); o[2] = rk.fk; o[3] = __int_as_float(rk.fi);
-    }
-  }
-}
-
-int launch_race_stored(const RaceParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_race_stored, dim3(p.groups), dim3(256), 0, st, p);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
 int launch_race(const RaceParams& p, hipStream_t st) {
   dim3 grid(p.groups, p.L), block(256);
   hipLaunchKernelGGL(k_race_f32, grid, block, 0, st, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+
+
+// ------------------------------------------------------------------------------- sampled LM head
+// Sampled rounds of a bf16 model in one cooperative launch, so that no logit is ever
+// written to memory ("Draft heads and speculative decoding", "Guess, then check": the
+// textbook rule needs the whole row's normaliser before a residual weight is known):
+//  1. Workgroup b (one per CU, eight waves) streams the weights of its slice of
+//     ceil(V / 16 / G) or one fewer 16-token tiles, in passes of eight tiles (wave w takes
+//     local tile 8 q + w in pass q), and keeps every logit of the slice in its
+//     accumulators; it writes one statistics partial per row (max, sum exp((z - m) / T),
+//     argmax, z at the next draft, the bonus race key), penalties applied.
+//  2. Grid barrier; workgroup r reduces row r's partials in workgroup order.
+//  3. Grid barrier; every workgroup reads the row statistics and takes every lane's
+//     decision by the textbook rule (the same walk as k_lane_accept), then runs the
+//     residual race of each rejecting lane over its own slice, on the logits it still
+//     holds, and writes one (key, index) partial per lane; k_accept_coop reduces them.
+// Weights are read through a buffer resource spanning the head: a pass slot past the
+// workgroup's slice reads out of range (zeros, no memory traffic), so every load sits on
+// a straight-line path and the compiler's vmcnt waits stay exact.
+constexpr int kCoopWaves = 8;
+constexpr int kSpinLimit = 1 << 21;   // polls of one barrier (about a second) before giving up
+
+// Grid barrier of a cooperative launch (every workgroup resident).  Each thread's
+// agent-coherent stores have completed before its workgroup counts itself in; thread 0
+// polls the count with agent-coherent loads.  The wait is bounded: past the limit the
+// workgroup raises the error flag and goes on, so every wave ends.
+__device__ __forceinline__ void grid_barrier(int* cnt, int target, int* err) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int spin = 0; __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
+      if (spin >= kSpinLimit) {
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// Agent-coherent (sc1) 16-byte stores and loads of records whole 16-byte words long,
+// element i of the array at `base`: the resource is built on the array (the same for
+// every lane), the element offset goes in the lane's VGPR.
+template <typename T>
+__device__ __forceinline__ void st_coherent16(T* base, uint32_t i, const T& v) {
+  static_assert(sizeof(T) % 16 == 0, "16-byte records");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  const u32x4* s = reinterpret_cast<const u32x4*>(&v);
+#pragma unroll
+  for (int w = 0; w < (int)(sizeof(T) / 16); ++w)
+    __builtin_amdgcn_raw_buffer_store_b128(s[w], rs, i * (uint32_t)sizeof(T) + 16 * w, 0, 16);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent16(const T* base, uint32_t i) {
+  static_assert(sizeof(T) % 16 == 0, "16-byte records");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, 0x7fffffff, 0x00020000);
+  T v;
+  u32x4* d = reinterpret_cast<u32x4*>(&v);
+#pragma unroll
+  for (int w = 0; w < (int)(sizeof(T) / 16); ++w)
+    d[w] = __builtin_amdgcn_raw_buffer_load_b128(rs, i * (uint32_t)sizeof(T) + 16 * w, 0, 16);
+  return v;
+}
+
+__device__ __forceinline__ Stat stat_of(const LmPartial& o) {
+  Stat s;
+  s.m = o.m; s.se = o.se; s.arg = o.arg; s.zn = o.zn; s.gk = o.gk; s.gi = o.gi;
+  return s;
+}
+
+template <int RT, int XS, int NP, int T>
+__global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
+  constexpr int NW = kCoopWaves, KC = chunk_steps<RT>(), NC = kUnit / KC;
+  constexpr int NB = KC * RT * XS;                 // 1 KB X fragments per chunk
+  constexpr int NBW = (NB + NW - 1) / NW;          // staged per wave
+  constexpr int RING = 2 * NB * 1024;              // double-buffered X chunk
+  constexpr int NLOC = NP * NW * T;                // tile slots of a workgroup
+  constexpr int LDSB = RING > 65536 ? RING : 65536;
+  constexpr int LB = LDSB / (NLOC * 64) < kMaxLanes ? LDSB / (NLOC * 64) : kMaxLanes;   // race lanes per batch
+  static_assert(LB >= 1, "a lane's slice fits LDS");
+  static_assert(NW * kMaxRows * sizeof(Stat) <= (size_t)LDSB, "wave stats fit LDS");
+  __shared__ __attribute__((aligned(16))) char lds[LDSB];
+  __shared__ RowStat srs[kMaxRows];
+  __shared__ LaneDecision sdec[kMaxLanes];
+  __shared__ int srow[kMaxLanes];   // the row each lane draws from (rejected row, or its last row)
+  u32x4* xl = reinterpret_cast<u32x4*>(lds);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int ntiles = p.V >> 4, KS = p.H >> 5, U = p.H >> 8;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int tb0 = (int)((long long)b * ntiles / G), tb1 = (int)((long long)(b + 1) * ntiles / G);
+  const int nloc = tb1 - tb0;
+  // row tables (read while the weights stream): the drafter's q of each draft row at its
+  // own token, each row's next draft token (-1 on a lane's last row)
+  __shared__ float sqd[kMaxRows];
+  __shared__ int snext[kMaxRows];
+  __shared__ int sslot[kMaxRows];   // race batches: the batch slot of a drawn row, or -1
+  if ((int)threadIdx.x < p.R) {
+    const int r = threadIdx.x, tk = p.tokens[r];
+    const int l = p.ri.row_lane[r], j = p.ri.row_col[r];
+    sqd[r] = j > 0 && tk >= 0 && tk < p.V ? p.q[(size_t)r * p.V + tk] : 0.f;
+    snext[r] = j == p.ri.lane_cols[l] - 1 ? -1 : p.tokens[r + 1];
+  }
+
+  // ---- 1. logits of the slice, pass by pass; X chunks cycle through a double-buffered ring
+  const uint32_t wbytes = (uint32_t)((size_t)ntiles * KS * 1024);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.W), 0, (int)wbytes, 0x00020000);
+  // slot (pass q, tile j) of wave w holds local tile q NW T + j NW + w
+  uint32_t wbase[NP][T];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const int tile = tb0 + (q * T + j) * NW + wave;
+      wbase[q][j] = tile < tb1 ? (uint32_t)tile * (uint32_t)KS * 1024u + lane * 16 : wbytes;
+    }
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(p.X);
+  uint32_t xoff[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int bb = min(wave * NBW + i, NB - 1);
+    const int pl = bb / (RT * KC), t = (bb / KC) % RT, st = bb % KC;
+    xoff[i] = (uint32_t)(pl * p.xplane + ((size_t)t * KS + st) * 512 + lane * 8);
+  }
+  u32x4 sx[NBW];
+  auto stage_load = [&](int stepc) {
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+      if (NB % NW == 0 || wave * NBW + i < NB) sx[i] = *reinterpret_cast<const u32x4*>(X + xoff[i] + (size_t)stepc * 512);
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+      if (NB % NW == 0 || wave * NBW + i < NB) xl[((size_t)buf * NB + wave * NBW + i) * 64 + lane] = sx[i];
+  };
+  auto wload = [&](uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 2));   // nt
+  };
+  f32x4 acc[NP][T][RT];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[q][j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 wr[kUnit][T];
+  stage_load(0);
+#pragma unroll
+  for (int k = 0; k < kUnit; ++k)
+#pragma unroll
+    for (int j = 0; j < T; ++j) wr[k][j] = wload(wbase[0][j] + k * 1024);
+  stage_store(0);
+  __syncthreads();
+  int cb = 0;
+  const int nchunks = U * NC;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    if (q > 0 && tb0 + q * T * NW >= tb1) break;   // workgroup-uniform: the slice is done
+    for (int u = 0; u < U; ++u) {
+      // refills of this unit load unit u + 1 of the pass, or unit 0 of the next pass
+      uint32_t nb[T];
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+        nb[j] = u + 1 < U ? wbase[q][j] + (uint32_t)(u + 1) * kUnit * 1024u : (q + 1 < NP ? wbase[q + 1][j] : wbytes);
+#pragma unroll
+      for (int h = 0; h < NC; ++h) {
+        const int c = u * NC + h;
+        stage_load(c + 1 < nchunks ? (c + 1) * KC : 0);   // the next chunk (the X ring cycles over passes)
+        // keep the issue order as written: the scheduler would otherwise sink the
+        // prefetches next to their first use and expose the full memory latency
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < KC; ++st) {
+          const int k = h * KC + st;
+          u32x4 xo[XS][RT];
+#pragma unroll
+          for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+            for (int t = 0; t < RT; ++t) xo[pl][t] = xl[((size_t)cb * NB + (pl * RT + t) * KC + st) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < T; ++j)
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+              for (int pl = XS - 1; pl >= 0; --pl) acc[q][j][t] = mfma_bf16(wr[k][j], xo[pl][t], acc[q][j][t]);
+#pragma unroll
+          for (int j = 0; j < T; ++j) wr[k][j] = wload(nb[j] + k * 1024);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        stage_store(cb ^ 1);
+        __syncthreads();
+        cb ^= 1;
+      }
+    }
+  }
+
+  // ---- per-row statistics of the slice: each lane over its four tokens of every tile of
+  // the wave (token order), then across the four lanes of a row, then over the waves in
+  // wave order.  The bonus draw is not part of them: it runs after the decisions, for the
+  // lanes that keep every draft.
+  Stat* sh = reinterpret_cast<Stat*>(lds);   // the ring is free after the last chunk barrier
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = t * 16 + r16;
+    const int next_tok = r < p.R ? snext[r] : -1;
+    RowPenalty pen;
+    pen.cnt = nullptr;
+    if (p.counts && r < p.R) pen = row_penalty(p.counts, p.V, p.tokens, p.ri, r, p.presence, p.frequency);
+    float z[NP][T][4];
+    float m = -INFINITY, zn = -INFINITY;
+    int a = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const int tile = tb0 + (q * T + j) * NW + wave;
+        const int v0 = tile * 16 + 4 * kq;
+        float pz[1][4] = {};
+        if (pen.cnt && tile < tb1) {
+          const int vv[1] = {v0};
+          penalties4<1>(pen, vv, pz);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[q][j][e] = acc[q][j][t][e] - pz[0][e];
+          if (tile < tb1) {
+            if (z[q][j][e] > m) { m = z[q][j][e]; a = v0 + e; }
+            if (v0 + e == next_tok) zn = z[q][j][e];
+          }
+        }
+      }
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      const float om = __shfl_xor(m, x);
+      const int oa = __shfl_xor(a, x);
+      if (better(om, oa, m, a)) { m = om; a = oa; }
+      zn = fmaxf(zn, __shfl_xor(zn, x));
+    }
+    float se = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q)
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+          if (tb0 + (q * T + j) * NW + wave < tb1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) se += __expf((z[q][j][e] - m) * p.inv_t);
+    }
+    se += __shfl_xor(se, 16);
+    se += __shfl_xor(se, 32);
+    if (kq == 0 && r < p.R) {
+      Stat s;
+      s.m = m; s.arg = a; s.se = se; s.zn = zn == -INFINITY ? NAN : zn; s.gk = -INFINITY; s.gi = 0x7fffffff;
+      sh[wave * kMaxRows + r] = s;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < p.R) {
+    const int r = threadIdx.x;
+    Stat s = sh[r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s = stat_merge(s, sh[w * kMaxRows + r], p.inv_t);
+    LmPartial o;
+    o.m = s.m; o.se = s.se; o.arg = s.arg; o.zn = s.zn; o.gk = s.gk; o.gi = s.gi; o.pad0 = o.pad1 = 0;
+    st_coherent16(p.part, (uint32_t)(b * p.R + r), o);
+  }
+  if (b == 0 && threadIdx.x == 0) __hip_atomic_store(p.bar + 3, G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  grid_barrier(p.bar + 0, G, p.bar + 2);
+
+  // ---- 2. row r's partials in workgroup order: 256 threads, a fixed tree
+  for (int r = b; r < p.R; r += G) {   // workgroup-uniform
+    float* fm = reinterpret_cast<float*>(lds);
+    float* fse = fm + 256;
+    float* fzn = fm + 512;
+    float* fgk = fm + 768;
+    int* iarg = reinterpret_cast<int*>(fm + 1024);
+    int* igi = iarg + 256;
+    const int t = threadIdx.x;
+    if (t < 256) {
+      Stat s = stat_identity();
+      for (int g = (int)((long long)t * G / 256); g < (int)((long long)(t + 1) * G / 256); ++g)
+        s = stat_merge(s, stat_of(ld_coherent16(p.part, (uint32_t)(g * p.R + r))), p.inv_t);
+      fm[t] = s.m; fse[t] = s.se; fzn[t] = s.zn; fgk[t] = s.gk; iarg[t] = s.arg; igi[t] = s.gi;
+    }
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (t < w) {
+        Stat a, c;
+        a.m = fm[t]; a.se = fse[t]; a.zn = fzn[t]; a.gk = fgk[t]; a.arg = iarg[t]; a.gi = igi[t];
+        c.m = fm[t + w]; c.se = fse[t + w]; c.zn = fzn[t + w]; c.gk = fgk[t + w]; c.arg = iarg[t + w]; c.gi = igi[t + w];
+        a = stat_merge(a, c, p.inv_t);
+        fm[t] = a.m; fse[t] = a.se; fzn[t] = a.zn; fgk[t] = a.gk; iarg[t] = a.arg; igi[t] = a.gi;
+      }
+      __syncthreads();
+    }
+    if (t == 0) {
+      RowStat o;
+      o.m = fm[0]; o.se = fse[0]; o.zn = fzn[0]; o.gk = fgk[0]; o.arg = iarg[0]; o.gi = igi[0]; o.pad0 = o.pad1 = 0;
+      st_coherent16(p.rstat, (uint32_t)r, o);
+    }
+    __syncthreads();
+  }
+  grid_barrier(p.bar + 1, G, p.bar + 2);
+
+  // ---- 3. every lane's decision, then each lane's draw over the slice: the residual race of
+  // a lane that rejected a draft, the bonus race (Gumbel-max on z / T, as a minimum of
+  // ln E_v - z_v / T) of a lane that kept them all
+  if ((int)threadIdx.x < p.R) {
+    const int r = threadIdx.x;
+    srs[r] = ld_coherent16(p.rstat, (uint32_t)r);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < p.ri.L) {
+    const int l = threadIdx.x;
+    auto qd = [&](int r) { return sqd[r]; };
+    const LaneDecision d = decide_sampled(srs, p.tokens, p.kv_len, qd, p.inv_t, p.key0, p.key1, p.ri, l, nullptr);
+    sdec[l] = d;
+    srow[l] = d.resid_row >= 0 ? d.resid_row : p.ri.lane_start[l + 1] - 1;
+    if (b == 0) p.dec[l] = d;
+  }
+  __syncthreads();
+  const int L = p.ri.L;
+  float* zl = reinterpret_cast<float*>(lds);   // [LB][NLOC][16] logits of the drawn rows
+  constexpr int GI = (NLOC * 4 + 63) / 64;     // four-token groups per lane of a wave
+  for (int b0 = 0; b0 < L; b0 += LB) {
+    const int nb = min(LB, L - b0);
+    __syncthreads();   // the previous batch has read zl and sslot
+    if ((int)threadIdx.x < kMaxRows) sslot[threadIdx.x] = -1;
+    __syncthreads();
+    if ((int)threadIdx.x < nb) sslot[srow[b0 + threadIdx.x]] = threadIdx.x;
+    __syncthreads();
+    // each lane writes the drawn rows among its own (rows 16 t + r16)
+    int slot[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) slot[t] = sslot[t * 16 + r16];
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const int lt = (q * T + j) * NW + wave;
+        if (tb0 + lt < tb1) {
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            if (slot[t] >= 0) *reinterpret_cast<f32x4*>(zl + ((size_t)slot[t] * NLOC + lt) * 16 + 4 * kq) = acc[q][j][t];
+        }
+      }
+    __syncthreads();
+    for (int i = wave; i < nb; i += NW) {   // wave-uniform
+      const int l = b0 + i;
+      const LaneDecision d = sdec[l];
+      const bool resid = d.resid_row >= 0;
+      const int rr = srow[l];
+      RaceKey rk = race_identity();
+      // every group's logits and q first, then the keys
+      f32x4 zv[GI], qv[GI];
+#pragma unroll
+      for (int gi = 0; gi < GI; ++gi) {
+        const int g = min(gi * 64 + lane, max(nloc * 4 - 1, 0));
+        const int lt = g >> 2, v0 = (tb0 + lt) * 16 + 4 * (g & 3);
+        zv[gi] = *reinterpret_cast<const f32x4*>(zl + ((size_t)i * NLOC + lt) * 16 + 4 * (g & 3));
+        qv[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (resid && nloc > 0) qv[gi] = *reinterpret_cast<const f32x4*>(p.q + (size_t)(rr + 1) * p.V + v0);
+      }
+#pragma unroll
+      for (int gi = 0; gi < GI; ++gi) {
+        const int g = gi * 64 + lane;
+        if (g < nloc * 4) {
+          const int v0 = (tb0 + (g >> 2)) * 16 + 4 * (g & 3);
+          const float z[4] = {zv[gi][0], zv[gi][1], zv[gi][2], zv[gi][3]};
+          const float qq[4] = {qv[gi][0], qv[gi][1], qv[gi][2], qv[gi][3]};
+          if (resid) race_lane(z, qq, v0, p, l, d, rk);
+          else bonus_lane(z, v0, p, l, rr, rk);
+        }
+      }
+#pragma unroll
+      for (int x = 1; x <= 32; x <<= 1) rk = race_xor(rk, x);
+      if (lane == 0) {
+        float* o = p.racep + ((size_t)l * G + b) * 4;
+        o[0] = rk.k; o[1] = __int_as_float(rk.i); o[2] = rk.fk; o[3] = __int_as_float(rk.fi);
+      }
+    }
+  }
+}
+
+// Workgroups of the cooperative head: one per CU of the current device, at most kCUs.
+int coop_grid() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  const int g = std::min(cus, kCUs);
+  if (dev < 64) cached[dev] = g;
+  return g;
+}
+
+// Slice shape of the cooperative head: T tiles per wave and pass, NP passes of 8 T tiles,
+// rounded up to an instantiated count.  Two tiles per wave keep 16 KB of weights in flight
+// per wave; one tile per wave in up to eight passes where four passes of two would hold
+// more accumulators than the registers of two waves per SIMD.
+struct CoopShape {
+  int np, t;
+};
+
+static CoopShape coop_shape(int V, int grid, int RT) {
+  const int per = (V / 16 + grid - 1) / grid;
+  const int np2 = (per + 2 * kCoopWaves - 1) / (2 * kCoopWaves);
+  if (np2 <= 3 || (np2 == 4 && RT <= 2)) return CoopShape{std::max(np2, 1), 2};
+  const int np1 = (per + kCoopWaves - 1) / kCoopWaves;
+  if (np1 <= 8) return CoopShape{8, 1};
+  return CoopShape{0, 0};
+}
+
+int launch_lmhead_coop(const LmParams& p0, int grid, hipStream_t st) {
+  LmParams p = p0;
+  if (grid < 1) return -1;
+  const int RT = (p.R + 15) / 16;
+  const CoopShape cs = coop_shape(p.V, grid, RT);
+  if (cs.np == 0 || (size_t)p.V * p.H * 2 > 0x80000000ull) return -2;
+  p.groups = grid;
+  const void* f = nullptr;
+#define SV_C(RT_, XS_, NP_, T_) f = reinterpret_cast<const void*>(&k_lmhead_coop<RT_, XS_, NP_, T_>)
+#define SV_C_NP(RT_, XS_)                                    \
+  if (cs.t == 1) {                                           \
+    if constexpr (RT_ >= 3) SV_C(RT_, XS_, 8, 1);            \
+  } else {                                                   \
+    switch (cs.np) {                                         \
+      case 1: SV_C(RT_, XS_, 1, 2); break;                   \
+      case 2: SV_C(RT_, XS_, 2, 2); break;                   \
+      case 3: SV_C(RT_, XS_, 3, 2); break;                   \
+      default: if constexpr (RT_ <= 2) SV_C(RT_, XS_, 4, 2); break; \
+    }                                                        \
+  }
+#define SV_C_RT(XS_)                  \
+  switch (RT) {                       \
+    case 1: SV_C_NP(1, XS_); break;   \
+    case 2: SV_C_NP(2, XS_); break;   \
+    case 3: SV_C_NP(3, XS_); break;   \
+    default: SV_C_NP(4, XS_); break;  \
+  }
+  if (p.xs == 1) {
+    SV_C_RT(1);
+  } else {
+    SV_C_RT(2);
+  }
+#undef SV_C_RT
+#undef SV_C_NP
+#undef SV_C
+  if (!f) return -2;
+  void* args[] = {&p};
+  return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kCoopWaves * 64), args, 0, st) == hipSuccess ? 0 : -1;
+}
 
 }  // namespace sv

@@ -16,11 +16,16 @@ int launch_gemm_f32(const GemmF32Params& p, bool swiglu, hipStream_t st);
 int lmhead_groups(int V, bool bf16);
 int launch_lmhead(const LmParams& p, bool bf16, hipStream_t st);
 int launch_race(const RaceParams& p, hipStream_t st);
-int launch_race_stored(const RaceParams& p, hipStream_t st);
+// sampled rounds of a bf16 model: statistics, decisions and the residual race in one
+// cooperative launch of `grid` workgroups (one per CU); -2 when the vocabulary is too
+// large for the on-chip slices
+int coop_grid();
+int launch_lmhead_coop(const LmParams& p, int grid, hipStream_t st);
 
 // fragment packing
 int launch_pack_weight(const void* src, void* dst, int N, int K, hipStream_t st);
-int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, hipStream_t st);
+int launch_pack_rows(const void* src, void* dst, int R, int K, size_t plane, int xs, int* zero, int nzero,
+                     hipStream_t st);
 
 // attention
 int launch_attention(const AttnParams& p, bool bf16, hipStream_t st);
@@ -61,6 +66,9 @@ int launch_lane_accept(const RowStat* rs, const int32_t* tokens, const int32_t* 
                        int sampled, float inv_t, uint32_t key0, uint32_t key1, LaneDecision* dec,
                        int32_t* committed, int32_t* out, const RowInfo& ri, hipStream_t st);
 int launch_race_finish(const float* part, int groups, const LaneDecision* dec, int32_t* out,
+                       const RowInfo& ri, hipStream_t st);
+int launch_accept_coop(const RowStat* rs, const LaneDecision* dec, const float* part, const int* bar,
+                       const int32_t* tokens, float inv_t, int32_t* committed, int32_t* out, void* user_stats,
                        const RowInfo& ri, hipStream_t st);
 
 }  // namespace sv

@@ -75,8 +75,9 @@ int split_for(const spec_model* m, int N, int K, bool fused_pair) {
 }
 
 struct WsLayout {
-  size_t x, h, P, q, o, a, pieces, pcnt, rope, stk, stv, gst, apart, lmp, rstat, dec, racep, zs, total;
-  int n_cnt;                    // arrival counters of the gate/up cut units
+  size_t x, h, P, q, o, a, pieces, pcnt, bar, rope, stk, stv, gst, apart, lmp, rstat, dec, racep, total;
+  int n_cnt;                    // counters zeroed at the start of a round: the gate/up cut units', then the
+                                // sampled head's grid barrier (kCoopCounters)
   size_t stage_layer_elems;     // elements per attention layer in stk/stv
   size_t gst_layer_floats;      // floats per gdn layer in gst
   int n_chunks;
@@ -115,9 +116,10 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.a = take(R16 * d.ffn * 4);
   int rem = 0, pq = 0;
   if (m->bf16 && d.n_layers) sv::swiglu_pieces(d.ffn, (int)H, &rem, &pq);
-  w.n_cnt = rem;
+  w.n_cnt = rem + sv::kCoopCounters;
   w.pieces = take((size_t)rem * pq * 2 * R * 16 * 4);
-  w.pcnt = take((size_t)rem * 4);
+  w.pcnt = take((size_t)w.n_cnt * 4);
+  w.bar = w.pcnt + (size_t)rem * 4;
   w.rope = take((size_t)R * (d.head_dim / 2) * 2 * 8);
   w.stage_layer_elems = (size_t)L * sv::kStageBlocks * SPEC_KV_BLOCK * d.n_kv_heads * d.head_dim;
   w.stk = take((size_t)m->n_attn * w.stage_layer_elems * ab);
@@ -126,11 +128,13 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   w.gst = take((size_t)m->n_gdn * w.gst_layer_floats * 4);
   w.n_chunks = m->n_attn ? (max_blocks * SPEC_KV_BLOCK + m->chunk - 1) / m->chunk : 0;
   w.apart = take((size_t)L * d.n_kv_heads * w.n_chunks * 64 * (d.head_dim + sv::kAttnPartPad) * 4);
-  w.lmp = take((size_t)R * m->lm_groups * sizeof(sv::LmPartial));
+  // partials per row (LM head) and per lane (residual race): one per group of the greedy
+  // head or per workgroup of the sampled bf16 head's cooperative launch (at most kCUs)
+  const size_t groups = (size_t)std::max(m->lm_groups, m->bf16 ? sv::kCUs : 0);
+  w.lmp = take((size_t)R * groups * sizeof(sv::LmPartial));
   w.rstat = take((size_t)R * sizeof(sv::RowStat));
   w.dec = take((size_t)L * sizeof(sv::LaneDecision));
-  w.racep = take((size_t)L * m->lm_groups * 16);
-  w.zs = take(m->bf16 ? (size_t)R * d.vocab * 4 : 0);
+  w.racep = take((size_t)L * groups * 16);
   w.total = off;
   return w;
 }
@@ -179,6 +183,13 @@ int layer_window(const spec_model_desc& d, int attn_index) {
   return d.sliding_window;
 }
 
+// The sampled bf16 head keeps a workgroup's vocabulary slice on chip: at most 64 tiles of
+// 16 tokens per CU, and the head's bytes addressable by one buffer resource.
+bool coop_head_fits(const spec_model* m) {
+  const long long tiles = m->d.vocab / 16;
+  return tiles <= 64LL * sv::kCUs && (long long)m->d.vocab * m->d.hidden * 2 <= 0x80000000LL;
+}
+
 int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri, WsLayout& w) {
   if (!m) return SPEC_E_INVAL;
   int st = build_rowinfo(r, ri);
@@ -188,6 +199,7 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
   if (r->mode == SPEC_SAMPLED) {
     if (!r->q_probs || !(r->temperature > 0.f) || !std::isfinite(r->temperature)) return SPEC_E_INVAL;
   }
+  if (r->mode == SPEC_SAMPLED && m->bf16 && !coop_head_fits(m)) return SPEC_E_UNSUPPORTED;
   if (r->counts && (!std::isfinite(r->presence_penalty) || !std::isfinite(r->frequency_penalty) ||
                     (reinterpret_cast<uintptr_t>(r->counts) & 15) != 0))
     return SPEC_E_INVAL;
@@ -378,12 +390,20 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   p.key0 = (uint32_t)(r->seed & 0xffffffffu);
   p.key1 = (uint32_t)(r->seed >> 32);
   p.part = at<sv::LmPartial>(r->workspace, w.lmp);
-  p.zs = m->bf16 && r->mode == SPEC_SAMPLED ? at<float>(r->workspace, w.zs) : nullptr;
   p.ri = ri;
   p.counts = r->counts;
   p.presence = r->presence_penalty;
   p.frequency = r->frequency_penalty;
+  p.bar = at<int>(r->workspace, w.bar);
+  p.rstat = at<sv::RowStat>(r->workspace, w.rstat);
+  p.dec = at<sv::LaneDecision>(r->workspace, w.dec);
+  p.racep = at<float>(r->workspace, w.racep);
+  p.q = r->q_probs;
   ProfScope ps(m, SPEC_K_LM_HEAD, st);
+  if (m->bf16 && p.sampled) {   // statistics, decisions and residual race in one cooperative launch
+    const int rc = sv::launch_lmhead_coop(p, sv::coop_grid(), st);
+    return rc == 0 ? SPEC_OK : (rc == -2 ? SPEC_E_UNSUPPORTED : SPEC_E_HIP);
+  }
   return sv::launch_lmhead(p, m->bf16, st) ? SPEC_E_HIP : SPEC_OK;
 }
 
@@ -516,7 +536,8 @@ int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidde
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (m->bf16)
     SV_CHECK(sv::launch_pack_rows(hidden, at<void>(r->workspace, w.h), ri.R, m->d.hidden,
-                                  sv::act_plane(ri.R, m->d.hidden), m->d.n_layers == 0 ? 1 : 2, s));
+                                  sv::act_plane(ri.R, m->d.hidden), m->d.n_layers == 0 ? 1 : 2,
+                                  at<int>(r->workspace, w.pcnt), w.n_cnt, s));
   else
     SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * 4, s));
   return lm_stats(m, r, ri, w, s);
@@ -535,16 +556,20 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
   const bool sampled = r->mode == SPEC_SAMPLED;
   const float inv_t = sampled ? 1.0f / r->temperature : 1.0f;
   const uint32_t k0 = (uint32_t)(r->seed & 0xffffffffu), k1 = (uint32_t)(r->seed >> 32);
+  if (sampled && m->bf16) {   // the head's cooperative launch has taken the decisions and run the races
+    SV_CHECK(sv::launch_accept_coop(at<sv::RowStat>(ws, w.rstat), at<sv::LaneDecision>(ws, w.dec),
+                                    at<float>(ws, w.racep), at<int>(ws, w.bar), r->tokens, inv_t, committed,
+                                    out_tokens, row_stats, ri, s));
+    return SPEC_OK;
+  }
   SV_CHECK(sv::launch_row_reduce(at<sv::LmPartial>(ws, w.lmp), m->lm_groups, ri.R, inv_t, at<sv::RowStat>(ws, w.rstat),
                                  row_stats, s));
   SV_CHECK(sv::launch_lane_accept(at<sv::RowStat>(ws, w.rstat), r->tokens, r->kv_len, r->q_probs, m->d.vocab,
                                   sampled ? 1 : 0, inv_t, k0, k1, at<sv::LaneDecision>(ws, w.dec), committed,
                                   out_tokens, ri, s));
   if (sampled) {
-    sv::RaceParams p{};
-    p.xs = m->d.n_layers == 0 ? 1 : 2;
-    p.X = at<void>(ws, w.h);   // fp32: the round's hidden rows (bf16 reads the stored logits)
-    p.zs = at<float>(ws, w.zs);
+    sv::RaceParams p{};   // fp32 model: the race recomputes the rejected row's logits
+    p.X = at<void>(ws, w.h);
     p.W = m->d.lm_head;
     p.R = ri.R; p.V = m->d.vocab; p.H = m->d.hidden; p.L = ri.L;
     p.groups = m->lm_groups;
@@ -559,7 +584,7 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
     p.counts = r->counts;
     p.presence = r->presence_penalty;
     p.frequency = r->frequency_penalty;
-    SV_CHECK(m->bf16 ? sv::launch_race_stored(p, s) : sv::launch_race(p, s));
+    SV_CHECK(sv::launch_race(p, s));
     SV_CHECK(sv::launch_race_finish(at<float>(ws, w.racep), m->lm_groups, at<sv::LaneDecision>(ws, w.dec),
                                     out_tokens, ri, s));
   }
@@ -614,7 +639,7 @@ int spec_debug_gemm(const spec_model* m, const void* X, const void* W, float* Y,
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return SPEC_E_WORKSPACE;
   void* xp = workspace;
-  SV_CHECK(sv::launch_pack_rows(X, xp, R, K, sv::act_plane(R, K), 1, s));
+  SV_CHECK(sv::launch_pack_rows(X, xp, R, K, sv::act_plane(R, K), 1, nullptr, 0, s));
   if (S == 1) return project(m, SPEC_K_PROJ_IN, xp, false, W, nullptr, R, N, K, 1, Y, nullptr, s) ? SPEC_E_HIP : SPEC_OK;
   float* P = at<float>(workspace, xbytes);
   SV_CHECK(project(m, SPEC_K_PROJ_IN, xp, false, W, nullptr, R, N, K, S, P, nullptr, s));

@@ -62,7 +62,8 @@ enum spec_status {
   SPEC_E_RANGE = -2,        /* the round does not fit the lane's block table */
   SPEC_E_UNSUPPORTED = -3,  /* shape or combination this build does not run */
   SPEC_E_WORKSPACE = -4,    /* workspace missing or too small */
-  SPEC_E_HIP = -5           /* a HIP runtime call failed */
+  SPEC_E_HIP = -5,          /* a HIP runtime call failed */
+  SPEC_E_SCRATCH = -6       /* the round needs more than the library's static scratch */
 };
 
 enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -233,6 +234,21 @@ int spec_verify_round(const spec_model* model, const spec_round* round, void* st
  * round fields as spec_verify_round except the KV/state ones, which are unused. */
 int spec_verify_head(const spec_model* model, const spec_round* round, const void* hidden,
                      void* stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation: spec_verify_head followed by
+ * spec_accept in one call, with the library's own static device scratch in place of
+ * round->workspace (ignored; may be NULL).  The scratch is one 16 MiB array per GPU,
+ * held from the first such call on that GPU until the process ends; a round whose
+ * head-only buffers (hidden rows, LM-head and race partials, row statistics) exceed it
+ * returns SPEC_E_SCRATCH before anything is enqueued.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (several streams or threads at once)
+ * race: the caller serialises them.  The call allocates nothing (no hipMalloc, no
+ * hipFree).  Arguments and outputs as spec_verify_head and spec_accept; the results
+ * equal theirs. */
+int spec_verify_head_noalloc(const spec_model* model, const spec_round* round, const void* hidden,
+                             int32_t* committed, int32_t* out_tokens, spec_row_stat* row_stats,
+                             void* stream);
 
 /* Acceptance.  Greedy: per lane the longest prefix of drafts equal to the
  * argmax of the row before, then the argmax at the first mismatch (or after the

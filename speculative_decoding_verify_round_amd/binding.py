@@ -16,7 +16,8 @@ SPEC_MAX_COLS = 16
 SPEC_MAX_LANES = 64
 SPEC_KV_BLOCK = 16
 
-SPEC_OK, SPEC_E_INVAL, SPEC_E_RANGE, SPEC_E_UNSUPPORTED, SPEC_E_WORKSPACE, SPEC_E_HIP = 0, -1, -2, -3, -4, -5
+SPEC_OK, SPEC_E_INVAL, SPEC_E_RANGE, SPEC_E_UNSUPPORTED, SPEC_E_WORKSPACE, SPEC_E_HIP, SPEC_E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6)
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_LAYER_ATTN, SPEC_LAYER_GDN = 0, 1
 SPEC_GREEDY, SPEC_SAMPLED = 0, 1
@@ -29,7 +30,7 @@ HEADER_SYMBOLS = (
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
     "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
     "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass", "spec_counts_add",
-    "spec_window_live_block",
+    "spec_window_live_block", "spec_verify_head_noalloc",
 )
 SPEC_MAX_NGRAM = 8
 
@@ -99,6 +100,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
             getattr(lib, name).argtypes = [C.c_void_p, C.POINTER(SpecRound), C.c_void_p]
         lib.spec_verify_head.restype = C.c_int
         lib.spec_verify_head.argtypes = [C.c_void_p, C.POINTER(SpecRound), C.c_void_p, C.c_void_p]
+        lib.spec_verify_head_noalloc.restype = C.c_int
+        lib.spec_verify_head_noalloc.argtypes = [C.c_void_p, C.POINTER(SpecRound), C.c_void_p, C.c_void_p, C.c_void_p,
+                                                 C.c_void_p, C.c_void_p]
         lib.spec_accept.restype = C.c_int
         lib.spec_accept.argtypes = [C.c_void_p, C.POINTER(SpecRound), C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p]
@@ -175,6 +179,14 @@ def spec_verify_round(model, rnd: SpecRound, stream: int) -> None:
 def spec_verify_head(model, rnd: SpecRound, hidden_ptr: int, stream: int) -> None:
     _check(load_library().spec_verify_head(model, C.byref(rnd), C.c_void_p(hidden_ptr), C.c_void_p(stream)),
            "spec_verify_head")
+
+
+def spec_verify_head_noalloc(model, rnd: SpecRound, hidden_ptr: int, committed_ptr: int, out_tokens_ptr: int,
+                             row_stats_ptr, stream: int) -> None:
+    _check(load_library().spec_verify_head_noalloc(model, C.byref(rnd), C.c_void_p(hidden_ptr),
+                                                   C.c_void_p(committed_ptr), C.c_void_p(out_tokens_ptr),
+                                                   C.c_void_p(row_stats_ptr or 0), C.c_void_p(stream)),
+           "spec_verify_head_noalloc")
 
 
 def spec_accept(model, rnd: SpecRound, committed_ptr: int, out_tokens_ptr: int, row_stats_ptr, stream: int) -> None:

@@ -71,4 +71,9 @@ int launch_accept_coop(const RowStat* rs, const LaneDecision* dec, const float* 
                        const int32_t* tokens, float inv_t, int32_t* committed, int32_t* out, void* user_stats,
                        const RowInfo& ri, hipStream_t st);
 
+// the library's static device scratch on the current device (address and size); -1 on a
+// HIP error
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+int static_scratch(void** ptr, size_t* bytes);
+
 }  // namespace sv

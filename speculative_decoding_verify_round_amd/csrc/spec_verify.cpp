@@ -139,6 +139,26 @@ WsLayout layout(const spec_model* m, int R, int L, int max_blocks) {
   return w;
 }
 
+// The buffers of a head-only round (spec_verify_head, then spec_accept) alone: the hidden
+// rows, the counters, the LM-head and race partials, the row statistics and decisions.
+WsLayout head_layout(const spec_model* m, int R, int L) {
+  const spec_model_desc& d = m->d;
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
+  w.h = take((size_t)sv::round16(R) * d.hidden * 4);
+  w.n_cnt = sv::kCoopCounters;
+  w.pcnt = take((size_t)w.n_cnt * 4);
+  w.bar = w.pcnt;
+  const size_t groups = (size_t)std::max(m->lm_groups, m->bf16 ? sv::kCUs : 0);
+  w.lmp = take((size_t)R * groups * sizeof(sv::LmPartial));
+  w.rstat = take((size_t)R * sizeof(sv::RowStat));
+  w.dec = take((size_t)L * sizeof(sv::LaneDecision));
+  w.racep = take((size_t)L * groups * 16);
+  w.total = off;
+  return w;
+}
+
 template <typename T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off); }
 
@@ -190,7 +210,8 @@ bool coop_head_fits(const spec_model* m) {
   return tiles <= 64LL * sv::kCUs && (long long)m->d.vocab * m->d.hidden * 2 <= 0x80000000LL;
 }
 
-int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri, WsLayout& w) {
+// Validation of a round's arguments, the workspace aside; fills ri.
+int validate_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri) {
   if (!m) return SPEC_E_INVAL;
   int st = build_rowinfo(r, ri);
   if (st) return st;
@@ -223,7 +244,15 @@ int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::Ro
     }
     if (m->n_gdn && !r->gdn_state) return SPEC_E_UNSUPPORTED;
   }
-  w = layout(m, ri.R, ri.L, std::max(mb, 1));
+  (void)mb;
+  return SPEC_OK;
+}
+
+// Common validation of a round and of its workspace; fills ri and the workspace layout.
+int check_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri, WsLayout& w) {
+  int st = validate_round(m, r, head_only, ri);
+  if (st) return st;
+  w = layout(m, ri.R, ri.L, head_only ? 1 : std::max(r->max_blocks, 1));
   if (!r->workspace) return SPEC_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(r->workspace) % kAlign) != 0) return SPEC_E_WORKSPACE;
   if (r->workspace_bytes < w.total) return SPEC_E_WORKSPACE;
@@ -407,6 +436,11 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   return sv::launch_lmhead(p, m->bf16, st) ? SPEC_E_HIP : SPEC_OK;
 }
 
+int run_head(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, const void* hidden,
+             hipStream_t s);
+int run_accept(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, int32_t* committed,
+               int32_t* out_tokens, spec_row_stat* row_stats, hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -419,6 +453,7 @@ const char* spec_status_string(int status) {
     case SPEC_E_UNSUPPORTED: return "unsupported shape or configuration";
     case SPEC_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case SPEC_E_HIP: return "HIP runtime error";
+    case SPEC_E_SCRATCH: return "round needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -533,14 +568,7 @@ int spec_verify_head(const spec_model* m, const spec_round* r, const void* hidde
   if (!hidden) return SPEC_E_INVAL;
   int st = check_round(m, r, true, ri, w);
   if (st) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (m->bf16)
-    SV_CHECK(sv::launch_pack_rows(hidden, at<void>(r->workspace, w.h), ri.R, m->d.hidden,
-                                  sv::act_plane(ri.R, m->d.hidden), m->d.n_layers == 0 ? 1 : 2,
-                                  at<int>(r->workspace, w.pcnt), w.n_cnt, s));
-  else
-    SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * 4, s));
-  return lm_stats(m, r, ri, w, s);
+  return run_head(m, r, ri, w, hidden, reinterpret_cast<hipStream_t>(stream));
 }
 
 int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, int32_t* out_tokens,
@@ -551,7 +579,49 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
   const bool head_only = !m || m->d.n_layers == 0;
   int st = check_round(m, r, head_only, ri, w);
   if (st) return st;
+  return run_accept(m, r, ri, w, committed, out_tokens, row_stats, reinterpret_cast<hipStream_t>(stream));
+}
+
+int spec_verify_head_noalloc(const spec_model* m, const spec_round* r, const void* hidden, int32_t* committed,
+                             int32_t* out_tokens, spec_row_stat* row_stats, void* stream) {
+  sv::RowInfo ri;
+  if (!hidden || !committed || !out_tokens) return SPEC_E_INVAL;
+  int st = validate_round(m, r, true, ri);
+  if (st) return st;
+  const WsLayout w = head_layout(m, ri.R, ri.L);
+  if (w.total > sv::kStaticScratchBytes) return SPEC_E_SCRATCH;
+  void* scr = nullptr;
+  size_t scr_bytes = 0;
+  if (sv::static_scratch(&scr, &scr_bytes) || scr_bytes < w.total) return SPEC_E_HIP;
+  spec_round rs = *r;   // the same round on the library's scratch
+  rs.workspace = scr;
+  rs.workspace_bytes = scr_bytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = run_head(m, &rs, ri, w, hidden, s);
+  if (st) return st;
+  return run_accept(m, &rs, ri, w, committed, out_tokens, row_stats, s);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The LM head and row statistics on caller-given hidden states (spec_verify_head), on the
+// workspace of r laid out by w.
+int run_head(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, const void* hidden,
+             hipStream_t s) {
+  if (m->bf16)
+    SV_CHECK(sv::launch_pack_rows(hidden, at<void>(r->workspace, w.h), ri.R, m->d.hidden,
+                                  sv::act_plane(ri.R, m->d.hidden), m->d.n_layers == 0 ? 1 : 2,
+                                  at<int>(r->workspace, w.pcnt), w.n_cnt, s));
+  else
+    SV_CHECK(sv::launch_copy_rows(hidden, at<void>(r->workspace, w.h), (size_t)ri.R * m->d.hidden * 4, s));
+  return lm_stats(m, r, ri, w, s);
+}
+
+// Acceptance (spec_accept) on the workspace of r laid out by w.
+int run_accept(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, const WsLayout& w, int32_t* committed,
+               int32_t* out_tokens, spec_row_stat* row_stats, hipStream_t s) {
   void* ws = r->workspace;
   const bool sampled = r->mode == SPEC_SAMPLED;
   const float inv_t = sampled ? 1.0f / r->temperature : 1.0f;
@@ -590,6 +660,10 @@ int spec_accept(const spec_model* m, const spec_round* r, int32_t* committed, in
   }
   return SPEC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int spec_commit(const spec_model* m, const spec_round* r, const int32_t* committed, void* stream) {
   sv::RowInfo ri;

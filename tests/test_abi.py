@@ -29,8 +29,8 @@ def test_library_exports_every_header_function():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5):
-        assert B.spec_status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert B.spec_status_string(s) != "unknown status"
     assert B.spec_status_string(-99) == "unknown status"
 
 
@@ -251,3 +251,23 @@ def test_window_fields_and_live_block():
     for kv, W in ((0, 16), (100, 200), (300, 100), (700, 100), (8192, 1024), (64, 1), (63, 1)):
         lo = max(0, kv - W + 1)
         assert lib.spec_window_live_block(kv, W) == (lo // 64) * 4, (kv, W)
+
+
+def test_noalloc_head_validates_before_any_device_call():
+    """The no-allocation head round refuses bad arguments, and a round larger than the static
+    scratch, before it looks up the scratch or enqueues anything."""
+    lib = B.load_library()
+    h = C.c_void_p()
+    desc = make_desc(n_layers=0, kinds=[], vocab=1 << 20)      # greedy LM-head partials of 16.8 MB
+    assert lib.spec_model_create(C.byref(desc), C.byref(h)) == 0
+    try:
+        r = make_round(h, lanes=8, cols=[8] * 8, workspace=None, workspace_bytes=0)
+        assert lib.spec_verify_head_noalloc(h, C.byref(r), FAKE, FAKE, FAKE, None, None) == B.SPEC_E_SCRATCH
+        assert lib.spec_verify_head_noalloc(h, C.byref(r), None, FAKE, FAKE, None, None) == B.SPEC_E_INVAL
+        assert lib.spec_verify_head_noalloc(h, C.byref(r), FAKE, None, FAKE, None, None) == B.SPEC_E_INVAL
+        r = make_round(h, lanes=0, cols=[])
+        assert lib.spec_verify_head_noalloc(h, C.byref(r), FAKE, FAKE, FAKE, None, None) == B.SPEC_E_INVAL
+        r = make_round(h, mode=B.SPEC_SAMPLED)                   # sampled without q
+        assert lib.spec_verify_head_noalloc(h, C.byref(r), FAKE, FAKE, FAKE, None, None) == B.SPEC_E_INVAL
+    finally:
+        B.spec_model_destroy(h)

@@ -326,88 +326,129 @@ int launch_qkv_post(const float* P, int S, const double* rope, int use_rope, int
 }
 
 // ------------------------------------------------------------------------------- gated delta rule
-// State S is [dv][dk] fp32 per (lane, head); thread t owns row i = t / 2, columns
-// [64 (t % 2), 64 (t % 2) + 64).  One column step (Yang et al., Gated DeltaNet):
-//   S <- float32(alpha S + beta (v - alpha S k) k^T), evaluated in float64,
-// so the state is stored in float32 after every column.  Verify and commit run
-// this exact function on the exact staged inputs, so the committed state is
-// bitwise the state verify saw at the last committed column.
+// State S is [dv][dk] float32 per (lane, head).  One column step (Yang et al., Gated
+// DeltaNet), evaluated in float64 and stored in float32 after every column:
+//   S <- alpha S + beta (v - alpha S k) k^T,   o = S q.
+// Row i of the new state depends only on row i of the old one and on the column's
+// shared k, v_i, alpha, beta, so rows split freely: kGdnRowBlocks workgroups per (lane,
+// head) of kGdnRows rows each, eight threads per row holding sixteen entries of it.  Verify
+// and commit run the same step function on the same float32 inputs (the verify stages
+// them), so the committed state is bitwise the state verify saw at the last committed
+// column.
 constexpr int kGdnDim = 128;
+constexpr int kGdnRowBlocks = 4;
+constexpr int kGdnRows = kGdnDim / kGdnRowBlocks;   // 32 rows: 256 threads, 8 per row
+constexpr int kGdnSeg = kGdnDim / 8;                // 16 entries per thread
 
-__device__ __forceinline__ double gdn_rowdot(const float (&s)[64], const double* vec, int half) {
+// S[i,:] . vec over the eight threads of row i (entries 16 seg .. 16 seg + 15 each),
+// summed in a fixed tree; every thread of the row gets the same bits (a + b == b + a).
+__device__ __forceinline__ double gdn_dot(const float (&s)[kGdnSeg], const float* vec, int seg) {
   double part = 0.0;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) part += (double)s[c] * vec[64 * half + c];
-  const double other = __shfl_xor(part, 1);
-  return half == 0 ? part + other : other + part;   // (low half) + (high half) on both threads
+  for (int e = 0; e < kGdnSeg; ++e) part += (double)s[e] * (double)vec[kGdnSeg * seg + e];
+  part += __shfl_xor(part, 1);
+  part += __shfl_xor(part, 2);
+  part += __shfl_xor(part, 4);
+  return part;
 }
 
-__device__ __forceinline__ void gdn_update(float (&s)[64], const double* kn, int half, double v_i, double alpha,
-                                           double beta) {
-  const double sk = gdn_rowdot(s, kn, half);
-  const double coef = beta * (v_i - alpha * sk);
+__device__ __forceinline__ void gdn_step(float (&s)[kGdnSeg], const float* k, int seg, double v_i, double alpha,
+                                         double beta) {
+  const double coef = beta * (v_i - alpha * gdn_dot(s, k, seg));
 #pragma unroll
-  for (int c = 0; c < 64; ++c) s[c] = (float)(alpha * (double)s[c] + coef * kn[64 * half + c]);
+  for (int e = 0; e < kGdnSeg; ++e) s[e] = (float)(alpha * (double)s[e] + coef * (double)k[kGdnSeg * seg + e]);
 }
 
 // stage layout per (row, head): kn[128], v[128], alpha, beta  (kGdnStage floats)
 constexpr int kGdnStage = 2 * kGdnDim + 2;
 
+// The row's state slice: row i, entries 16 seg .. 16 seg + 15.
+__device__ __forceinline__ const float* gdn_slice(const float* state, int l, int n_gdn, int gi, int hg, int h, int row,
+                                                  int seg) {
+  return state + ((((size_t)l * n_gdn + gi) * hg + h) * kGdnDim + row) * kGdnDim + kGdnSeg * seg;
+}
+
+// Verify of one layer: workgroup (row block, head, lane).  First every column's inputs --
+// the projection's split partials summed in split order in float64 and rounded once;
+// q and k L2-normalised (q scaled by d^-1/2), alpha = sigmoid, beta = sigmoid -- into
+// LDS, with the norms reduced over 32 lanes in a fixed tree; then the columns one after
+// another with no further barrier.  The state is read, never written.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowInfo ri, int hg, const float* state,
                                                      int n_gdn, int gi, float* stage, T* o) {
-  __shared__ double qn[kGdnDim], kn[kGdnDim], vv[kGdnDim], red[32], ab[2];
-  const int h = blockIdx.x, l = blockIdx.y;
-  const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
-  const int R = ri.R;
-  const int N = 3 * hg * kGdnDim + 2 * hg;
-  const float* S0 = state + (((size_t)l * n_gdn + gi) * hg + h) * kGdnDim * kGdnDim + (size_t)row_i * kGdnDim + 64 * half;
-  float s[64];
-#pragma unroll
-  for (int c = 0; c < 64; c += 4) {
-    const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + c);
-    s[c] = v4[0]; s[c + 1] = v4[1]; s[c + 2] = v4[2]; s[c + 3] = v4[3];
-  }
+  __shared__ float sq[kMaxCols][kGdnDim], sk[kMaxCols][kGdnDim], sv[kMaxCols][kGdnRows], sab[kMaxCols][2];
+  const int rb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int t = threadIdx.x, row = rb * kGdnRows + (t >> 3), seg = t & 7;
+  const int R = ri.R, N = 3 * hg * kGdnDim + 2 * hg;
   const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
+  const size_t split = (size_t)R * N;
+  float s[kGdnSeg];
+  {
+    const float* S0 = gdn_slice(state, l, n_gdn, gi, hg, h, row, seg);
+#pragma unroll
+    for (int e = 0; e < kGdnSeg; e += 4) {
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + e);
+      s[e] = v4[0]; s[e + 1] = v4[1]; s[e + 2] = v4[2]; s[e + 3] = v4[3];
+    }
+  }
+  // q and k: 64 four-element items per column, 32 consecutive threads per vector
+  for (int it = t; it < cols * 64; it += 256) {   // uniform over each 32-thread group
+    const int j = it >> 6, vec = (it >> 5) & 1, quad = it & 31;
+    const int n = vec * hg * kGdnDim + h * kGdnDim + 4 * quad;
+    double a[4];
+    sum_splits4(P + (size_t)(rs + j) * N + n, split, S, a);
+    float f[4];
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = (float)a[e];
+      ss += (double)f[e] * (double)f[e];
+    }
+#pragma unroll
+    for (int x = 1; x <= 16; x <<= 1) ss += __shfl_xor(ss, x);
+    const double inv = 1.0 / sqrt(ss + 1e-6);
+    float* dst = vec ? &sk[j][4 * quad] : &sq[j][4 * quad];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dst[e] = vec ? (float)((double)f[e] * inv) : (float)((double)f[e] * inv / sqrt((double)kGdnDim));
+  }
+  // v of the block's rows, then alpha and beta
+  for (int it = t; it < cols * (kGdnRows / 4); it += 256) {
+    const int j = it / (kGdnRows / 4), quad = it % (kGdnRows / 4);
+    double a[4];
+    sum_splits4(P + (size_t)(rs + j) * N + 2 * hg * kGdnDim + h * kGdnDim + rb * kGdnRows + 4 * quad, split, S, a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[j][4 * quad + e] = (float)a[e];
+  }
+  if (t < 2 * cols) {
+    const int j = t >> 1, w = t & 1;
+    const float* src = P + (size_t)(rs + j) * N + 3 * hg * kGdnDim + w * hg + h;
+    double a = src[0];
+    for (int ss = 1; ss < S; ++ss) a += src[(size_t)ss * split];
+    sab[j][w] = (float)(1.0 / (1.0 + exp(-(double)(float)a)));
+  }
+  __syncthreads();
+  // stage the column inputs for the commit's replay: k, alpha, beta once (row block 0),
+  // v of each block's own rows
+  for (int it = t; it < cols * kGdnDim; it += 256) {
+    const int j = it / kGdnDim, e = it % kGdnDim;
+    float* stg = stage + ((size_t)(rs + j) * hg + h) * kGdnStage;
+    if (rb == 0) stg[e] = sk[j][e];
+    if (e < kGdnRows) stg[kGdnDim + rb * kGdnRows + e] = sv[j][e];
+    if (rb == 0 && e < 2) stg[2 * kGdnDim + e] = sab[j][e];
+  }
+  const size_t oplane = act_plane(R, hg * kGdnDim);
   for (int j = 0; j < cols; ++j) {
-    const int r = rs + j;
-    auto proj = [&](int n) {   // the projection, rounded once to float32
-      double a = P[(size_t)r * N + n];
-      for (int ss = 1; ss < S; ++ss) a += P[((size_t)ss * R + r) * N + n];
-      return (double)(float)a;
-    };
-    double qv = 0.0, kv = 0.0;
-    if (t < kGdnDim) {
-      qv = proj(h * kGdnDim + t);
-      kv = proj(hg * kGdnDim + h * kGdnDim + t);
-      vv[t] = proj(2 * hg * kGdnDim + h * kGdnDim + t);
-    }
-    if (t == 0) {
-      ab[0] = (double)(float)(1.0 / (1.0 + exp(-proj(3 * hg * kGdnDim + h))));
-      ab[1] = (double)(float)(1.0 / (1.0 + exp(-proj(3 * hg * kGdnDim + hg + h))));
-    }
-    const double qq = block_sum_f64(qv * qv, red);
-    const double kk = block_sum_f64(kv * kv, red);
-    if (t < kGdnDim) {
-      qn[t] = (double)(float)(qv / sqrt(qq + 1e-6) / sqrt((double)kGdnDim));
-      kn[t] = (double)(float)(kv / sqrt(kk + 1e-6));
-    }
-    __syncthreads();
-    const double alpha = ab[0], beta = ab[1];
-    float* stg = stage + ((size_t)r * hg + h) * kGdnStage;
-    if (t < kGdnDim) { stg[t] = (float)kn[t]; stg[kGdnDim + t] = (float)vv[t]; }
-    if (t == 0) { stg[2 * kGdnDim] = (float)alpha; stg[2 * kGdnDim + 1] = (float)beta; }
-    gdn_update(s, kn, half, vv[row_i], alpha, beta);
-    const double oi = gdn_rowdot(s, qn, half);
-    if (half == 0) st_out(o, act_plane(R, hg * kGdnDim), act_index(o, r, h * kGdnDim + row_i, hg * kGdnDim), (float)oi);
-    __syncthreads();
+    gdn_step(s, sk[j], seg, (double)sv[j][t >> 3], (double)sab[j][0], (double)sab[j][1]);
+    const double oi = gdn_dot(s, sq[j], seg);
+    if (seg == 0) st_out(o, oplane, act_index(o, rs + j, h * kGdnDim + row, hg * kGdnDim), (float)oi);
   }
 }
 
 int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state, int n_gdn, int gi,
                       float* stage, void* o, const RowInfo& ri, bool bf16, hipStream_t st) {
   (void)dg;
-  dim3 grid(hg, ri.L), block(256);
+  dim3 grid(kGdnRowBlocks, hg, ri.L), block(256);
   if (bf16)
     hipLaunchKernelGGL(k_gdn_verify<bf16_t>, grid, block, 0, st, P, S, ri, hg, state, n_gdn, gi, stage,
                        reinterpret_cast<bf16_t*>(o));
@@ -417,38 +458,46 @@ int launch_gdn_verify(const float* P, int S, int hg, int dg, const float* state,
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// commit: replay columns 0 .. c-1 of every gated-delta-rule layer from the staged inputs
+// Commit: replay columns 0 .. c-1 of every gated-delta-rule layer from the staged inputs,
+// workgroup (row block, head) x lane x layer, the same step function as the verify.
 __global__ __launch_bounds__(256) void k_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg,
                                                      const float* stage, size_t stage_layer_stride, RowInfo ri) {
-  __shared__ double kn[kGdnDim], vv[kGdnDim], ab[2];
-  const int h = blockIdx.x, l = blockIdx.y, gi = blockIdx.z;
-  const int t = threadIdx.x, row_i = t >> 1, half = t & 1;
+  __shared__ float sk[kMaxCols][kGdnDim], sv[kMaxCols][kGdnRows], sab[kMaxCols][2];
+  const int rb = blockIdx.x % kGdnRowBlocks, h = blockIdx.x / kGdnRowBlocks, l = blockIdx.y, gi = blockIdx.z;
+  const int t = threadIdx.x, row = rb * kGdnRows + (t >> 3), seg = t & 7;
   const int cols = ri.lane_cols[l], rs = ri.lane_start[l];
   const int c = max(1, min(committed[l], cols));
-  float* S0 = state + (((size_t)l * n_gdn + gi) * hg + h) * kGdnDim * kGdnDim + (size_t)row_i * kGdnDim + 64 * half;
-  float s[64];
+  float* S0 = const_cast<float*>(gdn_slice(state, l, n_gdn, gi, hg, h, row, seg));
+  float s[kGdnSeg];
 #pragma unroll
-  for (int q = 0; q < 64; q += 4) {
-    const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + q);
-    s[q] = v4[0]; s[q + 1] = v4[1]; s[q + 2] = v4[2]; s[q + 3] = v4[3];
+  for (int e = 0; e < kGdnSeg; e += 4) {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(S0 + e);
+    s[e] = v4[0]; s[e + 1] = v4[1]; s[e + 2] = v4[2]; s[e + 3] = v4[3];
   }
   const float* stl = stage + gi * stage_layer_stride;
-  for (int j = 0; j < c; ++j) {
+  for (int it = t; it < c * (kGdnDim / 4); it += 256) {
+    const int j = it / (kGdnDim / 4), quad = it % (kGdnDim / 4);
     const float* stg = stl + ((size_t)(rs + j) * hg + h) * kGdnStage;
-    if (t < kGdnDim) { kn[t] = (double)stg[t]; vv[t] = (double)stg[kGdnDim + t]; }
-    if (t < 2) ab[t] = (double)stg[2 * kGdnDim + t];
-    __syncthreads();
-    gdn_update(s, kn, half, vv[row_i], ab[0], ab[1]);
-    __syncthreads();
-  }
+    const f32x4 k4 = *reinterpret_cast<const f32x4*>(stg + 4 * quad);
 #pragma unroll
-  for (int q = 0; q < 64; q += 4) *reinterpret_cast<f32x4*>(S0 + q) = f32x4{s[q], s[q + 1], s[q + 2], s[q + 3]};
+    for (int e = 0; e < 4; ++e) sk[j][4 * quad + e] = k4[e];
+    if (quad < kGdnRows / 4) {
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + kGdnDim + rb * kGdnRows + 4 * quad);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[j][4 * quad + e] = v4[e];
+    }
+    if (quad < 2) sab[j][quad] = stg[2 * kGdnDim + quad];
+  }
+  __syncthreads();
+  for (int j = 0; j < c; ++j) gdn_step(s, sk[j], seg, (double)sv[j][t >> 3], (double)sab[j][0], (double)sab[j][1]);
+#pragma unroll
+  for (int e = 0; e < kGdnSeg; e += 4) *reinterpret_cast<f32x4*>(S0 + e) = f32x4{s[e], s[e + 1], s[e + 2], s[e + 3]};
 }
 
 int launch_gdn_replay(const int32_t* committed, float* state, int n_gdn, int hg, int dg, const float* stage,
                       size_t stage_layer_stride, const RowInfo& ri, hipStream_t st) {
   (void)dg;
-  dim3 grid(hg, ri.L, n_gdn), block(256);
+  dim3 grid(kGdnRowBlocks * hg, ri.L, n_gdn), block(256);
   hipLaunchKernelGGL(k_gdn_replay, grid, block, 0, st, committed, state, n_gdn, hg, stage, stage_layer_stride, ri);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

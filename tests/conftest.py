@@ -16,6 +16,36 @@ def pytest_configure(config):
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
+class MismatchBudget:
+    """Near-tie token mismatches excused across the session's GPU parity tests.
+
+    A committed token may differ from the oracle's only at a row whose oracle top-2 logit
+    gap is below 5e-2; such excused mismatches are counted against every compared row and
+    must stay under 0.1 % of them.  Tests add (name, rows, excused) as they run; the check
+    runs once, when the session ends, whatever the order the tests ran in."""
+
+    LIMIT = 1e-3
+
+    def __init__(self):
+        self.entries = []
+
+    def add(self, name, rows, excused):
+        self.entries.append((name, int(rows), int(excused)))
+
+    def totals(self):
+        return sum(r for _, r, _ in self.entries), sum(m for _, _, m in self.entries)
+
+
+@pytest.fixture(scope="session")
+def mismatch_budget():
+    budget = MismatchBudget()
+    yield budget
+    rows, excused = budget.totals()
+    print(f"\nmismatch budget: {excused} excused of {rows} compared rows: {budget.entries}")
+    if rows:
+        assert excused / rows < MismatchBudget.LIMIT, (excused, rows, budget.entries)
+
+
 def read_golden(name):
     """Rows of a whitespace-separated fixture; lines starting with '#' are citations/comments."""
     rows = []

@@ -21,9 +21,6 @@ from test_gpu_parity import _round_parity, check_committed_cache
 
 pytestmark = pytest.mark.gpu
 
-MISMATCH_LOG = []     # (config, rows, excused mismatches) for the report
-
-
 def _greedy_tokens(pair, anchors, steps):
     """The oracle's own plain greedy continuation (on a copy of its cache)."""
     return pair.om.plain_greedy(pair.oc.copy(), anchors, steps)
@@ -36,14 +33,14 @@ def _planted(pair, anchors, k, alpha, tag):
             for l, a in enumerate(anchors)]
 
 
-def _account(name, rows, mism):
+def _account(budget, name, rows, mism):
     for m in mism:
         assert m[-1] < GAP_EXCUSE, f"{name}: token mismatch at a row without a near-tie: {m}"
-    MISMATCH_LOG.append((name, rows, len(mism)))
+    budget.add(name, rows, len(mism))
     log(f"{name}: {rows} rows, {len(mism)} excused mismatches")
 
 
-def test_mid_bf16_greedy_sampled_and_budget_sweep():
+def test_mid_bf16_greedy_sampled_and_budget_sweep(mismatch_budget):
     cfg = synth.get_config("mid-bf16")
     log("mid-bf16: setup")
     pair = Pair(cfg, lanes=8, context=cfg.context, max_blocks=(cfg.context + 64) // 16 + 1)
@@ -52,13 +49,13 @@ def test_mid_bf16_greedy_sampled_and_budget_sweep():
     toks = _planted(pair, anchors, cfg.k, 0.7, 100)
     ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
     log(f"mid-bf16 greedy 8x5: logit err {lerr:.2e}, committed {list(c)}")
-    _account("mid-bf16 greedy", rc.R, mism)
+    _account(mismatch_budget, "mid-bf16 greedy", rc.R, mism)
     # sampled at T = 1.0
     q, d = synth.drafter_rows(cfg.input_seed, 7, rc.R, cfg.vocab)
     toks_s = [[anchors[l]] + [int(x) for x in d[l * 5 + 1:(l + 1) * 5]] for l in range(8)]
     ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks_s, "sampled", 1.0, q, seed=cfg.philox_seed)
     log(f"mid-bf16 sampled: logit err {lerr:.2e}, committed {list(c)}")
-    _account("mid-bf16 sampled", rc.R, mism)
+    _account(mismatch_budget, "mid-bf16 sampled", rc.R, mism)
     # row budget 8 across 1..8 lanes: drafts per lane from the planner, rows never above 8
     for L in range(1, 9):
         k_l = plan_drafts(cfg.k, 8, L)
@@ -73,11 +70,13 @@ def test_mid_bf16_greedy_sampled_and_budget_sweep():
         assert err <= 3e-2
         dc.verify(rcb); dc.accept(rcb)
         cb, emb, _ = dc.results(rcb)
+        mism_b = []
         for l in range(L):
             rows = ores.lane_rows[l]
             oc_, oem = accept_greedy(ores.logits[rows.start:rows.stop], toks_b[l][1:])
             if (oc_, oem) != (int(cb[l]), emb[l]):
-                assert min(top2_gap(ores.logits[r]) for r in rows) < GAP_EXCUSE
+                mism_b.append((l, min(top2_gap(ores.logits[r]) for r in rows)))
+        _account(mismatch_budget, f"mid-bf16 budget 8 at {L} lanes", rcb.R, mism_b)
         log(f"budget 8, {L} lanes: {k_l} drafts, {rcb.R} rows, logit err {err:.2e}")
     pair.close()
 
@@ -106,7 +105,7 @@ def _big(name, n_layers, lanes, context):
     return cfg, Pair(cfg, lanes=lanes, context=context, max_blocks=(context + 32) // 16 + 1)
 
 
-def test_dense_27b_full_width_two_layers():
+def test_dense_27b_full_width_two_layers(mismatch_budget):
     cfg, pair = _big("dense-27b", 2, 8, 8192)
     anchors = [int(t) for t in synth.uniform_tokens(cfg.input_seed, 5, 8, cfg.vocab)]
     log("dense-27b: planting drafts")
@@ -114,7 +113,7 @@ def test_dense_27b_full_width_two_layers():
     log("dense-27b: 8 lanes x 8 rows")
     ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
     log(f"dense-27b 8 lanes: logit err {lerr:.2e}, committed {list(c)}")
-    _account("dense-27b L8", rc.R, mism)
+    _account(mismatch_budget, "dense-27b 2 layers L8", rc.R, mism)
     pair.om.commit(pair.oc, ores, list(c))
     pair.dc.commit(rc)
     torch.cuda.synchronize()
@@ -129,34 +128,25 @@ def test_dense_27b_full_width_two_layers():
     pair.close()
 
 
-def test_hybrid_full_width_four_layers():
+def test_hybrid_full_width_four_layers(mismatch_budget):
     cfg, pair = _big("hybrid-gdn", 4, 4, 4096)
     anchors = [int(t) for t in synth.uniform_tokens(cfg.input_seed, 5, 4, cfg.vocab)]
     toks = _planted(pair, anchors, cfg.k, 0.7, 300)
     ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
     log(f"hybrid greedy: logit err {lerr:.2e}, committed {list(c)}")
-    _account("hybrid greedy", rc.R, mism)
+    _account(mismatch_budget, "hybrid 4 layers greedy", rc.R, mism)
     q, d = synth.drafter_rows(cfg.input_seed, 8, rc.R, cfg.vocab)
     toks_s = [[anchors[l]] + [int(x) for x in d[l * 4 + 1:(l + 1) * 4]] for l in range(4)]
     ores_s, rc_s, c_s, em_s, st_s, lerr_s, mism_s = _round_parity(pair, toks_s, "sampled", 1.0, q,
                                                                   seed=cfg.philox_seed)
     log(f"hybrid sampled: logit err {lerr_s:.2e}, committed {list(c_s)}")
-    _account("hybrid sampled", rc_s.R, mism_s)
+    _account(mismatch_budget, "hybrid 4 layers sampled", rc_s.R, mism_s)
     pair.om.commit(pair.oc, ores_s, list(c_s))
     pair.dc.commit(rc_s)
     torch.cuda.synchronize()
-    for gi in range(cfg.n_gdn):
+    for gi in range(cfg.n_gdn):   # the bar of the full-depth hybrid (test_gpu_full_depth.STATE_BAR)
         g = pair.dc.gdn[:, gi].cpu().numpy()
         o = pair.oc.gdn[gi]
-        assert np.max(np.abs(g - o)) <= 1e-2 * np.max(np.abs(o))
+        assert np.max(np.abs(g - o)) <= 2e-4 * np.max(np.abs(o))
     check_committed_cache(pair, 4096)
     pair.close()
-
-
-def test_zz_mismatch_budget():
-    """Excused (near-tie) token mismatches over the configs above stay under 0.1% of rows."""
-    rows = sum(r for _, r, _ in MISMATCH_LOG)
-    m = sum(k for _, _, k in MISMATCH_LOG)
-    log(f"mismatch budget: {m} excused of {rows} rows: {MISMATCH_LOG}")
-    assert rows > 0
-    assert m / rows < 1e-3

@@ -51,7 +51,7 @@ from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceMod
 HBM_PEAK_GBS = 8000.0
 # measured HBM traffic of the gate/up kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
 # calibrated against a plain copy); reported only while that kernel's sources are unchanged
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic_dense27b.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_dense27b.md")
 GATEUP_SOURCES = ("gemm.hip", "common.hpp")
 COPY_CALIBRATION_BYTES = 512 << 20
 EVICT_BYTES = 512 << 20

@@ -309,7 +309,8 @@ def _base_result(cfg, args, L, k, R, ctx, mode, committed_total, elapsed, steps,
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": workload_name(cfg, L, k, R, ctx, mode) + extra_workload,
-                   "lanes": L, "k": k, "rows": R, "context": ctx, "mode": mode},
+                   "lanes": L, "k": k, "rows": R, "context": ctx, "mode": mode,
+                   **({"attn_chunk": args.chunk_used} if getattr(args, "chunk_used", 0) else {})},
         "verify_rows_per_s": round(R * steps / elapsed, 1),
     }
 
@@ -395,11 +396,15 @@ def run_decoder(args, cfg):
     max_blocks = (ctx + ref_len + 32) // 16 + 1
     log(f"{cfg.name}: weights on the device")
     w = gpu_weights(cfg, cfg.weight_seed)
-    # split-KV chunks of 1024 positions at 8K context (512 with a window, where a window of
-    # W positions spans only about W / chunk + 1 chunks and smaller chunks keep more
-    # workgroups busy); the chunk grid is a per-model setting and results depend on it
-    # only through the fixed order of the merge
-    chunk = args.attn_chunk or (512 if args.window or ctx < 4096 else 1024)
+    # split-KV chunks: 1024 positions when the (lane, kv head, chunk) triples at that size
+    # give at least half as many workgroups as the card has CUs, else 512 (also with a
+    # window, where a window of W positions spans only about W / chunk + 1 chunks).  At
+    # context 8192 that is 1024 for 8 lanes and 512 for one lane (measured: 15.4 against
+    # 15.9 ms a round at 8 lanes, 10.2 against 10.7 ms at one lane).  The chunk grid is a
+    # per-model setting and results depend on it only through the fixed order of the merge.
+    wide = L * cfg.n_kv_heads * ((ctx + 1023) // 1024) >= 128
+    chunk = args.attn_chunk or (1024 if wide and not args.window and ctx >= 4096 else 512)
+    args.chunk_used = chunk
     dm = DeviceModel(cfg, w, prepacked=True, attn_chunk=chunk)
     del w
     bt, nb = synth.block_table(cfg, L, max_blocks)

@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from speculative_decoding_verify_round_amd import binding as B  # noqa: E402
-from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel, pack_weight  # noqa: E402
+from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel, attn_chunk_for, pack_weight  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 # measured HBM traffic of the gate/up kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
@@ -396,14 +396,9 @@ def run_decoder(args, cfg):
     max_blocks = (ctx + ref_len + 32) // 16 + 1
     log(f"{cfg.name}: weights on the device")
     w = gpu_weights(cfg, cfg.weight_seed)
-    # split-KV chunks: 1024 positions when the (lane, kv head, chunk) triples at that size
-    # give at least half as many workgroups as the card has CUs, else 512 (also with a
-    # window, where a window of W positions spans only about W / chunk + 1 chunks).  At
-    # context 8192 that is 1024 for 8 lanes and 512 for one lane (measured: 15.4 against
-    # 15.9 ms a round at 8 lanes, 10.2 against 10.7 ms at one lane).  The chunk grid is a
-    # per-model setting and results depend on it only through the fixed order of the merge.
-    wide = L * cfg.n_kv_heads * ((ctx + 1023) // 1024) >= 128
-    chunk = args.attn_chunk or (1024 if wide and not args.window and ctx >= 4096 else 512)
+    # split-KV chunk by workgroup count (at context 8192: 1024 for 8 lanes, 512 for one lane;
+    # measured 15.4 against 15.9 ms a round at 8 lanes, 10.2 against 10.7 ms at one lane)
+    chunk = args.attn_chunk or attn_chunk_for(cfg.n_kv_heads, L, ctx, args.window)
     args.chunk_used = chunk
     dm = DeviceModel(cfg, w, prepacked=True, attn_chunk=chunk)
     del w

@@ -36,6 +36,17 @@ def pack_weight(w: torch.Tensor, stream: Optional[int] = None) -> torch.Tensor:
     return out
 
 
+def attn_chunk_for(n_kv_heads: int, lanes: int, context: int, window: int = 0) -> int:
+    """Split-KV chunk (positions) for a model that serves `lanes` lanes at about `context`
+    positions: 1024 when the (lane, kv head, chunk) triples at that size give at least half
+    as many workgroups as the card has CUs (128), else 512; 512 with a sliding window (a
+    window of W positions spans only about W / chunk + 1 chunks) or below 4096 positions.
+    The chunk grid is fixed per model, and results depend on it only through the fixed
+    order of the merge."""
+    wide = lanes * n_kv_heads * ((context + 1023) // 1024) >= 128
+    return 1024 if wide and not window and context >= 4096 else 512
+
+
 class DeviceModel:
     """Weights on the device plus the library's model handle.
 

@@ -391,6 +391,13 @@ int spec_backoff_pass(spec_backoff* states, int n, const int32_t* kept, int spec
 int spec_profile_enable(spec_model* model, int kernel_class, int every);
 int spec_profile_collect(spec_model* model, double* total_ms, int* launches);
 
+/* Tests only: the number of polls a workgroup of the sampled bf16 head's cooperative
+ * launch makes at each grid barrier before it gives up (default about a second of
+ * polling; >= 0, else SPEC_E_INVAL).  A small limit lets a test force the failure path
+ * from the host: a workgroup that gives up raises the launch's error flag and goes on,
+ * every wave ends, and spec_accept reports committed[l] = 0 for every lane. */
+int spec_debug_barrier_spin(spec_model* model, int polls);
+
 #ifdef __cplusplus
 }
 #endif

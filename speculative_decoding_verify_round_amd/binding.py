@@ -28,7 +28,8 @@ HEADER_SYMBOLS = (
     "spec_status_string", "spec_plan_drafts", "spec_model_create", "spec_model_destroy",
     "spec_workspace_bytes", "spec_verify_round", "spec_verify_head", "spec_accept", "spec_commit",
     "spec_debug_logits", "spec_debug_gemm", "spec_packed_weight_bytes", "spec_pack_weight",
-    "spec_profile_enable", "spec_profile_collect", "spec_ngram_draft", "spec_history_append",
+    "spec_profile_enable", "spec_profile_collect", "spec_debug_barrier_spin", "spec_ngram_draft",
+    "spec_history_append",
     "spec_backoff_init", "spec_backoff_call", "spec_backoff_pass", "spec_counts_add",
     "spec_window_live_block", "spec_verify_head_noalloc",
 )
@@ -119,6 +120,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         lib.spec_pack_weight.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         lib.spec_profile_enable.restype = C.c_int
         lib.spec_profile_enable.argtypes = [C.c_void_p, C.c_int, C.c_int]
+        lib.spec_debug_barrier_spin.restype = C.c_int
+        lib.spec_debug_barrier_spin.argtypes = [C.c_void_p, C.c_int]
         lib.spec_profile_collect.restype = C.c_int
         lib.spec_profile_collect.argtypes = [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int)]
         lib.spec_ngram_draft.restype = C.c_int
@@ -217,6 +220,10 @@ def spec_packed_weight_bytes(N: int, K: int) -> int:
 def spec_pack_weight(src_ptr: int, dst_ptr: int, N: int, K: int, stream: int) -> None:
     _check(load_library().spec_pack_weight(C.c_void_p(src_ptr), C.c_void_p(dst_ptr), int(N), int(K),
                                            C.c_void_p(stream)), "spec_pack_weight")
+
+
+def spec_debug_barrier_spin(model, polls: int) -> None:
+    _check(load_library().spec_debug_barrier_spin(model, int(polls)), "spec_debug_barrier_spin")
 
 
 def spec_profile_enable(model, kernel_class: int, every: int = 1) -> None:

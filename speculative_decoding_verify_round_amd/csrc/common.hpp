@@ -317,6 +317,7 @@ struct LmParams {
   // counters (kCoopCounters ints, zero at launch), the reduced row statistics, the lane
   // decisions, the residual race partials [L][groups][4] and the drafter's q [R][V]
   int* bar;
+  int spin_limit;          // polls per grid barrier before the error flag is raised
   RowStat* rstat;
   LaneDecision* dec;
   float* racep;

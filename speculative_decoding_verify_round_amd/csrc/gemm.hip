@@ -1159,19 +1159,18 @@ int launch_race(const RaceParams& p, hipStream_t st) {
 // workgroup's slice reads out of range (zeros, no memory traffic), so every load sits on
 // a straight-line path and the compiler's vmcnt waits stay exact.
 constexpr int kCoopWaves = 8;
-constexpr int kSpinLimit = 1 << 21;   // polls of one barrier (about a second) before giving up
 
 // Grid barrier of a cooperative launch (every workgroup resident).  Each thread's
 // agent-coherent stores have completed before its workgroup counts itself in; thread 0
 // polls the count with agent-coherent loads.  The wait is bounded: past the limit the
 // workgroup raises the error flag and goes on, so every wave ends.
-__device__ __forceinline__ void grid_barrier(int* cnt, int target, int* err) {
+__device__ __forceinline__ void grid_barrier(int* cnt, int target, int* err, int limit) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int spin = 0; __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
-      if (spin >= kSpinLimit) {
+      if (spin >= limit) {
         __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -1408,7 +1407,7 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
     st_coherent16(p.part, (uint32_t)(b * p.R + r), o);
   }
   if (b == 0 && threadIdx.x == 0) __hip_atomic_store(p.bar + 3, G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  grid_barrier(p.bar + 0, G, p.bar + 2);
+  grid_barrier(p.bar + 0, G, p.bar + 2, p.spin_limit);
 
   // ---- 2. row r's partials in workgroup order: 256 threads, a fixed tree
   for (int r = b; r < p.R; r += G) {   // workgroup-uniform
@@ -1443,7 +1442,7 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
     }
     __syncthreads();
   }
-  grid_barrier(p.bar + 1, G, p.bar + 2);
+  grid_barrier(p.bar + 1, G, p.bar + 2, p.spin_limit);
 
   // ---- 3. every lane's decision, then each lane's draw over the slice: the residual race of
   // a lane that rejected a draft, the bonus race (Gumbel-max on z / T, as a minimum of

@@ -6,6 +6,7 @@
 namespace sv {
 
 // projections
+constexpr int kBarrierSpin = 1 << 21;   // default polls of one grid barrier (about a second)
 int launch_proj(const ProjParams& p, bool swiglu, int xs, hipStream_t st);
 // cut units of a balanced gate/up launch of N features over K (rem units of pq pieces
 // each); returns rem * pq, 0 when the launch needs no cut

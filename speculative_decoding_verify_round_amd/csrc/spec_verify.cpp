@@ -47,6 +47,7 @@ struct spec_model {
   int chunk = kDefaultChunk;
   Split s_in_attn{1}, s_in_gdn{1}, s_o_attn{1}, s_o_gdn{1}, s_gateup{1}, s_down{1};
   int lm_groups = 1;
+  int barrier_spin = sv::kBarrierSpin;   // polls per grid barrier of the cooperative head
   // profiling
   int prof_class = SPEC_K_NONE;
   int prof_every = 1;             // record launches 0, every, 2 every, ... of the class
@@ -424,6 +425,7 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   p.presence = r->presence_penalty;
   p.frequency = r->frequency_penalty;
   p.bar = at<int>(r->workspace, w.bar);
+  p.spin_limit = m->barrier_spin;
   p.rstat = at<sv::RowStat>(r->workspace, w.rstat);
   p.dec = at<sv::LaneDecision>(r->workspace, w.dec);
   p.racep = at<float>(r->workspace, w.racep);
@@ -815,6 +817,12 @@ int spec_profile_enable(spec_model* m, int kernel_class, int every) {
   m->prof_seen = 0;
   m->prof_events.clear();
   m->prof_used = 0;
+  return SPEC_OK;
+}
+
+int spec_debug_barrier_spin(spec_model* m, int polls) {
+  if (!m || polls < 0) return SPEC_E_INVAL;
+  m->barrier_spin = polls;
   return SPEC_OK;
 }
 

@@ -182,6 +182,9 @@ def test_other_calls_validate(model):
     assert lib.spec_debug_gemm(model, FAKE, FAKE, FAKE, 0, 16, 256, None, 0, None) == B.SPEC_E_INVAL
     assert lib.spec_debug_gemm(model, FAKE, FAKE, FAKE, 8, 16, 100, None, 0, None) == B.SPEC_E_UNSUPPORTED
     assert lib.spec_profile_enable(model, 99, 1) == B.SPEC_E_INVAL
+    assert lib.spec_debug_barrier_spin(model, -1) == B.SPEC_E_INVAL
+    assert lib.spec_debug_barrier_spin(None, 5) == B.SPEC_E_INVAL
+    assert lib.spec_debug_barrier_spin(model, 0) == B.SPEC_OK
     assert lib.spec_profile_enable(model, B.SPEC_K_GATE_UP, 0) == B.SPEC_E_INVAL
 
 

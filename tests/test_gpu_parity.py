@@ -297,6 +297,42 @@ def test_head_only_full_size_greedy_and_sampled(split, mismatch_budget):
     dm.close()
 
 
+def test_sampled_head_barrier_failure_reports_zero():
+    """The cooperative head's failure path, forced from the host: with no polls allowed at
+    its grid barriers the workgroups that arrive early give up, raise the error flag and
+    go on, every wave ends, and acceptance reports committed = 0 on every lane; with the
+    default limit restored the same round commits what it committed before."""
+    from speculative_decoding_verify_round_amd import binding as B
+    from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel
+    cfg = synth.get_config("head-v151936")
+    L, k = 8, 7
+    w = _head_weights_cached(cfg)
+    dm = DeviceModel(cfg, w)
+    dc = DeviceCache(dm, L, 1, 1, kv_len=[cfg.context] * L)
+    hd = torch.from_numpy(synth.hidden_states(cfg, L * (k + 1))).to("cuda", torch.bfloat16)
+    q, d = synth.drafter_rows(cfg.input_seed, 99, L * (k + 1), cfg.vocab)
+    toks = [[int(l)] + [int(x) for x in d[l * (k + 1) + 1:(l + 1) * (k + 1)]] for l in range(L)]
+    qd = torch.from_numpy(q).cuda()
+
+    def run():
+        rc = dc.round(toks, mode="sampled", temperature=cfg.temperature, q_probs=qd, seed=cfg.philox_seed)
+        dc.verify_head(rc, hd)
+        dc.accept(rc)
+        c, em, _ = dc.results(rc)
+        return [int(x) for x in c], em
+
+    c_ref, em_ref = run()
+    assert all(1 <= x <= k + 1 for x in c_ref), c_ref
+    B.spec_debug_barrier_spin(dm.handle, 0)
+    c_fail, _ = run()
+    log(f"barrier failure forced: committed {c_fail} (normal {c_ref})")
+    assert c_fail == [0] * L
+    B.spec_debug_barrier_spin(dm.handle, 1 << 21)
+    c_again, em_again = run()
+    assert c_again == c_ref and em_again == em_ref
+    dm.close()
+
+
 _HEAD_CACHE = {}
 
 

@@ -221,6 +221,36 @@ def test_small_hybrid_bf16_round_and_commit():
     pair.close()
 
 
+def test_maximum_rows_columns_and_hidden():
+    """The largest shapes the kernels take: hidden 8192 (the row kernels' limit; the QKV
+    projection at the largest split, 8), 4 lanes x 16 columns = 64 rows (every lane at the
+    column limit, 64 query rows per lane with 4 query heads per kv head, so all four query
+    tiles are busy), the columns starting at slot 15 of a cache block so they straddle two
+    staged blocks.  A greedy and a sampled round, then a teacher-forced commit of all 16
+    columns of every lane against the oracle's."""
+    ctx = 47
+    cfg = small_dense(hidden=8192, n_q_heads=4, n_kv_heads=1, head_dim=128, ffn=512, vocab=2048, context=ctx,
+                      n_layers=1, layer_kinds=("attn",))
+    L, cols = 4, 16
+    pair = Pair(cfg, lanes=L, context=ctx, max_blocks=(ctx + cols + 16) // 16 + 1)
+    rng = np.random.default_rng(11)
+    toks = [[int(x) for x in rng.integers(0, cfg.vocab, cols)] for _ in range(L)]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks)
+    log(f"maximum sizes greedy: logit err {lerr:.2e}, committed {list(c)}, mismatches {mism}")
+    assert not mism
+    q, d = synth.drafter_rows(cfg.input_seed, 77, L * cols, cfg.vocab)
+    toks = [[int(100 + l)] + [int(x) for x in d[l * cols + 1:(l + 1) * cols]] for l in range(L)]
+    ores, rc, c, em, st, lerr, mism = _round_parity(pair, toks, "sampled", 0.9, q, seed=99)
+    log(f"maximum sizes sampled: logit err {lerr:.2e}, committed {list(c)}, mismatches {mism}")
+    assert not mism
+    pair.om.commit(pair.oc, ores, [cols] * L)
+    pair.dc.commit(rc, torch.full((L,), cols, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert list(pair.dc.kv_len.cpu().numpy()) == [ctx + cols] * L == list(pair.oc.kv_len)
+    check_committed_cache(pair, ctx)
+    pair.close()
+
+
 def test_sampled_rounds_small_dense():
     cfg = small_dense(hidden=256, head_dim=128, ffn=512, vocab=1024, context=37)
     pair = Pair(cfg, lanes=4, context=37, max_blocks=8)

@@ -1240,7 +1240,7 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
   if ((int)threadIdx.x < p.R) {
     const int r = threadIdx.x, tk = p.tokens[r];
     const int l = p.ri.row_lane[r], j = p.ri.row_col[r];
-    sqd[r] = j > 0 && tk >= 0 && tk < p.V ? p.q[(size_t)r * p.V + tk] : 0.f;
+    sqd[r] = p.sampled && j > 0 && tk >= 0 && tk < p.V ? p.q[(size_t)r * p.V + tk] : 0.f;
     snext[r] = j == p.ri.lane_cols[l] - 1 ? -1 : p.tokens[r + 1];
   }
 
@@ -1404,8 +1404,10 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
     for (int w = 1; w < NW; ++w) s = stat_merge(s, sh[w * kMaxRows + r], p.inv_t);
     LmPartial o;
     o.m = s.m; o.se = s.se; o.arg = s.arg; o.zn = s.zn; o.gk = s.gk; o.gi = s.gi; o.pad0 = o.pad1 = 0;
-    st_coherent16(p.part, (uint32_t)(b * p.R + r), o);
+    if (p.sampled) st_coherent16(p.part, (uint32_t)(b * p.R + r), o);
+    else p.part[(size_t)r * G + b] = o;   // greedy: row-major partials for k_row_reduce, nothing else
   }
+  if (!p.sampled) return;
   if (b == 0 && threadIdx.x == 0) __hip_atomic_store(p.bar + 3, G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   grid_barrier(p.bar + 0, G, p.bar + 2, p.spin_limit);
 
@@ -1591,7 +1593,10 @@ int launch_lmhead_coop(const LmParams& p0, int grid, hipStream_t st) {
 #undef SV_C
   if (!f) return -2;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kCoopWaves * 64), args, 0, st) == hipSuccess ? 0 : -1;
+  // greedy statistics need no grid barrier: a plain launch of the same one-per-CU grid
+  const hipError_t e = p.sampled ? hipLaunchCooperativeKernel(f, dim3(grid), dim3(kCoopWaves * 64), args, 0, st)
+                                 : hipLaunchKernel(f, dim3(grid), dim3(kCoopWaves * 64), args, 0, st);
+  return e == hipSuccess ? 0 : -1;
 }
 
 }  // namespace sv

@@ -211,6 +211,12 @@ bool coop_head_fits(const spec_model* m) {
   return tiles <= 64LL * sv::kCUs && (long long)m->d.vocab * m->d.hidden * 2 <= 0x80000000LL;
 }
 
+// Greedy statistics of a bf16 head through the same one-workgroup-per-CU kernel (no grid
+// barrier) when the head fits it on this device.
+bool greedy_head_coop(const spec_model* m) {
+  return m->bf16 && coop_head_fits(m) && (long long)m->d.vocab / 16 <= 64LL * sv::coop_grid();
+}
+
 // Validation of a round's arguments, the workspace aside; fills ri.
 int validate_round(const spec_model* m, const spec_round* r, bool head_only, sv::RowInfo& ri) {
   if (!m) return SPEC_E_INVAL;
@@ -431,7 +437,9 @@ int lm_stats(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, co
   p.racep = at<float>(r->workspace, w.racep);
   p.q = r->q_probs;
   ProfScope ps(m, SPEC_K_LM_HEAD, st);
-  if (m->bf16 && p.sampled) {   // statistics, decisions and residual race in one cooperative launch
+  if (m->bf16 && (p.sampled || greedy_head_coop(m))) {
+    // one workgroup per CU over a vocabulary slice each: sampled, statistics, decisions and
+    // residual race in one cooperative launch; greedy, the per-workgroup statistics only
     const int rc = sv::launch_lmhead_coop(p, sv::coop_grid(), st);
     return rc == 0 ? SPEC_OK : (rc == -2 ? SPEC_E_UNSUPPORTED : SPEC_E_HIP);
   }
@@ -634,7 +642,8 @@ int run_accept(const spec_model* m, const spec_round* r, const sv::RowInfo& ri, 
                                     out_tokens, row_stats, ri, s));
     return SPEC_OK;
   }
-  SV_CHECK(sv::launch_row_reduce(at<sv::LmPartial>(ws, w.lmp), m->lm_groups, ri.R, inv_t, at<sv::RowStat>(ws, w.rstat),
+  const int groups = greedy_head_coop(m) ? sv::coop_grid() : m->lm_groups;   // the head's partials per row
+  SV_CHECK(sv::launch_row_reduce(at<sv::LmPartial>(ws, w.lmp), groups, ri.R, inv_t, at<sv::RowStat>(ws, w.rstat),
                                  row_stats, s));
   SV_CHECK(sv::launch_lane_accept(at<sv::RowStat>(ws, w.rstat), r->tokens, r->kv_len, r->q_probs, m->d.vocab,
                                   sampled ? 1 : 0, inv_t, k0, k1, at<sv::LaneDecision>(ws, w.dec), committed,

@@ -66,35 +66,31 @@ __device__ __forceinline__ float col_sum(float v) {
 // ---------------------------------------------------------------- QKV post-processing
 // A bf16 model's attention kernel takes the QKV projection's split partials directly:
 // each value is the sum of the S partials in split order in float64, rounded once to
-// float; q and k are then rotated (rotate-half RoPE, "per-token side inputs such as
-// positions" of the FreeToken issue's "Flow") in float64 and rounded to float, k and v to
-// bf16 for the cache.
+// float; q and k are then rotated (rotate-half RoPE: the token positions are among the
+// per-token inputs of the FreeToken issue's "Flow") in float64 and rounded to float, k and
+// v to bf16 for the cache.
 
-// NG groups of four consecutive floats, every split loaded (four splits at a time)
-// before the first addition.
-template <int NG>
-__device__ __forceinline__ void proj_sum(const float* const (&src)[NG], size_t ss, int S, float (&out)[NG][4]) {
-  constexpr int B = 4;
-  double acc[NG][4];
-  for (int s0 = 0; s0 < S; s0 += B) {
-    f32x4 v[B][NG];
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive floats summed over the splits s = 0 .. S - 1 in split order in float64,
+// rounded once: the first OB splits come loaded (v[b] = split min(b, S - 1)), later ones
+// are read here from src + s ss.  Selects rather than branches, so that the compiler keeps
+// the loads of v where the caller issued them.
+template <int OB>
+__device__ __forceinline__ f32x4 split_sum(const f32x4 (&v)[OB], const float* src, size_t ss, int S) {
+  double a[4];
 #pragma unroll
-    for (int b = 0; b < B; ++b)
+  for (int e = 0; e < 4; ++e) a[e] = (double)v[0][e];
 #pragma unroll
-      for (int n = 0; n < NG; ++n) v[b][n] = *reinterpret_cast<const f32x4*>(src[n] + (size_t)min(s0 + b, S - 1) * ss);
+  for (int b = 1; b < OB; ++b)
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if (s0 + b >= S) break;
+    for (int e = 0; e < 4; ++e) a[e] = b < S ? a[e] + (double)v[b][e] : a[e];
+  for (int b = OB; b < S; ++b) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(src + (size_t)b * ss);
 #pragma unroll
-      for (int n = 0; n < NG; ++n)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[n][e] = (s0 + b == 0) ? (double)v[b][n][e] : acc[n][e] + (double)v[b][n][e];
-    }
+    for (int e = 0; e < 4; ++e) a[e] += (double)w[e];
   }
-#pragma unroll
-  for (int n = 0; n < NG; ++n)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[n][e] = (float)acc[n][e];
+  return f32x4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
 }
 
 // Two bf16 values in one word, a at the lower address.
@@ -107,6 +103,15 @@ __device__ __forceinline__ void rotate_half(float& a, float& b, double c, double
   const double av = (double)a, bv = (double)b;
   a = (float)(av * c - bv * sn);
   b = (float)(bv * c + av * sn);
+}
+
+// rotate_half by the loaded angle cs = (cos, sin) when `on`, else (a, b) unchanged (a
+// select: cs holds no angle then).
+__device__ __forceinline__ void rotate_half_if(bool on, float& a, float& b, f64x2 cs) {
+  float x = a, y = b;
+  rotate_half(x, y, cs[0], cs[1]);
+  a = on ? x : a;
+  b = on ? y : b;
 }
 
 // bf16 verify attention, one workgroup per (chunk range, kv head, lane).  The
@@ -217,13 +222,23 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
   }
   const int N = (p.nq + 2 * nkv) * D;
   const size_t ss = (size_t)p.ri.R * N;
+  // Every load of the prologue is issued before the first use of any: the split partials
+  // of up to OB splits and the RoPE angles of the own columns and of the queries.  The
+  // sums take the loaded splits through selects, not branches, so that no load is sunk to
+  // its use (a chain of memory round trips otherwise).
+  constexpr int OB = 4;                        // splits requested up front
+  const bool rope = p.rope != nullptr;
+  // without RoPE the angle loads read this (valid) row instead and are discarded
+  const f64x2* rdummy = reinterpret_cast<const f64x2*>(p.P + (size_t)rs * N);
+  auto rope_at = [&](int row, int i0) -> const f64x2* {
+    return rope ? reinterpret_cast<const f64x2*>(p.rope + ((size_t)row * (D / 2) + i0) * 2) : rdummy;
+  };
   // own columns: item k of this thread (k = 0, 1) is (column j, rotation pairs i0 .. i0 + 3
-  // of K) for items below cols 16, then (column j, elements i0 .. i0 + 3 of V); the split
-  // partials of up to four splits are requested here, summed after the queries
+  // of K) for items below cols 16, then (column j, elements i0 .. i0 + 3 of V)
   const bool own = min(c1 * p.chunk, end) > kvl;
   const int nownk = cols * 16, nown = cols * 48;
-  constexpr int OB = 4;                        // splits requested up front
   f32x4 ownraw[2][2][OB];
+  f64x2 ownrt[2][4];
   auto own_item = [&](int it, bool& isk, int& j, int& i0) {
     isk = it < nownk;
     const int jt = isk ? it : it - nownk, per = isk ? 16 : 32;
@@ -242,69 +257,74 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnParams p) {
     for (int k = 0; k < 2; ++k) {
       if (k == 1 && nown <= 512) break;        // one item per thread
       const int it = min(tid + 512 * k, nown - 1);
-      const int nh = it < nownk ? 2 : 1;       // K items read both halves of the head
+      bool isk;
+      int j, i0;
+      own_item(it, isk, j, i0);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int b = 0; b < OB; ++b)
-          if (hf < nh) ownraw[k][hf][b] = *reinterpret_cast<const f32x4*>(own_src(it, hf) + (size_t)min(b, p.S - 1) * ss);
+        for (int b = 0; b < OB; ++b)   // V items read their elements twice (the second copy is unused)
+          ownraw[k][hf][b] = *reinterpret_cast<const f32x4*>(own_src(it, isk ? hf : 0) + (size_t)min(b, p.S - 1) * ss);
+      const f64x2* rt = isk ? rope_at(rs + j, i0) : rdummy;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ownrt[k][e] = rt[e];
     }
   }
   // queries, each element once per workgroup: item it (two per thread) = (query row mr,
-  // rotation pairs i0 .. i0 + 3); the float32 queries go to ring slot NS - 1 (untouched
-  // until the loop's first barrier), float4 group c of row mr at c ^ (mr & 31)
-  float* qs = reinterpret_cast<float*>(ring + (NS - 1) * SBYTES);   // [64][128] floats
-  float qv[2][2][4];
+  // rotation pairs i0 .. i0 + 3)
+  f32x4 qraw2[2][2][OB];
+  f64x2 qrt[2][4];
+  const float* qrow[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int it = min(tid + 512 * k, Mq * 16 - 1);
     const int mr = it >> 4, i0 = 4 * (it & 15);
     const int jr = mr / p.G, hr = mr - jr * p.G;
-    const float* row = p.P + (size_t)(rs + jr) * N + (size_t)(g * p.G + hr) * D + i0;
-    const float* src[2] = {row, row + D / 2};
-    proj_sum<2>(src, ss, p.S, qv[k]);
-    if (p.rope) {
-      const double* rt = p.rope + ((size_t)(rs + jr) * (D / 2) + i0) * 2;
+    qrow[k] = p.P + (size_t)(rs + jr) * N + (size_t)(g * p.G + hr) * D + i0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rotate_half(qv[k][0][e], qv[k][1][e], rt[2 * e], rt[2 * e + 1]);
-    }
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int b = 0; b < OB; ++b)
+        qraw2[k][hf][b] = *reinterpret_cast<const f32x4*>(qrow[k] + hf * (D / 2) + (size_t)min(b, p.S - 1) * ss);
+    const f64x2* rt = rope_at(rs + jr, i0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qrt[k][e] = rt[e];
   }
-  // own columns: sums in split order in float64 (splits past OB requested now), rotation,
-  // bf16; held in registers until the column's stage is in LDS
+  // the float32 queries go to ring slot NS - 1 (untouched until the loop's first
+  // barrier), float4 group c of row mr at c ^ (mr & 31)
+  float* qs = reinterpret_cast<float*>(ring + (NS - 1) * SBYTES);   // [64][128] floats
+  float qv[2][2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 v = split_sum<OB>(qraw2[k][hf], qrow[k] + hf * (D / 2), ss, p.S);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[k][hf][e] = v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rotate_half_if(rope, qv[k][0][e], qv[k][1][e], qrt[k][e]);
+  }
+  // own columns: sums in split order in float64, rotation, bf16; held in registers until
+  // the column's stage is in LDS
   u32x4 ownv[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
   if (own) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       if (k == 1 && nown <= 512) break;
-      const int it = tid + 512 * k;
+      const int it = min(tid + 512 * k, nown - 1);
       bool isk;
       int j, i0;
-      own_item(min(it, nown - 1), isk, j, i0);
+      own_item(it, isk, j, i0);
       float v[2][4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        if (hf == 1 && !isk) break;
-        double a[4];
+        const f32x4 w = split_sum<OB>(ownraw[k][hf], own_src(it, isk ? hf : 0), ss, p.S);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = (double)ownraw[k][hf][0][e];
-#pragma unroll
-        for (int b = 1; b < OB; ++b)
-          if (b < p.S)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] += (double)ownraw[k][hf][b][e];
-        for (int b = OB; b < p.S; ++b) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(own_src(min(it, nown - 1), hf) + (size_t)b * ss);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] += (double)w[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[hf][e] = (float)a[e];
+        for (int e = 0; e < 4; ++e) v[hf][e] = w[e];
       }
-      if (isk && p.rope) {
-        const double* rt = p.rope + ((size_t)(rs + j) * (D / 2) + i0) * 2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rotate_half(v[0][e], v[1][e], rt[2 * e], rt[2 * e + 1]);
-      }
+      for (int e = 0; e < 4; ++e) rotate_half_if(isk && rope, v[0][e], v[1][e], ownrt[k][e]);
       ownv[k] = isk ? u32x4{pack_bf16(v[0][0], v[0][1]), pack_bf16(v[0][2], v[0][3]), pack_bf16(v[1][0], v[1][1]),
                             pack_bf16(v[1][2], v[1][3])}
                     : u32x4{pack_bf16(v[0][0], v[0][1]), pack_bf16(v[0][2], v[0][3]), 0u, 0u};

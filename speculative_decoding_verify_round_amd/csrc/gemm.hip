@@ -1285,10 +1285,13 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
     for (int j = 0; j < T; ++j)
 #pragma unroll
       for (int t = 0; t < RT; ++t) acc[q][j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 wr[kUnit][T];
+  // weight ring: RD steps of the wave's T tiles in flight (a whole unit for up to two
+  // tiles, half a unit for more, within the registers of two waves per SIMD)
+  constexpr int RD = T > 2 ? kUnit / 2 : kUnit;
+  u32x4 wr[RD][T];
   stage_load(0);
 #pragma unroll
-  for (int k = 0; k < kUnit; ++k)
+  for (int k = 0; k < RD; ++k)
 #pragma unroll
     for (int j = 0; j < T; ++j) wr[k][j] = wload(wbase[0][j] + k * 1024);
   stage_store(0);
@@ -1299,11 +1302,14 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
   for (int q = 0; q < NP; ++q) {
     if (q > 0 && tb0 + q * T * NW >= tb1) break;   // workgroup-uniform: the slice is done
     for (int u = 0; u < U; ++u) {
-      // refills of this unit load unit u + 1 of the pass, or unit 0 of the next pass
-      uint32_t nb[T];
+      // refills RD steps ahead: within this unit, else into unit u + 1 of the pass or unit 0
+      // of the next pass
+      uint32_t cu[T], nb[T];
 #pragma unroll
-      for (int j = 0; j < T; ++j)
+      for (int j = 0; j < T; ++j) {
+        cu[j] = wbase[q][j] + (uint32_t)u * kUnit * 1024u;
         nb[j] = u + 1 < U ? wbase[q][j] + (uint32_t)(u + 1) * kUnit * 1024u : (q + 1 < NP ? wbase[q + 1][j] : wbytes);
+      }
 #pragma unroll
       for (int h = 0; h < NC; ++h) {
         const int c = u * NC + h;
@@ -1324,9 +1330,10 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
 #pragma unroll
             for (int t = 0; t < RT; ++t)
 #pragma unroll
-              for (int pl = XS - 1; pl >= 0; --pl) acc[q][j][t] = mfma_bf16(wr[k][j], xo[pl][t], acc[q][j][t]);
+              for (int pl = XS - 1; pl >= 0; --pl) acc[q][j][t] = mfma_bf16(wr[k % RD][j], xo[pl][t], acc[q][j][t]);
 #pragma unroll
-          for (int j = 0; j < T; ++j) wr[k][j] = wload(nb[j] + k * 1024);
+          for (int j = 0; j < T; ++j)
+            wr[k % RD][j] = wload(k + RD < kUnit ? cu[j] + (k + RD) * 1024 : nb[j] + (k + RD - kUnit) * 1024);
           __builtin_amdgcn_sched_barrier(0);
         }
         stage_store(cb ^ 1);
@@ -1549,6 +1556,9 @@ struct CoopShape {
 
 static CoopShape coop_shape(int V, int grid, int RT) {
   const int per = (V / 16 + grid - 1) / grid;
+  // one pass of up to five tiles per wave: the activation is staged once
+  const int t1 = (per + kCoopWaves - 1) / kCoopWaves;
+  if (t1 > 2 && t1 <= 5) return CoopShape{1, 5};
   const int np2 = (per + 2 * kCoopWaves - 1) / (2 * kCoopWaves);
   if (np2 <= 3 || (np2 == 4 && RT <= 2)) return CoopShape{std::max(np2, 1), 2};
   const int np1 = (per + kCoopWaves - 1) / kCoopWaves;
@@ -1568,6 +1578,8 @@ int launch_lmhead_coop(const LmParams& p0, int grid, hipStream_t st) {
 #define SV_C_NP(RT_, XS_)                                    \
   if (cs.t == 1) {                                           \
     if constexpr (RT_ >= 3) SV_C(RT_, XS_, 8, 1);            \
+  } else if (cs.t == 5) {                                    \
+    SV_C(RT_, XS_, 1, 5);                                    \
   } else {                                                   \
     switch (cs.np) {                                         \
       case 1: SV_C(RT_, XS_, 1, 2); break;                   \

@@ -1286,8 +1286,9 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_coop(LmParams p) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) acc[q][j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // weight ring: RD steps of the wave's T tiles in flight (a whole unit for up to two
-  // tiles, half a unit for more, within the registers of two waves per SIMD)
-  constexpr int RD = T > 2 ? kUnit / 2 : kUnit;
+  // tiles, half a unit for up to five, a quarter for more: 16-20 fragments a wave, within
+  // the registers of two waves per SIMD)
+  constexpr int RD = T > 5 ? kUnit / 4 : T > 2 ? kUnit / 2 : kUnit;
   u32x4 wr[RD][T];
   stage_load(0);
 #pragma unroll
@@ -1547,18 +1548,22 @@ int coop_grid() {
 }
 
 // Slice shape of the cooperative head: T tiles per wave and pass, NP passes of 8 T tiles,
-// rounded up to an instantiated count.  Two tiles per wave keep 16 KB of weights in flight
-// per wave; one tile per wave in up to eight passes where four passes of two would hold
-// more accumulators than the registers of two waves per SIMD.
+// rounded up to an instantiated count.  One pass of five tiles per wave (eight with at
+// most two row tiles) stages the activation once; smaller slices take passes of two tiles
+// per wave (16 KB of weights in flight per wave); one tile per wave in up to eight passes
+// where four passes of two would hold more accumulators than the registers of two waves
+// per SIMD.
 struct CoopShape {
   int np, t;
 };
 
 static CoopShape coop_shape(int V, int grid, int RT) {
   const int per = (V / 16 + grid - 1) / grid;
-  // one pass of up to five tiles per wave: the activation is staged once
+  // one pass of up to five tiles per wave (eight with at most two row tiles): the
+  // activation is staged once
   const int t1 = (per + kCoopWaves - 1) / kCoopWaves;
   if (t1 > 2 && t1 <= 5) return CoopShape{1, 5};
+  if (t1 > 5 && t1 <= 8 && RT <= 2) return CoopShape{1, 8};
   const int np2 = (per + 2 * kCoopWaves - 1) / (2 * kCoopWaves);
   if (np2 <= 3 || (np2 == 4 && RT <= 2)) return CoopShape{std::max(np2, 1), 2};
   const int np1 = (per + kCoopWaves - 1) / kCoopWaves;
@@ -1580,6 +1585,8 @@ int launch_lmhead_coop(const LmParams& p0, int grid, hipStream_t st) {
     if constexpr (RT_ >= 3) SV_C(RT_, XS_, 8, 1);            \
   } else if (cs.t == 5) {                                    \
     SV_C(RT_, XS_, 1, 5);                                    \
+  } else if (cs.t == 8) {                                    \
+    if constexpr (RT_ <= 2) SV_C(RT_, XS_, 1, 8);            \
   } else {                                                   \
     switch (cs.np) {                                         \
       case 1: SV_C(RT_, XS_, 1, 2); break;                   \

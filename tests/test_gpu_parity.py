@@ -327,6 +327,63 @@ def test_head_only_full_size_greedy_and_sampled(split, mismatch_budget):
     dm.close()
 
 
+# Vocabularies whose slices on 256 workgroups take each streaming shape of the cooperative
+# head: 20-21 tiles (one pass, five tile slots per wave, many empty), 45-46 tiles (one pass
+# of eight per wave up to two row tiles; three passes of two beyond), 60-61 tiles (one pass
+# of eight; eight passes of one beyond two row tiles), each with a ragged last slice.
+@pytest.mark.parametrize("V", [16 * (256 * 20 + 37), 16 * (256 * 45 + 100), 16 * (256 * 60 + 5)])
+@pytest.mark.parametrize("split", [(4, 3), (8, 7)])
+def test_head_slice_shapes(V, split, mismatch_budget):
+    """LM head statistics and acceptance (greedy and sampled T 0.7) at hidden 512 for
+    vocabularies that put every slice shape of the head kernel to work, at 16 and 64 rows."""
+    import dataclasses
+    from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceModel
+    from oracle import OracleModel
+    L, k = split
+    R = L * (k + 1)
+    cfg = dataclasses.replace(synth.get_config("head-v151936"), name=f"head-v{V}", vocab=V, hidden=512)
+    w = synth.head_weights(cfg)
+    dm = DeviceModel(cfg, w)
+    dc = DeviceCache(dm, L, 1, 1, kv_len=[cfg.context] * L)
+    hid = synth.hidden_states(cfg, R)
+    z = OracleModel(cfg, w).lm_head(hid)
+    hd = torch.from_numpy(hid).to("cuda", torch.bfloat16)
+    q, d = synth.drafter_rows(cfg.input_seed, 98, R, V)
+    toks = [[int(l)] + [int(x) for x in d[l * (k + 1) + 1:(l + 1) * (k + 1)]] for l in range(L)]
+    nxt = []
+    for l in range(L):
+        nxt += toks[l][1:] + [-1]
+    for mode in ("greedy", "sampled"):
+        T = cfg.temperature if mode == "sampled" else 1.0
+        rc = dc.round(toks, mode=mode, temperature=T, q_probs=torch.from_numpy(q).cuda() if mode == "sampled" else None,
+                      seed=cfg.philox_seed)
+        dc.verify_head(rc, hd)
+        dc.accept(rc)
+        c, em, st = dc.results(rc)
+        os_ = row_stats(z, nxt, T)
+        assert np.max(np.abs(st["max"] - os_["max"])) < 1e-3
+        assert np.max(np.abs(st["lse"] - os_["lse"])) < 1e-3
+        assert (np.isnan(os_["z_next"]) == np.isnan(st["z_next"])).all()
+        m = ~np.isnan(os_["z_next"])
+        assert np.max(np.abs(st["z_next"][m] - os_["z_next"][m])) < 1e-3
+        arg_mism = [r for r in range(R) if st["argmax"][r] != os_["argmax"][r]]
+        assert all(top2_gap(z[r]) < GAP_EXCUSE for r in arg_mism), arg_mism
+        mismatch_budget.add(f"head V {V} {L}x{k + 1} {mode} argmax", R, len(arg_mism))
+        lanes_bad = []
+        for l in range(L):
+            lz = z[l * (k + 1):(l + 1) * (k + 1)]
+            if mode == "greedy":
+                oc_, oem = accept_greedy(lz, toks[l][1:])
+            else:
+                oc_, oem = accept_sampled(lz, toks[l][1:], q[l * (k + 1) + 1:(l + 1) * (k + 1)], T,
+                                          cfg.philox_seed, l, cfg.context)
+            if (oc_, oem) != (int(c[l]), em[l]):
+                lanes_bad.append((l, oc_, oem, int(c[l]), em[l]))
+        log(f"head V {V} {L}x{k + 1} {mode}: committed {list(c)}, differing lanes {lanes_bad}, argmax mism {arg_mism}")
+        assert not lanes_bad
+    dm.close()
+
+
 def test_sampled_head_barrier_failure_reports_zero():
     """The cooperative head's failure path, forced from the host: with no polls allowed at
     its grid barriers the workgroups that arrive early give up, raise the error flag and

@@ -109,18 +109,22 @@ int launch_embed_norm(const int32_t* tokens, const void* embed, int V, int H, co
 }
 
 // Sum of the S split partials of one float4 of a projection, in split order, in float64.
+// A batch's splits past S are loaded (clamped to split S - 1) and dropped by selects, not
+// branches: a branch lets the compiler sink each load to its addition, one memory round
+// trip per split.
 __device__ __forceinline__ void sum_splits4(const float* P, size_t split_stride, int S, double (&t)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = 0.0;
   for (int s0 = 0; s0 < S; s0 += kSplitBatch) {
     f32x4 pv[kSplitBatch];
 #pragma unroll
     for (int i = 0; i < kSplitBatch; ++i)
       pv[i] = *reinterpret_cast<const f32x4*>(P + (size_t)min(s0 + i, S - 1) * split_stride);
 #pragma unroll
-    for (int i = 0; i < kSplitBatch; ++i) {
-      if (s0 + i >= S) break;
+    for (int i = 0; i < kSplitBatch; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (s0 + i == 0) ? (double)pv[i][e] : t[e] + (double)pv[i][e];
-    }
+      for (int e = 0; e < 4; ++e)
+        t[e] = s0 + i == 0 ? (double)pv[i][e] : s0 + i < S ? t[e] + (double)pv[i][e] : t[e];
   }
 }
 
@@ -136,11 +140,9 @@ __device__ __forceinline__ void sum_loaded4(const f32x4 (&pv)[kSplitBatch], cons
 #pragma unroll
   for (int e = 0; e < 4; ++e) t[e] = (double)pv[0][e];
 #pragma unroll
-  for (int i = 1; i < kSplitBatch; ++i) {
-    if (i >= S) break;
+  for (int i = 1; i < kSplitBatch; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t[e] += (double)pv[i][e];
-  }
+    for (int e = 0; e < 4; ++e) t[e] = i < S ? t[e] + (double)pv[i][e] : t[e];
   if (S > kSplitBatch) {   // more splits than one batch (the split rule allows at most 8)
     double u[4];
     sum_splits4(P + kSplitBatch * split_stride, split_stride, S - kSplitBatch, u);
@@ -167,20 +169,21 @@ __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int 
     gn[gi] = *reinterpret_cast<const f32x4*>(gain + 4 * g);
     load_splits4(P + (size_t)r * H + 4 * g, sstride, S, pv[gi]);
   }
+  // every group is summed (a clamped group repeats the row's last one) and only valid
+  // groups are stored and counted: no branch between the loads and their use
   f32x4 xn[kRowGroups];
   double ss = 0.0;
 #pragma unroll
   for (int gi = 0; gi < kRowGroups; ++gi) {
     const int g = threadIdx.x + gi * kRowThreads;
-    xn[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (4 * g >= H) continue;
+    const bool ok = 4 * g < H;
     double t[4];
-    sum_loaded4(pv[gi], P + (size_t)r * H + 4 * g, sstride, S, t);
+    sum_loaded4(pv[gi], P + (size_t)r * H + 4 * min(g, H / 4 - 1), sstride, S, t);
 #pragma unroll
     for (int e = 0; e < 4; ++e) xn[gi][e] = (float)((double)xo[gi][e] + (double)(float)t[e]);   // x + float(projection)
-    *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
+    if (ok) *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ss += (double)xn[gi][q] * (double)xn[gi][q];
+    for (int q = 0; q < 4; ++q) ss += ok ? (double)xn[gi][q] * (double)xn[gi][q] : 0.0;
   }
   const double tot = block_sum_f64(ss, red);
   const double scale = 1.0 / sqrt(tot / (double)H + (double)eps);

@@ -324,9 +324,13 @@ struct LmParams {
   const float* q;
 };
 
-// Counters of the sampled head's grid barriers in the workspace: arrivals at barrier 1
-// and 2, the error flag (a barrier wait that ran out), the grid size.
-constexpr int kCoopCounters = 4;
+// Counters of the sampled head's grid barriers in the workspace: group arrivals at
+// barrier 1 and 2, the error flag (a barrier wait that ran out), the grid size; then, from
+// int kCoopGroupBase on, the workgroup arrivals of each barrier's eight groups, each
+// count in a 128-byte line of its own (barrier j, group g at kCoopGroupBase + (8 j + g) 32).
+constexpr int kCoopGroups = 8;
+constexpr int kCoopGroupBase = 32;
+constexpr int kCoopCounters = kCoopGroupBase + 2 * kCoopGroups * 32;
 
 // The textbook rule on one lane's rows (Leviathan et al., Def. 3.7): draft d_i is kept iff
 // u * q_i(d_i) < p_{i-1}(d_i), u the Philox uniform at (seed; position kv_len + i, lane,

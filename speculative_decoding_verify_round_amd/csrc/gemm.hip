@@ -1139,17 +1139,17 @@ int launch_race(const RaceParams& p, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-
-
 // ------------------------------------------------------------------------------- sampled LM head
 // Sampled rounds of a bf16 model in one cooperative launch, so that no logit is ever
 // written to memory ("Draft heads and speculative decoding", "Guess, then check": the
 // textbook rule needs the whole row's normaliser before a residual weight is known):
 //  1. Workgroup b (one per CU, eight waves) streams the weights of its slice of
-//     ceil(V / 16 / G) or one fewer 16-token tiles, in passes of eight tiles (wave w takes
-//     local tile 8 q + w in pass q), and keeps every logit of the slice in its
-//     accumulators; it writes one statistics partial per row (max, sum exp((z - m) / T),
-//     argmax, z at the next draft, the bonus race key), penalties applied.
+//     ceil(V / 16 / G) or one fewer 16-token tiles, in NP passes of 8 T tiles (wave w
+//     takes local tiles 8 (q T + j) + w, j < T, in pass q; one pass where the slice fits
+//     the accumulators, so the activation is staged once), and keeps every logit of the
+//     slice in its accumulators; it writes one statistics partial per row (max,
+//     sum exp((z - m) / T), argmax, z at the next draft, the bonus race key), penalties
+//     applied.  Greedy rounds stop here (a plain launch; k_row_reduce takes the partials).
 //  2. Grid barrier; workgroup r reduces row r's partials in workgroup order.
 //  3. Grid barrier; every workgroup reads the row statistics and takes every lane's
 //     decision by the textbook rule (the same walk as k_lane_accept), then runs the

@@ -394,12 +394,31 @@ __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowIn
       s[e] = v4[0]; s[e + 1] = v4[1]; s[e + 2] = v4[2]; s[e + 3] = v4[3];
     }
   }
-  // q and k: 64 four-element items per column, 32 consecutive threads per vector
-  for (int it = t; it < cols * 64; it += 256) {   // uniform over each 32-thread group
+  // q and k: 64 four-element items per column, 32 consecutive threads per vector; v of
+  // the block's rows: eight items per column; alpha and beta: two per column.  The
+  // thread's first item of each kind has its splits loaded together with the state, so
+  // rounds of up to four columns wait for memory once; later q/k items load their own.
+  const int nqk = cols * 64, nv = cols * (kGdnRows / 4), nab = 2 * cols;
+  auto qk_src = [&](int it) {
     const int j = it >> 6, vec = (it >> 5) & 1, quad = it & 31;
-    const int n = vec * hg * kGdnDim + h * kGdnDim + 4 * quad;
-    double a[4];
-    sum_splits4(P + (size_t)(rs + j) * N + n, split, S, a);
+    return P + (size_t)(rs + j) * N + vec * hg * kGdnDim + h * kGdnDim + 4 * quad;
+  };
+  auto v_src = [&](int it) {
+    const int j = it / (kGdnRows / 4), quad = it % (kGdnRows / 4);
+    return P + (size_t)(rs + j) * N + 2 * hg * kGdnDim + h * kGdnDim + rb * kGdnRows + 4 * quad;
+  };
+  f32x4 pqk[kSplitBatch], pvv[kSplitBatch];
+  float pab[kSplitBatch];
+  load_splits4(qk_src(min(t, nqk - 1)), split, S, pqk);
+  load_splits4(v_src(min(t, nv - 1)), split, S, pvv);
+  {
+    const int i = min(t, nab - 1), j = i >> 1, w = i & 1;
+    const float* src = P + (size_t)(rs + j) * N + 3 * hg * kGdnDim + w * hg + h;
+#pragma unroll
+    for (int b = 0; b < kSplitBatch; ++b) pab[b] = src[(size_t)min(b, S - 1) * split];
+  }
+  auto qk_item = [&](int it, const double (&a)[4]) {   // uniform over each 32-thread group
+    const int j = it >> 6, vec = (it >> 5) & 1, quad = it & 31;
     float f[4];
     double ss = 0.0;
 #pragma unroll
@@ -414,21 +433,29 @@ __global__ __launch_bounds__(256) void k_gdn_verify(const float* P, int S, RowIn
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       dst[e] = vec ? (float)((double)f[e] * inv) : (float)((double)f[e] * inv / sqrt((double)kGdnDim));
-  }
-  // v of the block's rows, then alpha and beta
-  for (int it = t; it < cols * (kGdnRows / 4); it += 256) {
-    const int j = it / (kGdnRows / 4), quad = it % (kGdnRows / 4);
+  };
+  if (t < nqk) {
     double a[4];
-    sum_splits4(P + (size_t)(rs + j) * N + 2 * hg * kGdnDim + h * kGdnDim + rb * kGdnRows + 4 * quad, split, S, a);
+    sum_loaded4(pqk, qk_src(t), split, S, a);
+    qk_item(t, a);
+  }
+  for (int it = t + 256; it < nqk; it += 256) {
+    double a[4];
+    sum_splits4(qk_src(it), split, S, a);
+    qk_item(it, a);
+  }
+  if (t < nv) {
+    double a[4];
+    sum_loaded4(pvv, v_src(t), split, S, a);
+    const int j = t / (kGdnRows / 4), quad = t % (kGdnRows / 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[j][4 * quad + e] = (float)a[e];
   }
-  if (t < 2 * cols) {
-    const int j = t >> 1, w = t & 1;
-    const float* src = P + (size_t)(rs + j) * N + 3 * hg * kGdnDim + w * hg + h;
-    double a = src[0];
-    for (int ss = 1; ss < S; ++ss) a += src[(size_t)ss * split];
-    sab[j][w] = (float)(1.0 / (1.0 + exp(-(double)(float)a)));
+  if (t < nab) {
+    double a = (double)pab[0];
+#pragma unroll
+    for (int b = 1; b < kSplitBatch; ++b) a = b < S ? a + (double)pab[b] : a;
+    sab[t >> 1][t & 1] = (float)(1.0 / (1.0 + exp(-(double)(float)a)));
   }
   __syncthreads();
   // stage the column inputs for the commit's replay: k, alpha, beta once (row block 0),

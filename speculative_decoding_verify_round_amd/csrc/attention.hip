@@ -772,8 +772,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o, int rp
     for (int i = 0; i < kCombineBatch; ++i) {
       const float* src = base + (size_t)min(c0 + i, nch - 1) * cstride;
       ov[i] = *reinterpret_cast<const f32x4*>(src + io);
-      mv[i] = src[im];
-      lv[i] = src[im + 1];
+      const float2 ml = *reinterpret_cast<const float2*>(src + im);   // (max, sum): one load
+      mv[i] = ml.x;
+      lv[i] = ml.y;
     }
     float bm = -INFINITY;
 #pragma unroll

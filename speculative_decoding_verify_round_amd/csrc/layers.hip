@@ -153,21 +153,23 @@ __device__ __forceinline__ void sum_loaded4(const f32x4 (&pv)[kSplitBatch], cons
 
 // x[r] += float(sum_s P[s][r]) (s in order), then h[r] = round(rmsnorm(x[r]) * gain).
 // Every load of the row (residual, the S partials, the gains of both float4 groups) is
-// issued before the first is used, so the kernel pays one memory round trip.
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int S, int R, float* x, int H,
+// issued before the first is used, so the kernel pays one memory round trip; S is a
+// template argument so that no lane loads a split twice.
+template <typename T, int S>
+__global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int R, float* x, int H,
                                                              const float* gain, float eps, T* h) {
   __shared__ double red[32];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * H;
   const size_t sstride = (size_t)R * H;
-  f32x4 xo[kRowGroups], gn[kRowGroups], pv[kRowGroups][kSplitBatch];
+  f32x4 xo[kRowGroups], gn[kRowGroups], pv[kRowGroups][S];
 #pragma unroll
   for (int gi = 0; gi < kRowGroups; ++gi) {
-    const int g = min(threadIdx.x + gi * kRowThreads, H / 4 - 1);   // a valid address for every lane
+    const int g = min(threadIdx.x + gi * (int)blockDim.x, H / 4 - 1);   // a valid address for every lane
     xo[gi] = *reinterpret_cast<const f32x4*>(xr + 4 * g);
     gn[gi] = *reinterpret_cast<const f32x4*>(gain + 4 * g);
-    load_splits4(P + (size_t)r * H + 4 * g, sstride, S, pv[gi]);
+#pragma unroll
+    for (int b = 0; b < S; ++b) pv[gi][b] = *reinterpret_cast<const f32x4*>(P + (size_t)r * H + 4 * g + b * sstride);
   }
   // every group is summed (a clamped group repeats the row's last one) and only valid
   // groups are stored and counted: no branch between the loads and their use
@@ -175,10 +177,15 @@ __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int 
   double ss = 0.0;
 #pragma unroll
   for (int gi = 0; gi < kRowGroups; ++gi) {
-    const int g = threadIdx.x + gi * kRowThreads;
+    const int g = threadIdx.x + gi * (int)blockDim.x;
     const bool ok = 4 * g < H;
     double t[4];
-    sum_loaded4(pv[gi], P + (size_t)r * H + 4 * min(g, H / 4 - 1), sstride, S, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (double)pv[gi][0][e];
+#pragma unroll
+    for (int b = 1; b < S; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] += (double)pv[gi][b][e];
 #pragma unroll
     for (int e = 0; e < 4; ++e) xn[gi][e] = (float)((double)xo[gi][e] + (double)(float)t[e]);   // x + float(projection)
     if (ok) *reinterpret_cast<f32x4*>(xr + 4 * g) = xn[gi];
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int 
   const size_t plane = act_plane(R, H);
 #pragma unroll
   for (int gi = 0; gi < kRowGroups; ++gi) {
-    const int g = threadIdx.x + gi * kRowThreads;
+    const int g = threadIdx.x + gi * (int)blockDim.x;
     if (4 * g >= H) break;
     float v[4];
 #pragma unroll
@@ -199,14 +206,35 @@ __global__ __launch_bounds__(kRowThreads) void k_resid_norm(const float* P, int 
   }
 }
 
+// Threads of a row's workgroup: just enough for kRowGroups float4 groups each (whole
+// waves).  Every load instruction costs the address unit the same time whether or not its
+// lanes need it, and one workgroup per row leaves most of a round's 64 rows on one CU each.
+static int row_threads(int H) {
+  const int t = ((H / 4 + kRowGroups - 1) / kRowGroups + 63) / 64 * 64;
+  return t < kRowThreads ? t : kRowThreads;
+}
+
 int launch_resid_norm(const float* P, int S, float* x, int H, const float* gain, float eps, void* h,
                       const RowInfo& ri, bool bf16, hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, x, H, gain, eps,
-                       reinterpret_cast<bf16_t*>(h));
-  else
-    hipLaunchKernelGGL(k_resid_norm<float>, dim3(ri.R), dim3(kRowThreads), 0, st, P, S, ri.R, x, H, gain, eps,
-                       reinterpret_cast<float*>(h));
+  if (H / 4 > kRowGroups * kRowThreads || S < 1 || S > kSplitBatch) return -1;
+  const dim3 block(row_threads(H));
+  const void* f = nullptr;
+#define SV_RN(S_) f = bf16 ? reinterpret_cast<const void*>(&k_resid_norm<bf16_t, S_>) \
+                         : reinterpret_cast<const void*>(&k_resid_norm<float, S_>)
+  switch (S) {
+    case 1: SV_RN(1); break;
+    case 2: SV_RN(2); break;
+    case 3: SV_RN(3); break;
+    case 4: SV_RN(4); break;
+    case 5: SV_RN(5); break;
+    case 6: SV_RN(6); break;
+    case 7: SV_RN(7); break;
+    default: SV_RN(8); break;
+  }
+#undef SV_RN
+  int R = ri.R;
+  void* args[] = {&P, &R, &x, &H, &gain, &eps, &h};
+  if (hipLaunchKernel(f, dim3(ri.R), block, args, 0, st) != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

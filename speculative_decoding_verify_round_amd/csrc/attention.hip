@@ -789,7 +789,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p, T* o, int rp
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
       if (c0 + i < nch && mv[i] != -INFINITY) {
-        const double f = exp2((double)mv[i] - M);
+        // the chunk's weight 2^(m_c - M) <= 1 by the hardware exp2 (float32; the float64
+        // library call, once per thread and chunk, was most of the launch's arithmetic)
+        const double f = (double)__builtin_amdgcn_exp2f((float)((double)mv[i] - M));
 #pragma unroll
         for (int e = 0; e < 4; ++e) Oc[e] += (double)ov[i][e] * f;
         Lc += (double)lv[i] * f;

@@ -579,16 +579,37 @@ __global__ __launch_bounds__(256) void k_commit_kv(const int32_t* committed, con
   T* vp = vpool + li * layer_pool;
   const T* skl = sk + li * stage_layer_elems;
   const T* svl = sv + li * stage_layer_elems;
-  const int per_col = nkv * d;
-  for (int it = threadIdx.x; it < c * per_col; it += blockDim.x) {
-    const int j = it / per_col, rem = it - j * per_col;
-    const int g = rem / d, dd = rem - g * d;
-    const int pos = kvl + j;
-    const int blk = clamp_blk(block_table[(size_t)l * max_blocks + (pos >> 4)], n_blocks);
-    const int slot = (kvl & 15) + j;
-    const size_t sb = (size_t)kStageBlocks * l + (slot >> 4);
-    kp[(((size_t)blk * nkv + g) * kBlock + (pos & 15)) * d + dd] = skl[((sb * nkv + g) * kBlock + (slot & 15)) * d + dd];
-    vp[(((size_t)blk * nkv + g) * d + dd) * kBlock + (pos & 15)] = svl[((sb * nkv + g) * d + dd) * kBlock + (slot & 15)];
+  const int per_col = nkv * d, n = c * per_col;
+  // the committed columns span at most two cache blocks: their ids are read once
+  const int* btl = block_table + (size_t)l * max_blocks;
+  const int blk0 = clamp_blk(btl[kvl >> 4], n_blocks);
+  const int blk1 = clamp_blk(btl[min((kvl + c - 1) >> 4, max_blocks - 1)], n_blocks);
+  // kU elements per thread per pass: every load of a pass is issued before its stores
+  constexpr int kU = 8;
+  for (int base = threadIdx.x; base < n; base += kU * (int)blockDim.x) {
+    T kv[kU], vv[kU];
+    size_t kd[kU], vd[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = min(base + u * (int)blockDim.x, n - 1);
+      const int j = it / per_col, rem = it - j * per_col;
+      const int g = rem / d, dd = rem - g * d;
+      const int pos = kvl + j;
+      const int blk = (pos >> 4) == (kvl >> 4) ? blk0 : blk1;
+      const int slot = (kvl & 15) + j;
+      const size_t sb = (size_t)kStageBlocks * l + (slot >> 4);
+      kv[u] = skl[((sb * nkv + g) * kBlock + (slot & 15)) * d + dd];
+      vv[u] = svl[((sb * nkv + g) * d + dd) * kBlock + (slot & 15)];
+      kd[u] = (((size_t)blk * nkv + g) * kBlock + (pos & 15)) * d + dd;
+      vd[u] = (((size_t)blk * nkv + g) * d + dd) * kBlock + (pos & 15);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (base + u * (int)blockDim.x < n) {
+        kp[kd[u]] = kv[u];
+        vp[vd[u]] = vv[u];
+      }
+    }
   }
 }
 

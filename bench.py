@@ -346,12 +346,14 @@ def run_head(args, cfg):
     kw = dict(mode="sampled", temperature=args.sampled, q_probs=qd) if sampled else {}
     rc = dc.round([[0] * (k + 1)] * L, tokens_dev=toks, seed=cfg.philox_seed, **kw)
     committed_log = []
+    com_host = torch.empty(L, dtype=torch.int32).pin_memory()
 
     def step(i):
         rc.r.seed = cfg.philox_seed + i
         dc.verify_head(rc, hid)
         dc.accept(rc, stats=False)
-        committed_log.append(dc.committed.cpu().numpy().copy())
+        com_host.copy_(dc.committed)        # the per-round device -> host crossing (blocking)
+        committed_log.append(com_host.numpy().copy())
 
     log(f"warmup {warm} steps")
     for i in range(warm):
@@ -469,20 +471,25 @@ def run_decoder(args, cfg):
     pos = np.zeros(L, np.int64)          # tokens committed so far per lane (ref[l, pos] is the anchor)
     planted_hits = []                    # per step: [L] leading planted hits (the expected kept drafts)
 
-    def drafts_for(l):
-        p = int(pos[l])
-        d, lead, run = [], 0, True
-        for i in range(k):
-            t = int(ref[l, p + 1 + i])
-            if rng.random() >= alpha[i]:
-                t = (t + 1 + int(rng.integers(0, cfg.vocab - 1))) % cfg.vocab
-                run = False
-            elif run:
-                lead += 1
-            d.append(t)
-        return d, lead
+    def draw_plant():
+        # one step's planted decisions, drawn lane by lane and slot by slot: a miss (and the
+        # offset of its planted token) depends on the draw alone, not on where the lane stands,
+        # so a step's draw is taken while the previous round still runs on the device
+        miss = np.zeros((L, k), bool)
+        off = np.zeros((L, k), np.int64)
+        for l in range(L):
+            for i in range(k):
+                if rng.random() >= alpha[i]:
+                    miss[l, i] = True
+                    off[l, i] = int(rng.integers(0, cfg.vocab - 1))
+        # leading planted hits per lane: the drafts a correct round keeps
+        lead = np.where(miss.any(axis=1), miss.argmax(axis=1), k)
+        return miss, off, lead
 
-    samp, qsets = {}, None
+    lane_ix = np.arange(L)[:, None]
+    slot_ix = np.arange(1, k + 1)[None, :]
+
+    qsets = None
     if sampled:
         # the drafter: seeded softmax rows q (logits N(0, 2)), each draft drawn from its
         # row; a pool of four (q, drafts) sets made before the timed steps, used in turn
@@ -492,31 +499,37 @@ def run_decoder(args, cfg):
             qd = torch.softmax(2.0 * torch.randn((R, cfg.vocab), generator=gq, device="cuda"), dim=-1)
             dr = torch.multinomial(qd, 1, generator=gq).view(L, k + 1)[:, 1:].cpu().numpy()
             qsets.append((qd, dr))
-        samp = {"mode": "sampled", "temperature": args.sampled}
     n_step = [0]
     tok_host = torch.empty(R, dtype=torch.int32).pin_memory()
     tok_dev = torch.empty(R, dtype=torch.int32, device="cuda")
+    com_host = torch.empty(L, dtype=torch.int32).pin_memory()
+    out_host = torch.empty(tuple(dc.out_tokens.shape), dtype=dc.out_tokens.dtype).pin_memory()
+    tok_np, com_np, out_np = tok_host.numpy(), com_host.numpy(), out_host.numpy()
     committed_log = []
-    anchor = list(anchors)
+    anchor = np.array(anchors, np.int64)
     ev_pairs = []
+    # the round descriptor is the same every step (the tokens are rewritten in place);
+    # sampled steps change only the drafter rows and the seed
+    rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev, **pen,
+                  **({"mode": "sampled", "temperature": args.sampled, "q_probs": qsets[0][0]} if sampled else {}))
+    plant = [None if sampled else draw_plant()]
 
     def step(timed):
-        flat, leads = [], []
         if sampled:
             qd, dr = qsets[n_step[0] % len(qsets)]
-            for l in range(L):
-                flat += [anchor[l]] + [int(x) for x in dr[l]]
-            samp["q_probs"] = qd
-            samp["seed"] = 1000 + n_step[0]
+            toks = np.concatenate([anchor[:, None], dr.astype(np.int64)], axis=1)
+            rc.q = qd
+            rc.r.q_probs = qd.data_ptr()
+            rc.r.seed = 1000 + n_step[0]
+            lead = None
         else:
-            for l in range(L):
-                d, lead = drafts_for(l)
-                flat += [int(ref[l, pos[l]])] + d
-                leads.append(lead)
-        tok_host.copy_(torch.tensor(flat, dtype=torch.int32))
+            miss, off, lead = plant[0]
+            cur = ref[lane_ix, pos[:, None] + slot_ix]
+            toks = np.concatenate([ref[lane_ix[:, 0], pos][:, None],
+                                   np.where(miss, (cur + 1 + off) % cfg.vocab, cur)], axis=1)
+        tok_np[:] = toks.reshape(-1)
         tok_dev.copy_(tok_host, non_blocking=True)
         n_step[0] += 1
-        rc = dc.round([[0] * (k + 1)] * L, tokens_dev=tok_dev, **pen, **samp)
         if evict is not None:
             evict.fill_(n_step[0] & 255)    # outside the round's events: the cache holds no weights
         a = b = None
@@ -530,15 +543,19 @@ def run_decoder(args, cfg):
         if timed:
             b.record()
             ev_pairs.append((a, b))
-        c = dc.committed.cpu().numpy()          # the per-round device -> host crossing
+        if not sampled:
+            plant[0] = draw_plant()         # the next step's draw, while this round runs
+        # the per-round device -> host crossing (the drafter's input), a blocking copy into
+        # pinned memory that also waits for the round
+        com_host.copy_(dc.committed)
         if sampled:
-            last = dc.out_tokens.cpu().numpy()
-            for l in range(L):
-                anchor[l] = int(last[l, int(c[l]) - 1])
-        for l in range(L):
-            pos[l] += int(c[l])
-        committed_log.append(c.copy())
-        planted_hits.append(leads)
+            out_host.copy_(dc.out_tokens)
+        c = com_np.astype(np.int64)
+        if sampled:
+            anchor[:] = out_np[np.arange(L), c - 1]
+        pos[:] += c
+        committed_log.append(c)
+        planted_hits.append(lead)
 
     log(f"warmup {warm} steps")
     for _ in range(warm):

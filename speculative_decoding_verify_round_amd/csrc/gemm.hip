@@ -403,13 +403,15 @@ constexpr int chunk_steps() { return RT <= 2 ? 8 : 4; }
 
 
 // ------------------------------------------------------------------------------- projection
-// R > 16: at most 256 workgroups of eight waves per launch.  Units are tile
-// pairs (EPI 0: tiles 2u, 2u + 1; EPI 1: gate and up tile u).  Workgroup b
-// takes split s = b / cols and the units [w P / cols, (w + 1) P / cols) of it
-// (w = b % cols), at most five: units 0..3 to the main waves, a fifth to the two
-// helpers, so every CU streams the same number of units +-1 whatever the tile count
-// (1088 gate/up pairs become 4 or 5 per CU, where whole 4-pair workgroups leave 16
-// CUs with twice the work).
+// R > 16: at most 256 workgroups of eight waves per launch; workgroup b takes split
+// s = b / cols and part w = b % cols of it.  Plain outputs (EPI 0) are dealt by
+// 16-feature tile: tiles [w N_t / cols, (w + 1) N_t / cols), at most eight, two per main
+// wave, so the busiest CU streams at most one tile more than the others (448 QKV tiles
+// at four splits: seven per workgroup, where tile pairs would give half of them eight).
+// SwiGLU outputs (EPI 1) are dealt by unit (gate and up tile u): units [w P / cols,
+// (w + 1) P / cols), at most five, units 0..3 to the main waves and a fifth to the two
+// helpers (1088 gate/up pairs become 4 or 5 per CU, where whole 4-pair workgroups leave
+// 16 CUs with twice the work).
 template <int RT, int XS, int EPI, int NR>
 __device__ __forceinline__ void bal_epilogue(const ProjParams& p, const int (&tile)[2], int s, int r0, int RS,
                                              const f32x4 (&acc)[2][NR]) {
@@ -553,7 +555,6 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
-  const int ub = (int)((long long)w * p.units / p.cols), ue = (int)((long long)(w + 1) * p.units / p.cols);
   const int KS = p.K >> 5, U = p.K >> 8;
   const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
   if (wave >= kMainWaves + kHelpers) {
@@ -561,8 +562,20 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
     return;
   }
   const bool helper = wave >= kMainWaves;
-  const int unit = helper ? ub + kMainWaves : ub + wave;
-  if (unit >= ue) {   // no unit: keep the barrier count
+  // EPI 0: workgroup w of a split takes the 16-feature tiles [w tiles / cols, (w + 1) tiles /
+  // cols), at most 2 kMainWaves of them, two per main wave in order (the last busy wave may
+  // hold one); the helpers have none.  EPI 1: units (gate and up tile u) as listed above.
+  int t0, nt;
+  if constexpr (EPI == 0) {
+    const int tb = (int)((long long)w * p.tiles / p.cols), te = (int)((long long)(w + 1) * p.tiles / p.cols);
+    t0 = tb + 2 * wave;
+    nt = helper ? 0 : max(0, min(2, te - t0));
+  } else {
+    const int ub = (int)((long long)w * p.units / p.cols), ue = (int)((long long)(w + 1) * p.units / p.cols);
+    t0 = helper ? ub + kMainWaves : ub + wave;
+    nt = t0 < ue ? 2 : 0;
+  }
+  if (nt == 0) {   // nothing to stream: keep the barrier count
     for (int g = 0; g < (u1 - u0) * (kUnit / KC); ++g) wg_barrier();
     return;
   }
@@ -570,10 +583,28 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   const bf16_t* wp[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) {
-    tile[j] = EPI == 1 ? unit : unit * 2 + j;
+    tile[j] = EPI == 1 ? t0 : t0 + j;
     const int tc = min(tile[j], p.tiles - 1);
     const bf16_t* base = (EPI == 1 && j == 1) ? p.W1 : p.W0;
     wp[j] = base + ((size_t)tc * KS + (size_t)u0 * kUnit) * 512 + lane * 8;
+  }
+  if constexpr (EPI == 0) {
+    if (nt == 1) {   // one tile: its own chain, the second output slot skipped
+      const bf16_t* wp1[1] = {wp[0]};
+      f32x4 acc1[1][RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc1[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      proj_core_xw<RT, 1, XS, KC, RT, true>(wp1, 512, 0, 1, u1 - u0, xring, acc1);
+      f32x4 acc[T][RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        acc[0][t] = acc1[0][t];
+        acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const int tile1[T] = {tile[0], p.tiles};
+      bal_epilogue<RT, XS, EPI, RT>(p, tile1, s, 0, 1, acc);
+      return;
+    }
   }
   if (!helper) {
     f32x4 acc[T][RT];
@@ -676,11 +707,19 @@ __global__ __launch_bounds__(64) void k_proj_direct(ProjParams p) {
   }
 }
 
-// Workgroups per split of the balanced launch (at most 256 per launch, at most
-// kMaxUnits units each); the split count is the host's, a function of the shape.
+// Workgroups per split of the balanced SwiGLU launch (at most 256 per launch, at most
+// kMaxUnits units each).
 static int bal_cols(int units, int S) {
   int cols = std::min(kCUs / S, units);
   if ((units + cols - 1) / cols > kMaxUnits) cols = (units + kMaxUnits - 1) / kMaxUnits;
+  return std::max(cols, 1);
+}
+
+// Workgroups per split of a balanced plain launch: kCUs / S, or fewer when there are fewer
+// tiles, or more when a workgroup would otherwise hold more than two tiles per main wave.
+static int tile_cols(int tiles, int S) {
+  int cols = std::min(kCUs / S, tiles);
+  if ((tiles + cols - 1) / cols > 2 * kMainWaves) cols = (tiles + 2 * kMainWaves - 1) / (2 * kMainWaves);
   return std::max(cols, 1);
 }
 
@@ -702,7 +741,7 @@ int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   p.units = swiglu ? p.tiles : (p.tiles + 1) / 2;
-  p.cols = bal_cols(p.units, p.S);
+  p.cols = swiglu ? bal_cols(p.units, p.S) : tile_cols(p.tiles, p.S);
   dim3 grid(p.rem ? kCUs : p.cols * p.S), block(512);
 #define SV_P(RT_, XS_, E_) hipLaunchKernelGGL((k_proj_bal<RT_, XS_, E_>), grid, block, 0, st, p)
 #define SV_P_RT(XS_, E_)             \

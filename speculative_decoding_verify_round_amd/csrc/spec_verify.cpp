@@ -60,18 +60,20 @@ struct spec_model {
 namespace {
 
 // K splits of a bf16 projection, a function of (N, K) only so that results never
-// depend on R: the largest S (at most 8, with at least two 256-wide units per split)
-// for which the tile pairs of all splits fit four to a workgroup of the one-per-CU
-// launch.  Four pairs keep one weight-streaming wave per SIMD; a fifth pair would
-// share a SIMD with another MFMA-heavy wave, and the younger of the two is starved
-// of MFMA issue until the older one ends.  The gate/up pair is never split (its
-// SwiGLU epilogue needs the full sums).
-int split_for(const spec_model* m, int N, int K, bool fused_pair) {
+// depend on R: the largest S (at most `cap`, with at least two 256-wide units per split)
+// for which the tiles of all splits fit eight to a workgroup of the one-per-CU launch.
+// Eight tiles keep one weight-streaming wave per SIMD; a fifth tile pair would share a
+// SIMD with another MFMA-heavy wave, and the younger of the two is starved of MFMA issue
+// until the older one ends.  The input projections are capped at four splits: the
+// attention prologue and the recurrent verify load four splits of their inputs in one
+// batch, and a fifth costs another memory round trip.  The gate/up pair is never split
+// (its SwiGLU epilogue needs the full sums).
+int split_for(const spec_model* m, int N, int K, bool fused_pair, int cap = 8) {
   if (!m->bf16 || fused_pair) return 1;
-  const int pairs = ((N + 15) / 16 + 1) / 2;
+  const int tiles = (N + 15) / 16;
   const int units = K / 256;
   int S = 1;
-  while (S < 8 && 2 * (S + 1) <= units && pairs * (S + 1) <= 4 * sv::kCUs) ++S;
+  while (S < cap && 2 * (S + 1) <= units && tiles * (S + 1) <= 8 * sv::kCUs) ++S;
   return S;
 }
 
@@ -531,11 +533,11 @@ int spec_model_create(const spec_model_desc* desc, spec_model** out) {
   m->d.layers = nullptr;   // per-layer weights live in m->layers
   const int H = d.hidden;
   if (m->n_attn) {
-    m->s_in_attn.S = split_for(m, (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, H, false);
+    m->s_in_attn.S = split_for(m, (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, H, false, 4);
     m->s_o_attn.S = split_for(m, H, d.n_q_heads * d.head_dim, false);
   }
   if (m->n_gdn) {
-    m->s_in_gdn.S = split_for(m, 3 * d.gdn_heads * d.gdn_dim + 2 * d.gdn_heads, H, false);
+    m->s_in_gdn.S = split_for(m, 3 * d.gdn_heads * d.gdn_dim + 2 * d.gdn_heads, H, false, 4);
     m->s_o_gdn.S = split_for(m, H, d.gdn_heads * d.gdn_dim, false);
   }
   if (d.n_layers) {

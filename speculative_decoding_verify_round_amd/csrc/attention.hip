@@ -74,7 +74,7 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // Four consecutive floats summed over the splits s = 0 .. S - 1 in split order in float64,
 // rounded once: the first OB splits come loaded (v[b] = split min(b, S - 1)), later ones
-// are read here from src + s ss.  Selects rather than branches, so that the compiler keeps
+// (none while the split rule caps the QKV projection at four) are read here from src + s ss.  Selects rather than branches, so that the compiler keeps
 // the loads of v where the caller issued them.
 template <int OB>
 __device__ __forceinline__ f32x4 split_sum(const f32x4 (&v)[OB], const float* src, size_t ss, int S) {

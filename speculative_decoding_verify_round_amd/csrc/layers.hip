@@ -143,7 +143,7 @@ __device__ __forceinline__ void sum_loaded4(const f32x4 (&pv)[kSplitBatch], cons
   for (int i = 1; i < kSplitBatch; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) t[e] = i < S ? t[e] + (double)pv[i][e] : t[e];
-  if (S > kSplitBatch) {   // more splits than one batch (the split rule allows at most 8)
+  if (S > kSplitBatch) {   // more splits than one batch (the split rule caps the inputs at four)
     double u[4];
     sum_splits4(P + kSplitBatch * split_stride, split_stride, S - kSplitBatch, u);
 #pragma unroll

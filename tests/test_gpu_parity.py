@@ -223,7 +223,7 @@ def test_small_hybrid_bf16_round_and_commit():
 
 def test_maximum_rows_columns_and_hidden():
     """The largest shapes the kernels take: hidden 8192 (the row kernels' limit; the QKV
-    projection at the largest split, 8), 4 lanes x 16 columns = 64 rows (every lane at the
+    projection at its largest split, the cap of 4), 4 lanes x 16 columns = 64 rows (every lane at the
     column limit, 64 query rows per lane with 4 query heads per kv head, so all four query
     tiles are busy), the columns starting at slot 15 of a cache block so they straddle two
     staged blocks.  A greedy and a sampled round, then a teacher-forced commit of all 16

@@ -243,7 +243,8 @@ struct ProjParams {
   int R, N, K, S;
   int tiles;            // ceil(N / 16)
   int units;            // tile pairs (balanced launch)
-  int cols;             // workgroups per split
+  int cols;             // workgroups per split (SwiGLU and one-wave launches)
+  int scols[8];         // balanced plain launch: workgroups of split s, in split order
   float* P;             // [S][R][N] float32 partial sums
   bf16_t* Y;            // SwiGLU output planes, packed with width N
   size_t yplane;

@@ -554,7 +554,25 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
     }
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int s = blockIdx.x / p.cols, w = blockIdx.x % p.cols;
+  // workgroup -> (split s, part w of cols): plain launches give each split its own count
+  int s, w, cols;
+  if constexpr (EPI == 0) {
+    s = 0;
+    w = blockIdx.x;
+    cols = p.scols[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      if (i < p.S && w >= cols) {
+        w -= cols;
+        s = i;
+        cols = p.scols[i];
+      }
+    }
+  } else {
+    s = blockIdx.x / p.cols;
+    w = blockIdx.x % p.cols;
+    cols = p.cols;
+  }
   const int KS = p.K >> 5, U = p.K >> 8;
   const int u0 = (int)((long long)s * U / p.S), u1 = (int)((long long)(s + 1) * U / p.S);
   if (wave >= kMainWaves + kHelpers) {
@@ -567,11 +585,11 @@ __global__ __launch_bounds__(512, 1) void k_proj_bal(ProjParams p) {
   // hold one); the helpers have none.  EPI 1: units (gate and up tile u) as listed above.
   int t0, nt;
   if constexpr (EPI == 0) {
-    const int tb = (int)((long long)w * p.tiles / p.cols), te = (int)((long long)(w + 1) * p.tiles / p.cols);
+    const int tb = (int)((long long)w * p.tiles / cols), te = (int)((long long)(w + 1) * p.tiles / cols);
     t0 = tb + 2 * wave;
     nt = helper ? 0 : max(0, min(2, te - t0));
   } else {
-    const int ub = (int)((long long)w * p.units / p.cols), ue = (int)((long long)(w + 1) * p.units / p.cols);
+    const int ub = (int)((long long)w * p.units / cols), ue = (int)((long long)(w + 1) * p.units / cols);
     t0 = helper ? ub + kMainWaves : ub + wave;
     nt = t0 < ue ? 2 : 0;
   }
@@ -723,6 +741,51 @@ static int tile_cols(int tiles, int S) {
   return std::max(cols, 1);
 }
 
+// Workgroups of each split of a balanced plain launch (returns their sum, the grid).  The
+// splits of U units over S hold U / S units or one more, and a workgroup streams its units
+// x (its tiles x 16 x 256 x 2 weight bytes + 64 x 256 x 4 activation bytes at 64 rows, those
+// L2 hits holding the read window about a quarter as long): units x (tiles + 2.24) in tile
+// equivalents.  A split of more units gets more workgroups when that lowers the largest
+// such cost within kCUs workgroups of at most 2 kMainWaves tiles (six splits of 11 or 12
+// units over 320 tiles: 40 workgroups of eight tiles for an 11-unit split, 46 of seven for
+// a 12-unit one, where 42 each give the 12-unit splits eight); otherwise every split gets
+// tile_cols workgroups.
+static int plan_cols(int tiles, int S, int U, int (&scols)[8]) {
+  constexpr double kAct = 2.24;
+  int us[8];
+  for (int s = 0; s < S; ++s) us[s] = (s + 1) * U / S - s * U / S;
+  const int uc = tile_cols(tiles, S), ut = (tiles + uc - 1) / uc;
+  double uniform = 0.0;
+  for (int s = 0; s < S; ++s) uniform = std::max(uniform, us[s] * (ut + kAct));
+  auto tiles_for = [&](int u, double c) {   // most tiles a workgroup of u units may take at cost c
+    int t = 2 * kMainWaves;
+    while (t >= 1 && u * (t + kAct) > c + 1e-9) --t;
+    return t;
+  };
+  double best = uniform;
+  bool found = false;
+  for (int s0 = 0; s0 < S; ++s0)
+    for (int t0 = 1; t0 <= 2 * kMainWaves; ++t0) {
+      const double c = us[s0] * (t0 + kAct);
+      if (c >= best - 1e-9) continue;
+      int total = 0;
+      for (int s = 0; s < S && total <= kCUs; ++s) {
+        const int t = tiles_for(us[s], c);
+        total = t < 1 ? kCUs + 1 : total + (tiles + t - 1) / t;
+      }
+      if (total <= kCUs) {
+        best = c;
+        found = true;
+      }
+    }
+  int grid = 0;
+  for (int s = 0; s < 8; ++s) {
+    scols[s] = s >= S ? 0 : found ? (tiles + tiles_for(us[s], best) - 1) / tiles_for(us[s], best) : uc;
+    grid += scols[s];
+  }
+  return grid;
+}
+
 int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
   ProjParams p = p0;
   const int RT = (p.R + 15) / 16;
@@ -741,8 +804,14 @@ int launch_proj(const ProjParams& p0, bool swiglu, int xs, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   p.units = swiglu ? p.tiles : (p.tiles + 1) / 2;
-  p.cols = swiglu ? bal_cols(p.units, p.S) : tile_cols(p.tiles, p.S);
-  dim3 grid(p.rem ? kCUs : p.cols * p.S), block(512);
+  int nwg;
+  if (swiglu) {
+    p.cols = bal_cols(p.units, p.S);
+    nwg = p.rem ? kCUs : p.cols * p.S;
+  } else {
+    nwg = plan_cols(p.tiles, p.S, p.K >> 8, p.scols);
+  }
+  dim3 grid(nwg), block(512);
 #define SV_P(RT_, XS_, E_) hipLaunchKernelGGL((k_proj_bal<RT_, XS_, E_>), grid, block, 0, st, p)
 #define SV_P_RT(XS_, E_)             \
   switch (RT) {                      \

@@ -242,7 +242,7 @@ struct ProjParams {
   size_t xplane;        // elements per activation plane
   int R, N, K, S;
   int tiles;            // ceil(N / 16)
-  int units;            // tile pairs (balanced launch)
+  int units;            // balanced SwiGLU launch: gate/up units (one tile of each)
   int cols;             // workgroups per split (SwiGLU and one-wave launches)
   int scols[8];         // balanced plain launch: workgroups of split s, in split order
   float* P;             // [S][R][N] float32 partial sums

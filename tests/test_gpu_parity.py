@@ -27,8 +27,14 @@ def _bf16_head_model(H=256, V=1024):
 
 
 @pytest.mark.parametrize("R,N,K", [(1, 16, 256), (5, 40, 512), (16, 48, 1024), (33, 200, 2048),
-                                   (64, 7168, 5120), (8, 5120, 17408), (64, 34816, 5120)])
+                                   (64, 7168, 5120), (8, 5120, 17408), (64, 34816, 5120),
+                                   (64, 5120, 5120), (64, 5120, 17408), (24, 1024, 5120)])
 def test_projection_kernel(R, N, K):
+    """Against the float64 product of the same bf16 inputs.  The 27B shapes: QKV (7168 x
+    5120), down at 8 rows, a gate-sized plain launch, and O and down at 64 rows, whose six
+    splits of unequal length get unequal workgroup counts; (24, 1024, 5120) splits eight
+    ways into splits of 2 and 3 units.  Row 0 alone (the one-wave kernel) gives the same bits
+    as row 0 of the full launch."""
     from speculative_decoding_verify_round_amd import binding as B
     from speculative_decoding_verify_round_amd.runtime import pack_weight
     log(f"projection R={R} N={N} K={K}")

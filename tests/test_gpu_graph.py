@@ -1,19 +1,21 @@
-"""A greedy verify round captured once in a HIP graph and replayed, bit for bit.
+"""A verify round captured once in a HIP graph and replayed, bit for bit.
 
-Every launch of a greedy round goes on the caller's stream, and none of them
-allocates, copies or clears memory (counters are cleared by the kernels that use
-them), so verify, accept and commit can be recorded once and replayed with new
-tokens and new committed counts written into the same device buffers.  Each
+Every launch of a round goes on the caller's stream, and none of them allocates,
+copies or clears memory (counters are cleared by the kernels that use them), so
+verify, accept and commit can be recorded once and replayed with new tokens and new
+committed counts written into the same device buffers; a sampled round's LM head is
+a cooperative launch, which is recorded and replayed as such.  Each
 replay is compared bit for bit with the same round run eagerly on a twin cache:
 the row statistics, the committed runs and their tokens, kv_len, the paged K/V
 pools and the recurrent state.  Between replays the test does eager work of its
 own (the twin's round, the uploads of the next tokens and counts) and
 synchronises, and every replay is checked, not only the first.
 
-Two shapes: a ragged hybrid round (gated-delta-rule and attention layers, two
-lanes of 5 and 3 columns) and a 64-row dense round whose gate/up projection runs
-the balanced launch with cut units (their completion counters must be back at
-zero after every replay).
+Three cases: a ragged hybrid round (gated-delta-rule and attention layers, two
+lanes of 5 and 3 columns), greedy and sampled (the drafter rows and the seed fixed
+at capture), and a 64-row dense round whose gate/up projection runs the balanced
+launch with cut units (their completion counters must be back at zero after every
+replay).
 """
 import numpy as np
 import pytest
@@ -26,11 +28,16 @@ from speculative_decoding_verify_round_amd.runtime import DeviceCache, DeviceMod
 
 pytestmark = pytest.mark.gpu
 
+
+def _hybrid():
+    return small_hybrid(hidden=256, head_dim=128, ffn=512, vocab=1024, gdn_heads=2, gdn_dim=128, context=45)
+
+
 CASES = {
-    "hybrid-ragged": (lambda: small_hybrid(hidden=256, head_dim=128, ffn=512, vocab=1024, gdn_heads=2, gdn_dim=128,
-                                           context=45), [5, 3], 45, 8, 256),
+    "hybrid-ragged": (_hybrid, [5, 3], 45, 8, 256, False),
+    "hybrid-ragged-sampled": (_hybrid, [5, 3], 45, 8, 256, True),
     "dense-64rows-cut-units": (lambda: small_dense(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=5120,
-                                                   vocab=2048, context=300), [16, 16, 16, 16], 300, 24, 256),
+                                                   vocab=2048, context=300), [16, 16, 16, 16], 300, 24, 256, False),
 }
 
 
@@ -58,9 +65,13 @@ def _state(dc):
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_graph_replay_equals_eager(case):
-    make, cols, context, max_blocks, chunk = CASES[case]
+    make, cols, context, max_blocks, chunk, sampled = CASES[case]
     cfg = make()
     L, R = len(cols), sum(cols)
+    kw = {}
+    if sampled:
+        q, _ = synth.drafter_rows(cfg.input_seed, 5, R, cfg.vocab)
+        kw = dict(mode="sampled", temperature=0.9, q_probs=torch.from_numpy(q).cuda(), seed=321)
     w = synth.model_weights(cfg)
     dm = DeviceModel(cfg, w, attn_chunk=chunk)
     try:
@@ -73,14 +84,14 @@ def test_graph_replay_equals_eager(case):
         cnt_g = torch.ones(L, dtype=torch.int32, device="cuda")
         cnt_e = torch.ones(L, dtype=torch.int32, device="cuda")
         # every kernel of the round runs once before the capture (code objects loaded)
-        rc_w = warm.round(shape, tokens_dev=torch.zeros(R, dtype=torch.int32, device="cuda"))
+        rc_w = warm.round(shape, tokens_dev=torch.zeros(R, dtype=torch.int32, device="cuda"), **kw)
         warm.verify(rc_w)
         warm.accept(rc_w)
         warm.commit(rc_w)
         torch.cuda.synchronize()
         del warm
 
-        rc_g = graph.round(shape, tokens_dev=tok_g)
+        rc_g = graph.round(shape, tokens_dev=tok_g, **kw)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             graph.verify(rc_g)
@@ -94,7 +105,7 @@ def test_graph_replay_equals_eager(case):
             toks = rng.integers(0, cfg.vocab, R).astype(np.int32)
             cnt = np.array([rng.integers(1, c + 1) for c in cols], np.int32)
             # eager twin
-            rc_e = eager.round(shape, tokens_dev=torch.from_numpy(toks).cuda())
+            rc_e = eager.round(shape, tokens_dev=torch.from_numpy(toks).cuda(), **kw)
             eager.verify(rc_e)
             eager.accept(rc_e)
             cnt_e.copy_(torch.from_numpy(cnt))
